@@ -1,0 +1,167 @@
+/*
+ * fm.h - C ABI of the FlashMemory Memory-Indexer scoring pass for MI355X
+ * (gfx950).
+ *
+ * The pass is defined by the FlashMemory-DeepSeek-V4 README ("FlashMemory
+ * DS-V4 Retriever"):
+ *   - "Usage": inputs hidden [B, 4096] (decode-token hidden state),
+ *     comp_k [B, N, 132] uint8 (compressed CSA keys), positions [B] int64;
+ *     outputs per-layer sigmoid scores {l10, l12, l20} [B, N], an ensemble
+ *     [B, N] (mode max or mean) and a boolean keep mask from top_k=... or
+ *     threshold=...;
+ *   - "compressed_k format": one chunk = HEAD_DIM + 4 = 132 bytes, 128
+ *     float8_e4m3 codes followed by a float32 scale;
+ *   - "Architecture": the query branch (wq_a, RMSNorm, wq_b, reshape,
+ *     YaRN RoPE on the last 64 dims, normalized Walsh-Hadamard), the weight
+ *     branch (weights_proj times HEAD_DIM^-0.5 N_HEADS^-0.5) and
+ *     score = sigmoid(sum_heads relu(k . q_h) * w_h);
+ *   - "Joint checkpoint + ensemble": three independent layers (l10, l12,
+ *     l20), combined per chunk by max (default) or mean;
+ *   - "Inference flow": keep mask = top-K of the scores, or score > thresh.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device pointers must be device memory of the GPU
+ *     that was current when the context was created; host pointers are
+ *     named as such.  The caller owns every buffer.  Weights are borrowed
+ *     by the context and must outlive it.
+ *   - Row-major layouts, no padding: [B, N] has row stride N.
+ *   - Float buffers must be 4-byte aligned, positions 8-byte aligned,
+ *     comp_k 4-byte aligned (its records sit at a 132-byte stride).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  Inputs must stay valid
+ *     until that work completes.  One context serves one stream at a time
+ *     (its workspace is shared by the calls).
+ *   - No call allocates device memory after fm_create.
+ *   - Errors: every argument is checked before anything is enqueued; a
+ *     failing call enqueues nothing and returns a negative fm_status, with
+ *     a message in fm_last_error().  FM_EHIP means a HIP runtime call or a
+ *     launch failed (message from hipGetErrorString).
+ *   - B == 0 or N == 0 is an empty problem: FM_OK, nothing enqueued.
+ */
+#ifndef FM_H_
+#define FM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fm_ctx fm_ctx; /* opaque */
+
+typedef enum {
+  FM_OK = 0,
+  FM_EINVAL = -1,        /* bad argument: null pointer, out-of-range size, misalignment */
+  FM_EUNSUPPORTED = -2,  /* dimensions other than the compiled ones */
+  FM_ENOMEM = -3,        /* workspace allocation failed in fm_create */
+  FM_EHIP = -4           /* HIP runtime or launch failure */
+} fm_status;
+
+/* Cross-layer ensemble ("Joint checkpoint + ensemble"): max is the union
+ * and the default; mean is the arithmetic mean of the three sigmoid scores. */
+typedef enum { FM_ENSEMBLE_MAX = 0, FM_ENSEMBLE_MEAN = 1 } fm_ensemble;
+
+/* Layer dimensions and constants ("Architecture").  The compiled kernels
+ * support exactly n_layers 3, hidden 4096, q_lora_rank 1024, n_heads 64,
+ * head_dim 128, rope_dim 64; other values give FM_EUNSUPPORTED.
+ * yarn_factor 1 is plain RoPE with frequencies base^(-2j/rope_dim); above 1
+ * the frequencies blend linearly in j from base^(-2j/rope_dim) (below the
+ * fast correction bound, from beta_fast) to that divided by yarn_factor
+ * (above the slow bound, from beta_slow), both bounds taken over
+ * yarn_orig_ctx. */
+typedef struct {
+  int32_t n_layers;      /* 3 */
+  int32_t hidden;        /* 4096 */
+  int32_t q_lora_rank;   /* 1024 */
+  int32_t n_heads;       /* 64 */
+  int32_t head_dim;      /* 128 */
+  int32_t rope_dim;      /* 64: RoPE turns the last rope_dim dims of each head */
+  float rms_eps;         /* 1e-6 */
+  double rope_base;      /* 160000 */
+  double yarn_factor;    /* 1 = plain RoPE */
+  int64_t yarn_orig_ctx; /* 65536 */
+  double yarn_beta_fast; /* 32 */
+  double yarn_beta_slow; /* 1 */
+} fm_config;
+
+/* Device fp32 weights of the three layers, in the order l10, l12, l20,
+ * each row-major [out][in] (a linear map in -> out, no bias):
+ *   wq_a   [q_lora_rank][hidden]
+ *   q_norm [q_lora_rank]                 RMSNorm gain
+ *   wq_b   [n_heads * head_dim][q_lora_rank]; output row 128*h + d is
+ *          element d of head h
+ *   w_proj [n_heads][hidden]             weights_proj */
+typedef struct {
+  const float* wq_a[3];
+  const float* q_norm[3];
+  const float* wq_b[3];
+  const float* w_proj[3];
+} fm_weights;
+
+/* Fills *cfg with the defaults listed in fm_config. */
+void fm_config_default(fm_config* cfg);
+
+/* Creates a context on the current HIP device.  Checks cfg, derives the
+ * RoPE/YaRN frequencies (in double precision) and allocates the workspace
+ * for up to max_batch rows of up to max_n chunks.  max_batch in [1, 4096],
+ * max_n in [1, 2^26].  On success *out receives the context. */
+fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max_batch, int64_t max_n,
+                    fm_ctx** out);
+
+/* Frees the workspace.  Waits for nothing: the caller synchronises any
+ * stream still using the context first.  NULL is a no-op. */
+void fm_destroy(fm_ctx* ctx);
+
+/* Query and weight branches ("Architecture"), all three layers.
+ *   hidden    device fp32 [B][hidden]
+ *   positions device int64 [B], token position of each row (>= 0)
+ *   q_out     device fp32 [3][B][n_heads][head_dim]: q after RoPE and the
+ *             normalized Hadamard transform
+ *   w_out     device fp32 [3][B][n_heads]: fused_w
+ * B in [0, max_batch]. */
+fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* positions, int32_t B, float* q_out,
+                           float* w_out, void* stream);
+
+/* Per-layer score and ensemble ("Architecture" score line, "Joint checkpoint
+ * + ensemble").
+ *   q, w      device fp32, as written by fm_prepare_query
+ *   comp_k    device uint8 [B][N][132] ("compressed_k format"): bytes 0..127
+ *             are OCP float8 e4m3fn codes, bytes 128..131 a little-endian
+ *             fp32 scale; k = decode(code) * scale
+ *   valid_n   device int32 [B] or NULL (= N for every row): chunks at index
+ *             >= valid_n[b] are not read; values are clamped to [0, N]
+ *   mode      FM_ENSEMBLE_MAX or FM_ENSEMBLE_MEAN
+ *   scores    device fp32 [B][N]: ensemble score in [0, 1]; -inf at or
+ *             beyond valid_n
+ *   per_layer device fp32 [3][B][N] or NULL: each layer's sigmoid score
+ *             (the pages' {"l10","l12","l20"} dict); -inf beyond valid_n
+ * B in [0, max_batch], N in [0, max_n]. */
+fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                   const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream);
+
+/* Keep mask of the top_k highest scores of each row ("Usage" top_k=...;
+ * "Inference flow" top-K).  Ties are broken towards the lower chunk index,
+ * so the mask is unique; top_k >= valid_n keeps every valid chunk; top_k 0
+ * keeps none; chunks at or beyond valid_n are never kept.
+ *   scores  device fp32 [B][N] (finite or -inf; NaN is not ordered)
+ *   valid_n device int32 [B] or NULL, as in fm_score
+ *   mask    device uint8 [B][N], written 1 (keep) or 0
+ * top_k >= 0. */
+fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
+                         int32_t top_k, uint8_t* mask, void* stream);
+
+/* Keep mask score > threshold, strictly ("Usage" threshold=...;
+ * "Inference flow" sigmoid > thresh).  Chunks at or beyond valid_n are
+ * never kept.  threshold must be finite. */
+fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
+                              float threshold, uint8_t* mask, void* stream);
+
+/* Message of the last failing call on this thread ("" if none); valid until
+ * the next fm_* call on this thread. */
+const char* fm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H_ */

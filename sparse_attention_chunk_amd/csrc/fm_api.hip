@@ -1,0 +1,259 @@
+// C ABI of libfm (include/fm.h): argument checks, the context and its
+// workspace, and dispatch to the kernel launchers.  Every check runs before
+// anything is enqueued, so a failing call leaves the stream untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fm_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fm_status fail(fm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+fm_status hip_fail(hipError_t e, const char* what) {
+  return fail(FM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Frequencies theta'_j, j < rope_dim/2, in double precision (README
+// "Architecture": RoPE with YaRN, base 160000, on the last rope_dim dims).
+// theta_j = base^(-2j/d).  For yarn_factor s > 1 the frequencies blend
+// linearly in j from theta_j (j <= lo) to theta_j / s (j >= hi), where lo and
+// hi are the indices whose wavelengths complete beta_fast and beta_slow
+// turns over the original context: j(r) = d ln(L0 / (2 pi r)) / (2 ln base),
+// lo = floor(j(beta_fast)), hi = ceil(j(beta_slow)), clamped to [0, d-1];
+// equal bounds are separated by 0.001.
+void rope_frequencies(const fm_config& c, double* out) {
+  const int d = c.rope_dim;
+  const int half = d / 2;
+  const double pi = 3.14159265358979323846;
+  double lo = 0, hi = 1;
+  const bool yarn = c.yarn_factor != 1.0;
+  if (yarn) {
+    auto jr = [&](double turns) {
+      return d * std::log((double)c.yarn_orig_ctx / (turns * 2.0 * pi)) / (2.0 * std::log(c.rope_base));
+    };
+    lo = std::floor(jr(c.yarn_beta_fast));
+    hi = std::ceil(jr(c.yarn_beta_slow));
+    if (lo < 0) lo = 0;
+    if (hi > d - 1) hi = d - 1;
+    if (lo == hi) hi += 0.001;
+  }
+  for (int j = 0; j < half; ++j) {
+    const double theta = std::pow(c.rope_base, -2.0 * j / d);
+    if (!yarn) {
+      out[j] = theta;
+      continue;
+    }
+    double ramp = (j - lo) / (hi - lo);
+    ramp = ramp < 0 ? 0 : (ramp > 1 ? 1 : ramp);
+    out[j] = theta * (1.0 - ramp) + (theta / c.yarn_factor) * ramp;
+  }
+}
+
+fm_status check_ctx(fm_ctx* ctx) {
+  if (!ctx) return fail(FM_EINVAL, "null context");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != ctx->device) return fail(FM_EINVAL, "context belongs to device %d but device %d is current", ctx->device, dev);
+  return FM_OK;
+}
+
+fm_status check_shape(const fm_ctx* ctx, int32_t B, int64_t N, bool with_n) {
+  if (B < 0 || B > ctx->max_batch) return fail(FM_EINVAL, "B = %d outside [0, %d]", B, ctx->max_batch);
+  if (with_n && (N < 0 || N > ctx->max_n))
+    return fail(FM_EINVAL, "N = %lld outside [0, %lld]", (long long)N, (long long)ctx->max_n);
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void fm_config_default(fm_config* cfg) {
+  if (!cfg) return;
+  cfg->n_layers = 3;
+  cfg->hidden = 4096;
+  cfg->q_lora_rank = 1024;
+  cfg->n_heads = 64;
+  cfg->head_dim = 128;
+  cfg->rope_dim = 64;
+  cfg->rms_eps = 1e-6f;
+  cfg->rope_base = 160000.0;
+  cfg->yarn_factor = 1.0;
+  cfg->yarn_orig_ctx = 65536;
+  cfg->yarn_beta_fast = 32.0;
+  cfg->yarn_beta_slow = 1.0;
+}
+
+const char* fm_last_error(void) { return g_err.c_str(); }
+
+fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max_batch, int64_t max_n,
+                    fm_ctx** out) {
+  g_err.clear();
+  if (!cfg || !weights || !out) return fail(FM_EINVAL, "null argument to fm_create");
+  *out = nullptr;
+  using namespace fm;
+  if (cfg->n_layers != kLayers || cfg->hidden != kHidden || cfg->q_lora_rank != kQLora || cfg->n_heads != kHeads ||
+      cfg->head_dim != kHeadDim || cfg->rope_dim != kRopeDim)
+    return fail(FM_EUNSUPPORTED,
+                "compiled for n_layers 3, hidden 4096, q_lora_rank 1024, n_heads 64, head_dim 128, rope_dim 64");
+  if (!(cfg->rms_eps >= 0.f) || !std::isfinite(cfg->rms_eps)) return fail(FM_EINVAL, "rms_eps must be finite and >= 0");
+  if (!(cfg->rope_base > 1.0) || !std::isfinite(cfg->rope_base)) return fail(FM_EINVAL, "rope_base must be > 1");
+  if (!(cfg->yarn_factor >= 1.0) || !std::isfinite(cfg->yarn_factor)) return fail(FM_EINVAL, "yarn_factor must be >= 1");
+  if (cfg->yarn_factor != 1.0 && (cfg->yarn_orig_ctx <= 0 || !(cfg->yarn_beta_fast > 0) || !(cfg->yarn_beta_slow > 0)))
+    return fail(FM_EINVAL, "YaRN needs yarn_orig_ctx > 0 and positive betas");
+  if (max_batch < 1 || max_batch > 4096) return fail(FM_EINVAL, "max_batch = %d outside [1, 4096]", max_batch);
+  if (max_n < 1 || max_n > (int64_t(1) << 26)) return fail(FM_EINVAL, "max_n outside [1, 2^26]");
+  for (int l = 0; l < kLayers; ++l) {
+    if (!weights->wq_a[l] || !weights->q_norm[l] || !weights->wq_b[l] || !weights->w_proj[l])
+      return fail(FM_EINVAL, "null weight pointer (layer %d)", l);
+    if (!aligned(weights->wq_a[l], 16) || !aligned(weights->wq_b[l], 16) || !aligned(weights->w_proj[l], 16) ||
+        !aligned(weights->q_norm[l], 4))
+      return fail(FM_EINVAL, "weights must be 16-byte aligned (q_norm 4-byte)");
+  }
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  // One allocation, each buffer 256-byte aligned.
+  const size_t mb = (size_t)max_batch;
+  const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
+  size_t sizes[8] = {
+      sizeof(float) * kSplitK1 * kLayers * mb * kProj1Out,  // proj1_part
+      sizeof(float) * kLayers * mb * kQLora,                // a_hat
+      sizeof(float) * kLayers * mb * kHeads * kHeadDim,     // q_lin
+      sizeof(double) * (kRopeDim / 2),                      // rope_freq
+      (size_t)16 * kQFrags * 64 * mb,                       // qpack (f16x8 per lane)
+      sizeof(uint32_t) * mb * kSelBins,                     // sel_hist
+      sizeof(uint32_t) * mb * 4,                            // sel_state
+      sizeof(uint32_t) * mb * sel_blocks,                   // sel_eq
+  };
+  size_t offs[8];
+  size_t total = 0;
+  for (int i = 0; i < 8; ++i) {
+    offs[i] = total;
+    total += (sizes[i] + 255) & ~(size_t)255;
+  }
+  void* base = nullptr;
+  e = hipMalloc(&base, total);
+  if (e != hipSuccess) return fail(FM_ENOMEM, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
+
+  fm_ctx* ctx = new fm_ctx();
+  ctx->device = dev;
+  ctx->cfg = *cfg;
+  ctx->weights = *weights;
+  ctx->max_batch = max_batch;
+  ctx->max_n = max_n;
+  ctx->ws_base = base;
+  ctx->ws_bytes = total;
+  char* p = (char*)base;
+  ctx->ws.proj1_part = (float*)(p + offs[0]);
+  ctx->ws.a_hat = (float*)(p + offs[1]);
+  ctx->ws.q_lin = (float*)(p + offs[2]);
+  ctx->ws.rope_freq = (double*)(p + offs[3]);
+  ctx->ws.qpack = (void*)(p + offs[4]);
+  ctx->ws.sel_hist = (uint32_t*)(p + offs[5]);
+  ctx->ws.sel_state = (uint32_t*)(p + offs[6]);
+  ctx->ws.sel_eq = (uint32_t*)(p + offs[7]);
+
+  double freq[kRopeDim / 2];
+  rope_frequencies(*cfg, freq);
+  e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(base);
+    delete ctx;
+    return hip_fail(e, "upload of RoPE frequencies");
+  }
+  *out = ctx;
+  return FM_OK;
+}
+
+void fm_destroy(fm_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->ws_base) (void)hipFree(ctx->ws_base);
+  delete ctx;
+}
+
+fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* positions, int32_t B, float* q_out,
+                           float* w_out, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, 0, false)) != FM_OK) return st;
+  if (B == 0) return FM_OK;
+  if (!hidden || !positions || !q_out || !w_out) return fail(FM_EINVAL, "null pointer to fm_prepare_query");
+  if (!aligned(hidden, 16) || !aligned(q_out, 16) || !aligned(w_out, 16) || !aligned(positions, 8))
+    return fail(FM_EINVAL, "hidden, q_out, w_out must be 16-byte aligned, positions 8-byte aligned");
+  hipError_t e = fm::launch_prepare_query(ctx->cfg, ctx->weights, ctx->ws, ctx->max_batch, hidden, positions, B, q_out,
+                                          w_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_prepare_query launch");
+  return FM_OK;
+}
+
+fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                   const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (mode != FM_ENSEMBLE_MAX && mode != FM_ENSEMBLE_MEAN) return fail(FM_EINVAL, "unknown ensemble mode %d", (int)mode);
+  if (B == 0 || N == 0) return FM_OK;
+  if (!q || !w || !comp_k || !scores) return fail(FM_EINVAL, "null pointer to fm_score");
+  if (!aligned(q, 16) || !aligned(w, 16) || !aligned(comp_k, 4) || !aligned(scores, 4) ||
+      (per_layer && !aligned(per_layer, 4)) || (valid_n && !aligned(valid_n, 4)))
+    return fail(FM_EINVAL, "q, w must be 16-byte aligned; comp_k, scores, per_layer, valid_n 4-byte aligned");
+  hipError_t e = fm::launch_score(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, scores, per_layer,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_score launch");
+  return FM_OK;
+}
+
+fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
+                         int32_t top_k, uint8_t* mask, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (top_k < 0) return fail(FM_EINVAL, "top_k = %d < 0", top_k);
+  if (B == 0 || N == 0) return FM_OK;
+  if (!scores || !mask) return fail(FM_EINVAL, "null pointer to fm_select_topk");
+  if (!aligned(scores, 4) || (valid_n && !aligned(valid_n, 4)))
+    return fail(FM_EINVAL, "scores and valid_n must be 4-byte aligned");
+  hipError_t e = fm::launch_select_topk(ctx->ws, scores, B, N, valid_n, top_k, mask, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_select_topk launch");
+  return FM_OK;
+}
+
+fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
+                              float threshold, uint8_t* mask, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (!std::isfinite(threshold)) return fail(FM_EINVAL, "threshold must be finite");
+  if (B == 0 || N == 0) return FM_OK;
+  if (!scores || !mask) return fail(FM_EINVAL, "null pointer to fm_select_threshold");
+  if (!aligned(scores, 4) || (valid_n && !aligned(valid_n, 4)))
+    return fail(FM_EINVAL, "scores and valid_n must be 4-byte aligned");
+  hipError_t e = fm::launch_select_threshold(scores, B, N, valid_n, threshold, mask, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_select_threshold launch");
+  return FM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations of libfm: compiled dimensions, the context layout and
+// the launchers each kernel file provides to the C ABI layer (fm_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "fm.h"
+
+namespace fm {
+
+// Compiled layer dimensions (README "Architecture"; HEAD_DIM from the
+// 132-byte record of "compressed_k format").
+constexpr int kLayers = 3;
+constexpr int kHidden = 4096;
+constexpr int kQLora = 1024;
+constexpr int kHeads = 64;
+constexpr int kHeadDim = 128;
+constexpr int kRopeDim = 64;
+constexpr int kRecord = kHeadDim + 4;
+
+// First projection: wq_a rows [0, 1024) and weights_proj rows [1024, 1088)
+// share one pass over `hidden`, split over K in kSplitK1 slices whose
+// partial sums the RMSNorm kernel adds in a fixed order.
+constexpr int kProj1Out = kQLora + kHeads;
+constexpr int kSplitK1 = 4;
+
+// Score kernel: per request row the packed fp16 queries are 48 MFMA
+// fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves.
+constexpr int kQFrags = kLayers * 4 * 4;
+
+// Top-K selection: a block covers kSelSlice consecutive chunks of one row.
+constexpr int kSelThreads = 256;
+constexpr int kSelItems = 16;
+constexpr int kSelSlice = kSelThreads * kSelItems;
+constexpr int kSelBins = 2048;
+
+struct Workspace {
+  float* proj1_part = nullptr;   // [kSplitK1][3][max_batch][kProj1Out]
+  float* a_hat = nullptr;        // [3][max_batch][kQLora]
+  float* q_lin = nullptr;        // [3][max_batch][kHeads * kHeadDim]
+  double* rope_freq = nullptr;   // [kRopeDim / 2]
+  void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16
+  uint32_t* sel_hist = nullptr;  // [max_batch][kSelBins]
+  uint32_t* sel_state = nullptr; // [max_batch][4]
+  uint32_t* sel_eq = nullptr;    // [max_batch][ceil(max_n / kSelSlice)]
+};
+
+// Launchers.  Shapes are validated by the caller; each returns the launch
+// status (hipGetLastError after the launches).
+hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, const Workspace& ws, int max_batch,
+                                const float* hidden, const int64_t* positions, int B, float* q_out, float* w_out,
+                                hipStream_t stream);
+
+hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
+                        const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream);
+
+hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
+                              int32_t top_k, uint8_t* mask, hipStream_t stream);
+
+hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
+                                   uint8_t* mask, hipStream_t stream);
+
+}  // namespace fm
+
+struct fm_ctx {
+  int device = 0;
+  fm_config cfg{};
+  fm_weights weights{};
+  int32_t max_batch = 0;
+  int64_t max_n = 0;
+  fm::Workspace ws{};
+  void* ws_base = nullptr;  // one allocation holding every workspace buffer
+  size_t ws_bytes = 0;
+};

@@ -1,0 +1,150 @@
+"""The retriever interface of the FlashMemory DS-V4 README ("Usage") over libfm.
+
+    model = FlashMemoryRetriever(weights)                  # device fp32 weights
+    per_layer = model(hidden, comp_k, positions)           # {"l10","l12","l20"}: [B, N]
+    scores = model.ensemble(hidden, comp_k, positions, mode="max")     # [B, N]
+    keep = model.select_topk(hidden, comp_k, positions, top_k=512)     # bool [B, N]
+    keep = model.select_topk(hidden, comp_k, positions, threshold=0.5)
+
+Also the three stages on their own (prepare_query, score, keep_topk /
+keep_threshold).  Torch only allocates outputs and supplies the stream; the
+arithmetic runs in libfm.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+LAYER_NAMES = ("l10", "l12", "l20")
+MODES = {"max": _lib.FM_ENSEMBLE_MAX, "mean": _lib.FM_ENSEMBLE_MEAN}
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+class FlashMemoryRetriever:
+    """Three indexer layers (l10, l12, l20) behind one libfm context.
+
+    weights: three dicts (l10, l12, l20) of contiguous device float32
+    tensors "wq_a" [1024, 4096], "q_norm" [1024], "wq_b" [8192, 1024],
+    "w_proj" [64, 4096].  They are borrowed and must outlive the object.
+    yarn: optional dict with factor, orig_ctx, beta_fast, beta_slow.
+    """
+
+    def __init__(self, weights, max_batch: int = 64, max_n: int = 262144, yarn: dict | None = None,
+                 rms_eps: float | None = None, rope_base: float | None = None):
+        if len(weights) != 3:
+            raise ValueError("three layers (l10, l12, l20) expected")
+        self._weights = [{k: _need(lw[k], torch.float32, f"{k}[{i}]") for k in ("wq_a", "q_norm", "wq_b", "w_proj")}
+                         for i, lw in enumerate(weights)]
+        cfg = _lib.config_default()
+        if yarn:
+            cfg.yarn_factor = float(yarn.get("factor", 1.0))
+            cfg.yarn_orig_ctx = int(yarn.get("orig_ctx", 65536))
+            cfg.yarn_beta_fast = float(yarn.get("beta_fast", 32.0))
+            cfg.yarn_beta_slow = float(yarn.get("beta_slow", 1.0))
+        if rms_eps is not None:
+            cfg.rms_eps = rms_eps
+        if rope_base is not None:
+            cfg.rope_base = rope_base
+        w = _lib.FmWeights()
+        for i, lw in enumerate(self._weights):
+            w.wq_a[i] = lw["wq_a"].data_ptr()
+            w.q_norm[i] = lw["q_norm"].data_ptr()
+            w.wq_b[i] = lw["wq_b"].data_ptr()
+            w.w_proj[i] = lw["w_proj"].data_ptr()
+        self.config = cfg
+        self.device = self._weights[0]["wq_a"].device
+        self.max_batch, self.max_n = max_batch, max_n
+        with torch.cuda.device(self.device):
+            self._ctx = _lib.fm_create(cfg, w, max_batch, max_n)
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            torch.cuda.synchronize(self.device)
+            _lib.fm_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def ctx(self) -> int:
+        return self._ctx
+
+    # ----------------------------------------------------------------- stages
+    def prepare_query(self, hidden, positions):
+        _need(hidden, torch.float32, "hidden", 2)
+        _need(positions, torch.int64, "positions", 1)
+        B = hidden.shape[0]
+        q = torch.empty((3, B, 64, 128), dtype=torch.float32, device=hidden.device)
+        w = torch.empty((3, B, 64), dtype=torch.float32, device=hidden.device)
+        _lib.fm_prepare_query(self._ctx, hidden, positions, B, q, w)
+        return q, w
+
+    def score(self, q, w, comp_k, valid_n=None, mode="max", per_layer=False):
+        _need(comp_k, torch.uint8, "comp_k", 3)
+        _need(q, torch.float32, "q", 4)
+        _need(w, torch.float32, "w", 3)
+        B, N = comp_k.shape[0], comp_k.shape[1]
+        if comp_k.shape[2] != 132:
+            raise ValueError("comp_k records must be 132 bytes")
+        if valid_n is not None:
+            _need(valid_n, torch.int32, "valid_n", 1)
+        scores = torch.empty((B, N), dtype=torch.float32, device=comp_k.device)
+        pl = torch.empty((3, B, N), dtype=torch.float32, device=comp_k.device) if per_layer else None
+        _lib.fm_score(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], scores, pl)
+        return (scores, pl) if per_layer else scores
+
+    def keep_topk(self, scores, top_k: int, valid_n=None):
+        _need(scores, torch.float32, "scores", 2)
+        B, N = scores.shape
+        mask = torch.empty((B, N), dtype=torch.bool, device=scores.device)
+        _lib.fm_select_topk(self._ctx, scores, B, N, valid_n, int(top_k), mask)
+        return mask
+
+    def keep_threshold(self, scores, threshold: float, valid_n=None):
+        _need(scores, torch.float32, "scores", 2)
+        B, N = scores.shape
+        mask = torch.empty((B, N), dtype=torch.bool, device=scores.device)
+        _lib.fm_select_threshold(self._ctx, scores, B, N, valid_n, float(threshold), mask)
+        return mask
+
+    # ----------------------------------------------------- the pages' interface
+    def __call__(self, hidden, comp_k, positions, valid_n=None):
+        q, w = self.prepare_query(hidden, positions)
+        _, pl = self.score(q, w, comp_k, valid_n, "max", per_layer=True)
+        return {name: pl[i] for i, name in enumerate(LAYER_NAMES)}
+
+    def ensemble(self, hidden, comp_k, positions, mode="max", valid_n=None):
+        q, w = self.prepare_query(hidden, positions)
+        return self.score(q, w, comp_k, valid_n, mode)
+
+    def select_topk(self, hidden, comp_k, positions, top_k=None, threshold=None, mode="max", valid_n=None):
+        if (top_k is None) == (threshold is None):
+            raise ValueError("pass exactly one of top_k and threshold")
+        scores = self.ensemble(hidden, comp_k, positions, mode, valid_n)
+        if top_k is not None:
+            return self.keep_topk(scores, top_k, valid_n)
+        return self.keep_threshold(scores, threshold, valid_n)
+
+
+def weights_to_device(weights_np, device="cuda"):
+    """Numpy fp32 layer dicts -> device tensors (contiguous)."""
+    return [{k: torch.from_numpy(lw[k]).to(device).contiguous() for k in ("wq_a", "q_norm", "wq_b", "w_proj")}
+            for lw in weights_np]
+

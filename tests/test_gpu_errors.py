@@ -1,0 +1,94 @@
+"""Error conventions of the C ABI on a live context: every failing call
+returns its status before enqueueing anything, so outputs keep their
+sentinel contents."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import sparse_attention_chunk_amd as fm
+    from sparse_attention_chunk_amd import _lib
+    r = fm.FlashMemoryRetriever(fm.weights_to_device(synth.make_weights()), max_batch=4, max_n=1000)
+    yield r, _lib
+    r.close()
+
+
+def test_argument_errors_enqueue_nothing(env):
+    r, L = env
+    lib, ctx = L.LIB, r.ctx
+    EINVAL = L.FM_EINVAL
+    B, N = 2, 100
+    q = torch.zeros((3, B, 64, 128), device="cuda")
+    w = torch.zeros((3, B, 64), device="cuda")
+    ck = torch.zeros((B, N, 132), dtype=torch.uint8, device="cuda")
+    ck_big = torch.zeros((B * N * 132 + 16,), dtype=torch.uint8, device="cuda")
+    scores = torch.full((B, N), 7.0, device="cuda")
+    mask = torch.full((B, N), 9, dtype=torch.uint8, device="cuda")
+    hidden = torch.zeros((B, 4096), device="cuda")
+    pos = torch.zeros((B,), dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    P = L.ptr
+
+    cases = [
+        lib.fm_score(ctx, None, P(w), P(ck), B, N, None, 0, P(scores), None, s),             # null q
+        lib.fm_score(ctx, P(q), P(w), None, B, N, None, 0, P(scores), None, s),              # null comp_k
+        lib.fm_score(ctx, P(q), P(w), P(ck), 5, N, None, 0, P(scores), None, s),             # B > max_batch
+        lib.fm_score(ctx, P(q), P(w), P(ck), -1, N, None, 0, P(scores), None, s),            # B < 0
+        lib.fm_score(ctx, P(q), P(w), P(ck), B, 1001, None, 0, P(scores), None, s),          # N > max_n
+        lib.fm_score(ctx, P(q), P(w), P(ck), B, N, None, 2, P(scores), None, s),             # bad mode
+        lib.fm_score(ctx, P(q), P(w), P(ck_big) + 1, B, N, None, 0, P(scores), None, s),     # misaligned comp_k
+        lib.fm_score(ctx, P(q) + 4, P(w), P(ck), B, N, None, 0, P(scores), None, s),         # q not 16-aligned
+        lib.fm_select_topk(ctx, P(scores), B, N, None, -1, P(mask), s),                      # top_k < 0
+        lib.fm_select_topk(ctx, P(scores), B, N, None, 5, None, s),                          # null mask
+        lib.fm_select_threshold(ctx, P(scores), B, N, None, float("nan"), P(mask), s),       # NaN threshold
+        lib.fm_select_threshold(ctx, P(scores), B, N, None, float("inf"), P(mask), s),       # inf threshold
+        lib.fm_prepare_query(ctx, P(hidden), P(pos), 5, P(q), P(w), s),                      # B > max_batch
+        lib.fm_prepare_query(ctx, P(hidden), None, B, P(q), P(w), s),                        # null positions
+    ]
+    assert cases == [EINVAL] * len(cases)
+    assert L.last_error() != ""
+    torch.cuda.synchronize()
+    assert torch.all(scores == 7.0) and torch.all(mask == 9)
+
+
+def test_success_clears_last_error(env):
+    r, L = env
+    L.LIB.fm_select_topk(r.ctx, None, 1, 1, None, -1, None, None)
+    assert L.last_error() != ""
+    s = torch.rand((1, 10), device="cuda")
+    m = r.keep_topk(s, 3)
+    torch.cuda.synchronize()
+    assert L.last_error() == ""
+    assert int(m.sum()) == 3
+
+
+def test_fm_error_raised_by_binding(env):
+    r, L = env
+    with pytest.raises(L.FmError) as ei:
+        L.fm_select_topk(r.ctx, torch.zeros((1, 2000), device="cuda"), 1, 2000, None, 1,
+                         torch.zeros((1, 2000), dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == L.FM_EINVAL and "N = 2000" in str(ei.value)
+
+
+def test_create_unsupported_and_bad_sizes(env):
+    r, L = env
+    out = ctypes.c_void_p()
+    w = L.FmWeights()
+    for i in range(3):
+        w.wq_a[i] = w.q_norm[i] = w.wq_b[i] = w.w_proj[i] = r._weights[i]["wq_a"].data_ptr()
+    cfg = L.config_default()
+    assert L.LIB.fm_create(ctypes.byref(cfg), ctypes.byref(w), 4097, 10, ctypes.byref(out)) == L.FM_EINVAL
+    assert L.LIB.fm_create(ctypes.byref(cfg), ctypes.byref(w), 4, (1 << 26) + 1, ctypes.byref(out)) == L.FM_EINVAL
+    cfg.head_dim = 64
+    assert L.LIB.fm_create(ctypes.byref(cfg), ctypes.byref(w), 4, 10, ctypes.byref(out)) == L.FM_EUNSUPPORTED
+    assert out.value is None
+    np.testing.assert_equal(L.FM_OK, 0)

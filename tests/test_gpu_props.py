@@ -1,0 +1,189 @@
+"""GPU properties and edge cases through the C ABI: determinism, chunk
+permutation, row independence, ties, zero and negative-scale records,
+ragged and degenerate sizes, and the selection kernels on constructed
+scores (compared exactly with the oracle's selection of the same scores)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fm_cases import SCORE_TOL, max_score_err, oracle_scores, report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def weights_np():
+    return synth.make_weights()
+
+
+@pytest.fixture(scope="module")
+def retr(weights_np):
+    import sparse_attention_chunk_amd as fm
+    r = fm.FlashMemoryRetriever(fm.weights_to_device(weights_np), max_batch=64, max_n=1 << 17)
+    yield r
+    r.close()
+
+
+@pytest.fixture(scope="module")
+def qw(weights_np):
+    """Oracle queries of 4 rows (cfg 3 hidden states, random positions)."""
+    wl = synth.WORKLOADS[3]
+    hidden = synth.make_hidden(wl)[:4]
+    pos = synth.make_positions(wl)[:4]
+    q, w = oracle.prepare_query(weights_np, hidden, pos, oracle.OracleConfig())
+    return q, w
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def records(n, seed, rows=1):
+    rng = np.random.default_rng(seed)
+    return np.stack([synth.encode_records(rng.standard_normal((n, 128)).astype(np.float32)) for _ in range(rows)])
+
+
+def run(retr, q, w, comp_k, vn=None, mode="max"):
+    qd, wd = dev(q.astype(np.float32)), dev(w.astype(np.float32))
+    s, p = retr.score(qd, wd, dev(comp_k), None if vn is None else dev(np.asarray(vn, np.int32)), mode,
+                      per_layer=True)
+    return host(s), host(p)
+
+
+def test_bit_identical_run_to_run(retr, qw):
+    q, w = qw
+    ck = records(5000, 1, rows=2)
+    a, pa = run(retr, q[:, :2], w[:, :2], ck)
+    b, pb = run(retr, q[:, :2], w[:, :2], ck)
+    assert np.array_equal(a, b) and np.array_equal(pa, pb)
+
+
+def test_chunk_permutation_permutes_scores(retr, qw):
+    q, w = qw
+    ck = records(3000, 2)
+    perm = np.random.default_rng(3).permutation(3000)
+    a, _ = run(retr, q[:, :1], w[:, :1], ck)
+    b, _ = run(retr, q[:, :1], w[:, :1], ck[:, perm])
+    assert np.array_equal(a[0, perm], b[0])
+
+
+def test_row_independence(retr, qw):
+    q, w = qw
+    ck = records(2048, 4, rows=3)
+    a, _ = run(retr, q[:, :3], w[:, :3], ck)
+    b, _ = run(retr, q[:, 1:2], w[:, 1:2], ck[1:2])
+    assert np.array_equal(a[1], b[0])
+
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4095, 4097, 5000])
+def test_ragged_sizes_match_oracle(retr, qw, n):
+    q, w = qw
+    ck = records(n, 10 + n, rows=2)
+    vn = [n, max(0, n // 3)]
+    ck[1, vn[1]:] = 0xFF                      # tail must not be read
+    s, p = run(retr, q[:, :2], w[:, :2], ck, vn)
+    per_ref, ens_ref = oracle_scores(ck, q[:, :2], w[:, :2], vn, "max")
+    e = max(max_score_err(s, ens_ref), max_score_err(p, per_ref))
+    report(f"ragged n={n}", max_abs=e)
+    assert e <= SCORE_TOL
+
+
+def test_empty_rows_and_zero_valid(retr, qw, fm_lib):
+    q, w = qw
+    ck = records(64, 5, rows=2)
+    s, p = run(retr, q[:, :2], w[:, :2], ck, [0, 64])
+    assert np.all(np.isneginf(s[0])) and np.all(np.isneginf(p[:, 0]))
+    mask = retr.keep_topk(dev(s), 10, dev(np.array([0, 64], np.int32)))
+    m = host(mask)
+    assert m[0].sum() == 0 and m[1].sum() == 10
+    # B == 0 and N == 0 are empty problems: FM_OK, nothing written
+    assert fm_lib.LIB.fm_score(retr.ctx, 0, 0, 0, 0, 5, None, 0, 0, None, None) == 0
+    assert fm_lib.LIB.fm_select_topk(retr.ctx, 0, 3, 0, None, 5, 0, None) == 0
+
+
+@pytest.fixture(scope="module")
+def fm_lib():
+    from sparse_attention_chunk_amd import _lib
+    return _lib
+
+
+def test_zero_records_score_exactly_half(retr, qw):
+    q, w = qw
+    ck = np.zeros((1, 100, 132), np.uint8)     # codes 0, scale 0
+    s, p = run(retr, q[:, :1], w[:, :1], ck)
+    assert np.all(s == 0.5) and np.all(p == 0.5)
+
+
+def test_negative_and_mixed_scales(retr, qw):
+    q, w = qw
+    ck = records(1000, 6)
+    sc = ck[0, :, 128:].copy().view("<f4")[:, 0]
+    sc[::3] *= -1.0                            # every third chunk: negative scale
+    ck[0, :, 128:] = sc.astype("<f4").view(np.uint8).reshape(-1, 4)
+    s, p = run(retr, q[:, :1], w[:, :1], ck)
+    per_ref, ens_ref = oracle_scores(ck, q[:, :1], w[:, :1], [1000], "max")
+    e = max(max_score_err(s, ens_ref), max_score_err(p, per_ref))
+    report("negative scales", max_abs=e)
+    assert e <= SCORE_TOL
+
+
+def test_identical_records_tie_to_lowest_index(retr, qw):
+    q, w = qw
+    one = records(1, 7)[0, 0]
+    ck = np.tile(one, (1, 300, 1))
+    s, _ = run(retr, q[:, :1], w[:, :1], ck)
+    assert np.all(s[0] == s[0, 0])
+    m = host(retr.keep_topk(dev(s), 37))
+    assert list(np.nonzero(m[0])[0]) == list(range(37))
+
+
+# --------------------------------------------------------------------------- selection on constructed scores
+
+@pytest.mark.parametrize("n,k", [(1, 1), (10, 3), (4096, 512), (4097, 4096), (70000, 1024), (131072, 512)])
+def test_topk_many_ties_exact(retr, n, k):
+    rng = np.random.default_rng(n + k)
+    s = np.round(rng.uniform(0, 1, (3, n)), 3).astype(np.float32)   # heavy ties
+    vn = np.array([n, max(1, n // 2), 0], np.int32)
+    m = host(retr.keep_topk(dev(s), k, dev(vn)))
+    for b in range(3):
+        assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), int(vn[b]), k))
+
+
+def test_topk_all_equal_and_degenerate_k(retr):
+    s = np.full((2, 9000), 0.25, np.float32)
+    m = host(retr.keep_topk(dev(s), 4500))
+    assert all(list(np.nonzero(m[b])[0]) == list(range(4500)) for b in range(2))
+    assert host(retr.keep_topk(dev(s), 0)).sum() == 0
+    assert host(retr.keep_topk(dev(s), 9000)).all()
+    assert host(retr.keep_topk(dev(s), 100000)).all()
+
+
+def test_topk_with_negative_inf_and_signed_values(retr):
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal((2, 5000)).astype(np.float32)
+    s[0, ::7] = -np.inf
+    s[1, :10] = 0.0
+    s[1, 10:20] = -0.0
+    for k in (1, 100, 4000, 4999):
+        m = host(retr.keep_topk(dev(s), k))
+        for b in range(2):
+            assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), 5000, k)), (b, k)
+
+
+@pytest.mark.parametrize("tau", [0.5, 0.0, 0.9])
+def test_threshold_strict_exact(retr, tau):
+    rng = np.random.default_rng(12)
+    s = np.round(rng.uniform(0, 1, (4, 10001)), 2).astype(np.float32)
+    s[0, :50] = np.float32(tau)
+    vn = np.array([10001, 5000, 0, 1], np.int32)
+    m = host(retr.keep_threshold(dev(s), tau, dev(vn)))
+    for b in range(4):
+        assert np.array_equal(m[b].astype(np.uint8), oracle.select_threshold(s[b].astype(np.float64), int(vn[b]), tau))
