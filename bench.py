@@ -1,0 +1,245 @@
+"""Benchmark of the Memory-Indexer scoring pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = the whole pass over one batch: fm_prepare_query (query and weight
+branches of the three layers) + fm_score (3-layer fused score, max
+ensemble) + fm_select_topk (top-512 per row), on the B=30, N=262144
+workload (a 1M-token context at 4x compression, concurrency 30), synthetic
+seeded inputs already resident in HBM.  Prints one JSON line.
+
+`roofline` describes the score kernel (the dominant one, MFMA-bound at
+49152 flop per chunk); its duration comes from HIP events around each
+fm_score call on the stream the kernels run on.  `traffic` is read from the
+committed rocprofv3 counter summary when that summary was taken on the
+current score-kernel source, else null.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunks scored/s (3-layer fused score + top-K) and % of MFMA/HBM roofline"
+WORKLOAD_ID = 5
+TOP_K = 512
+FLOP_PER_CHUNK = 3 * 64 * 128 * 2      # 49152 MFMA flop
+SCORE_BYTES_PER_CHUNK = 132 + 4        # record read + ensemble score written
+PEAK_F16_TFLOPS = 2500.0               # MI355X dense f16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+SCORE_SRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc", "fm_score.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_b30_n262144_pmc.txt")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling FETCH_SIZE/WRITE_SIZE counters)")
+    return ap.parse_args(argv)
+
+
+def source_digest() -> str:
+    with open(SCORE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(chunks_per_launch: int):
+    """HBM bytes per score launch from the committed counter summary, or None
+    if it is missing or was taken on another version of the score kernel."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("score_source_sha256") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(budget_s: float):
+    """The oracle, as it stands, on whole rows of the workload until the time
+    budget is spent (at least one row); chunks/s over the rows done."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl = synth.WORKLOADS[WORKLOAD_ID]
+    weights = synth.make_weights()
+    hidden = synth.make_hidden(wl)
+    pos = synth.make_positions(wl)
+    cfg = oracle.OracleConfig()
+    rows = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while rows < wl.batch:
+        comp = synth.make_comp_k(wl, rows=[rows])[0]   # generation is outside the timed part
+        t1 = time.perf_counter()
+        oracle.run_row(weights, hidden[rows], int(pos[rows]), comp, cfg, mode="max", top_k=TOP_K)
+        elapsed += time.perf_counter() - t1
+        rows += 1
+        if elapsed >= budget_s:
+            break
+    _ = t0
+    return {"value": rows * wl.n_chunks / elapsed, "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {wl.batch} rows x {wl.n_chunks} chunks (query prep, 3-layer score, max "
+                      f"ensemble, top-{TOP_K}), fp64 numpy, {elapsed:.1f} s",
+            "_cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the scoring pass is built and timed on a single MI355X; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_attention_chunk_amd as fm
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of float32
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 4 * n, "copies": 3}))
+        return 0
+
+    wl = synth.WORKLOADS[WORKLOAD_ID]
+    B, N = wl.batch, wl.n_chunks
+    t_gen = time.perf_counter()
+    weights = fm.weights_to_device(synth.make_weights())
+    hidden = torch.from_numpy(synth.make_hidden(wl)).cuda()
+    pos = torch.from_numpy(synth.make_positions(wl)).cuda()
+    comp_k = torch.from_numpy(synth.make_comp_k(wl)).cuda()
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"# inputs ready in {t_gen:.1f} s: comp_k {tuple(comp_k.shape)}", file=sys.stderr, flush=True)
+
+    r = fm.FlashMemoryRetriever(weights, max_batch=B, max_n=N)
+    q = torch.empty((3, B, 64, 128), device="cuda")
+    w = torch.empty((3, B, 64), device="cuda")
+    scores = torch.empty((B, N), device="cuda")
+    mask = torch.empty((B, N), dtype=torch.bool, device="cuda")
+    L = fm._lib
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
+        if ev is not None:
+            ev[2].record(stream)
+        L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prep = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
+    score = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+    sel = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
+    s_step = wall / args.steps
+    chunks = B * N
+    t_score = float(score.mean())
+    achieved = FLOP_PER_CHUNK * chunks / t_score / 1e12
+    traffic = read_traffic(chunks)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu_model = cpu.pop("_cpu_model") if cpu else None
+    r.close()
+
+    out = {
+        "metric": METRIC,
+        "value": chunks / s_step,
+        "unit": "chunks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "n_chunks": N, "layers": 3, "heads": 64, "head_dim": 128,
+                   "q_lora_rank": 1024, "hidden": 4096, "ensemble": "max", "top_k": TOP_K, "positions": 4 * N},
+        "roofline": {
+            "kernel": "score_kernel (fm_score: q pack + fused 3-layer score)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_F16_TFLOPS,
+            "traffic": traffic,
+            "hbm_algorithmic_gbs": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9,
+            "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9 / PEAK_HBM_GBS,
+        },
+        "cpu_baseline": cpu,
+        "breakdown_us": {"prepare_query": float(prep.mean() * 1e6), "score": t_score * 1e6,
+                         "select_topk": float(sel.mean() * 1e6),
+                         "score_p10": float(np.percentile(score, 10) * 1e6),
+                         "score_p90": float(np.percentile(score, 90) * 1e6)},
+        "score_only_chunks_per_s": chunks / t_score,
+        "host_cpu": cpu_model,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

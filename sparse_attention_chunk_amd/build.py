@@ -23,7 +23,9 @@ SOURCES = ["fm_api.hip", "fm_query.hip", "fm_score.hip", "fm_select.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 vector ops stay off for every HIP file.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: the epilogue reads them every tile
+                "-mllvm", "--amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -7,12 +7,16 @@
 //
 // Per request row this is a [N x 128] x [128 x 192] contraction (3 layers x
 // 64 heads), 49152 flop per 132-byte chunk, on the 16x16x32 f16 MFMA.
+//
 // Exact-algebra choices that keep it within the fp64 result:
 //   - the e4m3 codes are converted exactly to f16 (every finite e4m3 value
-//     is an f16 value); the fp32 scale is applied to the fp32 head sum, not
-//     folded into the operand: relu(s x) = |s| relu(sign(s) x), and a
-//     negative scale flips the decoded operand's signs instead;
-//   - q is rounded once to f16 (11-bit significand).
+//     is an f16 value) and the fp32 scale s multiplies the fp32 head sum
+//     instead of the operand.  With x_h = code . q_h:
+//       sum_h w_h relu(s x_h) = s * sum_h w_h med3(x_h, 0, B),
+//     B = +inf for s >= 0 (relu) and -inf for s < 0 (min(x, 0)), so a scale
+//     of either sign costs nothing extra;
+//   - q is rounded once to f16 (11-bit significand);
+//   - max ensemble: max_l sigmoid(t_l) = sigmoid(max_l t_l), one sigmoid.
 #include "fm_internal.h"
 
 namespace fm {
@@ -22,8 +26,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kTile = 16;                        // chunks per MFMA column tile
+constexpr int kTileBytes = kTile * kRecord;      // 2112
+constexpr int kTilesPerWave = 65;                // 8 m + 1: the pipeline below runs in groups of 8
+constexpr int kCPW = kTilesPerWave * kTile;      // 1040 chunks per wave
+constexpr int kRing = 8;                         // register ring of record tiles
+constexpr int kAhead = 6;                        // tile i + 6 is requested in the phase of tile i
 
 // MFMA 16x16x32 f16 operand layout: lane l supplies A[l%16][8(l/16) + e] and
 // B[8(l/16) + e][l%16], e = 0..7, and receives C[4(l/16) + r][l%16].
@@ -43,26 +53,24 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* q, int B, f16x
   const int head = 16 * mt + (lane & 15);
   const int d0 = 32 * (lane >> 4) + 8 * t;
   const float* src = q + (((size_t)layer * B + b) * kHeads + head) * kHeadDim + d0;
-  f16x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (_Float16)src[e];
+  const float4 v0 = *(const float4*)src;
+  const float4 v1 = *(const float4*)(src + 4);
+  f16x8 v = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
+             (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
   qpack[gid] = v;
 }
 
-__device__ inline f16x8 decode8(uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ f16x8 decode8(uint32_t lo, uint32_t hi) {
   // four 2-code conversions; scale 1.0 leaves the value unchanged
   const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
   const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
   const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
   const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  f16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Sum over the four lane groups {l, l^16, l^32, l^48} (every lane gets it).
-__device__ inline float sum4groups(float v) {
+__device__ __forceinline__ float sum4groups(float v) {
   {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -74,21 +82,132 @@ __device__ inline float sum4groups(float v) {
   return v;
 }
 
-__device__ inline float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
 
-// grid = (ceil(N / (4 * CPW)), B), block = 256: wave w of block x scores
-// chunks [(4x + w) CPW, +CPW) of row blockIdx.y, 16 chunks per step.
-template <int CPW>
-__global__ __launch_bounds__(256) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
-                                                    const uint8_t* __restrict__ comp_k, int B, int64_t N,
-                                                    const int32_t* __restrict__ valid_n, int mode,
-                                                    float* __restrict__ scores, float* __restrict__ per_layer) {
+struct RawTile {
+  u32x4 lo, hi;  // this lane's 32 code bytes
+  float s;       // the chunk's scale
+};
+
+struct Ctx {
+  __amdgpu_buffer_rsrc_t rec;            // records of this wave's chunks; reads past them return 0
+  __amdgpu_buffer_rsrc_t out;            // scores of this wave's chunks; writes past them are dropped
+  __amdgpu_buffer_rsrc_t pl[kLayers];    // per-layer scores of this wave's chunks (when requested)
+  uint32_t lane_rec_off;                 // 132 c + 32 g
+  uint32_t lane_scale_off;               // 132 c + 128
+  uint32_t lane_out_off;                 // 4 c in lane group 0, out of range elsewhere
+  uint32_t lane_pl_off[kLayers];         // 4 c in lane group l, out of range elsewhere
+  int c, g;
+};
+
+// An offset past every buffer of one wave (they hold at most 4 * kCPW bytes
+// of scores): the store is dropped by the range check, with no branch.
+constexpr uint32_t kDropOffset = 0x40000000u;
+
+// Offsets go in the per-lane voffset (the range check covers voffset).
+__device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
+  const uint32_t so = (uint32_t)tile * kTileBytes;
+  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so, 0, 0));
+  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so + 16, 0, 0));
+  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cx.rec, cx.lane_scale_off + so, 0, 0));
+}
+
+__device__ __forceinline__ void decode_tile(const RawTile& t, f16x8 (&kf)[4]) {
+  kf[0] = decode8(t.lo[0], t.lo[1]);
+  kf[1] = decode8(t.lo[2], t.lo[3]);
+  kf[2] = decode8(t.hi[0], t.hi[1]);
+  kf[3] = decode8(t.hi[2], t.hi[3]);
+}
+
+__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const f16x8 (&kf)[4],
+                                          f32x4 (&acc)[kLayers][4]) {
+#pragma unroll
+  for (int l = 0; l < kLayers; ++l)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][0], kf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int t = 1; t < 4; ++t)
+#pragma unroll
+    for (int l = 0; l < kLayers; ++l)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][t], kf[t], acc[l][mt], 0, 0, 0);
+}
+
+// Head reduction, sigmoid, ensemble and store of one tile.
+template <bool MEAN, bool PER_LAYER>
+__device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4],
+                                            const f32x4 (&wv)[kLayers][4], float s, int tile) {
+  // B = copysign(inf, s): med3(x, 0, B) is relu(x) for s >= 0 and min(x, 0) for s < 0.
+  const float bound = __uint_as_float((__float_as_uint(s) & 0x80000000u) | 0x7f800000u);
+  float t[kLayers];
+#pragma unroll
+  for (int l = 0; l < kLayers; ++l) {
+    float p = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p = fmaf(__builtin_amdgcn_fmed3f(acc[l][mt][r], 0.f, bound), wv[l][mt][r], p);
+    t[l] = s * sum4groups(p);  // the layer's logit
+  }
+  float e;
+  float sl[kLayers];
+  if (MEAN || PER_LAYER) {
+#pragma unroll
+    for (int l = 0; l < kLayers; ++l) sl[l] = sigmoid(t[l]);
+    e = MEAN ? (sl[0] + sl[1] + sl[2]) * (1.0f / 3.0f) : fmaxf(fmaxf(sl[0], sl[1]), sl[2]);
+  } else {
+    e = sigmoid(fmaxf(fmaxf(t[0], t[1]), t[2]));
+  }
+  const uint32_t to = (uint32_t)tile * (kTile * 4);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), cx.out, cx.lane_out_off + to, 0, 0);
+  if (PER_LAYER) {
+#pragma unroll
+    for (int l = 0; l < kLayers; ++l)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl[l]), cx.pl[l], cx.lane_pl_off[l] + to, 0, 0);
+  }
+}
+
+// Instruction order of one phase for the scheduler: every MFMA followed by
+// three vector-ALU instructions (a wave issues in order, so the vector work
+// of the reduction and decode must sit between the MFMAs to overlap them),
+// then the phase's requests (after the decode has consumed the ring slot
+// they refill) and its stores.
+__device__ __forceinline__ void interleave_phase() {
+#pragma unroll
+  for (int k = 0; k < kLayers * 4 * 4; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);    // VMEM read: codes, scale
+  __builtin_amdgcn_sched_group_barrier(0x040, 4, 0);    // VMEM write
+  // Nothing crosses a phase boundary: the scheduler would otherwise sink a
+  // request next to the decode that consumes it, phases later.
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// grid = (ceil(N / (4 * kCPW)), B), block = 256: wave w of block x scores
+// chunks [(4x + w) kCPW, +kCPW) of row blockIdx.y in tiles of 16.
+//
+// Software pipeline, one wave per SIMD: in the phase of tile i the wave
+// issues the 48 MFMAs of tile i while the vector unit reduces tile i-1 and
+// decodes tile i+1; the records of tile i+4 are requested in the same
+// phase (4 tiles in flight).  Tiles past the wave's valid chunks read as
+// zeros and their stores are dropped by the buffer range checks.
+template <bool MEAN, bool PER_LAYER>
+__global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
+                                                       const uint8_t* __restrict__ comp_k, int B, int64_t N,
+                                                       const int32_t* __restrict__ valid_n,
+                                                       float* __restrict__ scores, float* __restrict__ per_layer) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t start = ((int64_t)blockIdx.x * 4 + wave) * CPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps descriptors scalar
+  const int64_t start = ((int64_t)blockIdx.x * 4 + wave) * kCPW;
   if (start >= N) return;
-  const int64_t end = start + CPW < N ? start + CPW : N;
+  const int64_t end = start + kCPW < N ? start + kCPW : N;
   int64_t vn = N;
   if (valid_n) {
     const int64_t v = valid_n[b];
@@ -101,14 +220,34 @@ __global__ __launch_bounds__(256) void score_kernel(const f16x8* __restrict__ qp
     const float ninf = -__builtin_huge_valf();
     for (int64_t n = (start > vn ? start : vn) + lane; n < end; n += 64) {
       scores[(size_t)b * N + n] = ninf;
-      if (per_layer)
+      if (PER_LAYER)
         for (int l = 0; l < kLayers; ++l) per_layer[((size_t)l * B + b) * N + n] = ninf;
     }
   }
   if (start >= vend) return;
+  const int64_t count = vend - start;
 
-  const int c = lane & 15;
-  const int g = lane >> 4;
+  Ctx cx;
+  cx.c = lane & 15;
+  cx.g = lane >> 4;
+  cx.lane_rec_off = (uint32_t)(cx.c * kRecord + 32 * cx.g);
+  cx.lane_scale_off = (uint32_t)(cx.c * kRecord + kHeadDim);
+  cx.lane_out_off = cx.g == 0 ? (uint32_t)(cx.c * 4) : kDropOffset;
+  cx.rec = __builtin_amdgcn_make_buffer_rsrc((void*)(comp_k + ((size_t)b * N + start) * kRecord), 0,
+                                             (int)(count * kRecord), kBufferWord3);
+  cx.out = __builtin_amdgcn_make_buffer_rsrc((void*)(scores + (size_t)b * N + start), 0, (int)(count * 4),
+                                             kBufferWord3);
+#pragma unroll
+  for (int l = 0; l < kLayers; ++l) {
+    cx.lane_pl_off[l] = cx.g == l ? (uint32_t)(cx.c * 4) : kDropOffset;
+    cx.pl[l] = __builtin_amdgcn_make_buffer_rsrc(
+        PER_LAYER ? (void*)(per_layer + ((size_t)l * B + b) * N + start) : (void*)scores, 0,
+        PER_LAYER ? (int)(count * 4) : 0, kBufferWord3);
+  }
+
+  RawTile ring[kRing];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) load_tile(cx, k, ring[k]);
 
   f16x8 qf[kLayers][4][4];
   {
@@ -118,74 +257,67 @@ __global__ __launch_bounds__(256) void score_kernel(const f16x8* __restrict__ qp
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
+        for (int t = 0; t < 4; ++t) {
+          qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
+          // Keep the query fragments in accumulation registers: the MFMA reads
+          // its A operand from there, leaving the vector registers to the
+          // accumulators, decoded keys and records in flight.
+          asm volatile("" : "+a"(qf[l][mt][t]));
+        }
   }
   // w of the heads this lane's accumulators hold: 16 mt + 4 g + r.
   f32x4 wv[kLayers][4];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      wv[l][mt] = *(const f32x4*)(w + ((size_t)l * B + b) * kHeads + 16 * mt + 4 * g);
-
-  const uint8_t* row = comp_k + (size_t)b * N * kRecord;
-  for (int64_t n0 = start; n0 < vend; n0 += 16) {
-    const int64_t n = n0 + c;
-    const bool valid = n < vend;
-    u32x8 raw = {0, 0, 0, 0, 0, 0, 0, 0};
-    float s = 0.f;
-    if (valid) {
-      const uint8_t* rp = row + (size_t)n * kRecord;
-      const u32x4 r0 = *(const u32x4_a4*)(rp + 32 * g);
-      const u32x4 r1 = *(const u32x4_a4*)(rp + 32 * g + 16);
-      raw = u32x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-      s = *(const float*)(rp + kHeadDim);
-    }
-    f16x8 kf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) kf[t] = decode8(raw[2 * t], raw[2 * t + 1]);
-    // A negative scale: relu(s x) = |s| relu(-x); flip the operand's signs.
-    if (__builtin_amdgcn_read_exec() & __ballot(s < 0.f)) {
-      if (s < 0.f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) kf[t] = -kf[t];
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      wv[l][mt] = *(const f32x4*)(w + ((size_t)l * B + b) * kHeads + 16 * mt + 4 * cx.g);
+      // Consume the loaded value here, so its wait is paid once, before the
+      // loop; a wait inside the loop would also drain the records in flight.
+      asm volatile("" : "+v"(wv[l][mt]));
     }
 
-    f32x4 acc[kLayers][4];
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[l][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int l = 0; l < kLayers; ++l)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][t], kf[t], acc[l][mt], 0, 0, 0);
+  const int tiles = (int)((count + kTile - 1) / kTile);
 
-    const float as = fabsf(s);
-    float S[kLayers];
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l) {
-      float p = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p = fmaf(fmaxf(acc[l][mt][r], 0.f), wv[l][mt][r], p);
-      p = sum4groups(p);
-      S[l] = sigmoidf_(as * p);
-    }
-    const float E = mode == FM_ENSEMBLE_MAX ? fmaxf(fmaxf(S[0], S[1]), S[2]) : (S[0] + S[1] + S[2]) / 3.0f;
-    if (valid) {
-      if (g == 0) scores[(size_t)b * N + n] = E;
-      if (per_layer && g < kLayers) {
-        const float v = g == 0 ? S[0] : (g == 1 ? S[1] : S[2]);
-        per_layer[((size_t)g * B + b) * N + n] = v;
-      }
-    }
+  f16x8 kf[2][4];
+  f32x4 acc[2][kLayers][4];
+
+  // Phase of tile i, P = i mod 8 (compile-time, so every register index is
+  // static): MFMAs of tile i; finish tile i-1 (its scale still in its ring
+  // slot); decode tile i+1 (requested five phases ago); request tile i+6
+  // into the slot of tile i-2, finished in the previous phase.
+#define FM_PHASE(P, I)                                                                                \
+  {                                                                                                   \
+    mfma_tile(qf, kf[(P) & 1], acc[(P) & 1]);                                                         \
+    finish_tile<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], wv, ring[((P) + 7) & 7].s, (I) - 1);         \
+    decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
+    load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
+    interleave_phase();                                                                               \
   }
+
+  // Tile 0 (nothing to finish yet).
+  decode_tile(ring[0], kf[0]);
+  mfma_tile(qf, kf[0], acc[0]);
+  decode_tile(ring[1], kf[1]);
+  load_tile(cx, kAhead, ring[kAhead]);
+
+  // Tiles 1 .. 8 m, eight per iteration, branch-free.  Tiles past the last
+  // valid one read zeros and their stores are dropped, so the count can be
+  // rounded up; a full wave has 8 m + 1 tiles and wastes none.
+  int i = 1;
+  do {
+    FM_PHASE(1, i)
+    FM_PHASE(2, i + 1)
+    FM_PHASE(3, i + 2)
+    FM_PHASE(4, i + 3)
+    FM_PHASE(5, i + 4)
+    FM_PHASE(6, i + 5)
+    FM_PHASE(7, i + 6)
+    FM_PHASE(0, i + 7)
+    i += 8;
+  } while (i < tiles);
+  finish_tile<MEAN, PER_LAYER>(cx, acc[0], wv, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
+#undef FM_PHASE
 }
 
 }  // namespace
@@ -197,11 +329,13 @@ hipError_t launch_score(const Workspace& ws, const float* q, const float* w, con
     const int total = B * kQFrags * 64;
     hipLaunchKernelGGL(pack_q_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, q, B, qpack);
   }
-  constexpr int kCPW = 1024;
   const int64_t per_block = 4 * (int64_t)kCPW;
   dim3 grid((unsigned)((N + per_block - 1) / per_block), (unsigned)B);
-  hipLaunchKernelGGL((score_kernel<kCPW>), grid, dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n,
-                     mode, scores, per_layer);
+  const bool mean = mode == FM_ENSEMBLE_MEAN;
+  auto kern = mean ? (per_layer ? score_kernel<true, true> : score_kernel<true, false>)
+                   : (per_layer ? score_kernel<false, true> : score_kernel<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n, scores,
+                     per_layer);
   return hipGetLastError();
 }
 
