@@ -1,6 +1,7 @@
 // C ABI of libfm (include/fm.h): argument checks, the context and its
 // workspace, and dispatch to the kernel launchers.  Every check runs before
 // anything is enqueued, so a failing call leaves the stream untouched.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -131,22 +132,31 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
 
-  // One allocation, each buffer 256-byte aligned.
+  // One allocation, each buffer 256-byte aligned.  The split-K partial
+  // buffers hold splits(B) * B rows, largest at B = max_batch or at the
+  // largest B of the most-split row-group count.
   const size_t mb = (size_t)max_batch;
+  size_t p1_rows = 0, p2_rows = 0;
+  for (int g = 1; g <= proj_row_groups(max_batch); ++g) {
+    const int b = g * kProjRowsPerWave < max_batch ? g * kProjRowsPerWave : max_batch;
+    p1_rows = std::max(p1_rows, (size_t)proj1_splits(b) * b);
+    p2_rows = std::max(p2_rows, (size_t)proj2_splits(b) * b);
+  }
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
-  size_t sizes[8] = {
-      sizeof(float) * kSplitK1 * kLayers * mb * kProj1Out,  // proj1_part
-      sizeof(float) * kLayers * mb * kQLora,                // a_hat
-      sizeof(float) * kLayers * mb * kHeads * kHeadDim,     // q_lin
-      sizeof(double) * (kRopeDim / 2),                      // rope_freq
-      (size_t)16 * kQFrags * 64 * mb,                       // qpack (f16x8 per lane)
-      sizeof(uint32_t) * mb * kSelBins,                     // sel_hist
-      sizeof(uint32_t) * mb * 4,                            // sel_state
-      sizeof(uint32_t) * mb * sel_blocks,                   // sel_eq
-  };
-  size_t offs[8];
+  enum { kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kSelState, kSelCand, kSelCount, kNumBuffers };
+  size_t sizes[kNumBuffers];
+  sizes[kPart1] = sizeof(float) * kLayers * p1_rows * kProj1Out;
+  sizes[kAHat] = sizeof(float) * kLayers * mb * kQLora;
+  sizes[kQLin] = sizeof(float) * kLayers * p2_rows * kHeads * kHeadDim;
+  sizes[kFreq] = sizeof(double) * (kRopeDim / 2);
+  sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
+  sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
+  sizes[kSelState] = sizeof(uint32_t) * mb * 4;
+  sizes[kSelCand] = 2 * sizeof(uint32_t) * mb * (size_t)max_n;  // (key, index) pairs
+  sizes[kSelCount] = sizeof(uint32_t) * mb * sel_blocks;
+  size_t offs[kNumBuffers];
   size_t total = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kNumBuffers; ++i) {
     offs[i] = total;
     total += (sizes[i] + 255) & ~(size_t)255;
   }
@@ -163,22 +173,24 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws_base = base;
   ctx->ws_bytes = total;
   char* p = (char*)base;
-  ctx->ws.proj1_part = (float*)(p + offs[0]);
-  ctx->ws.a_hat = (float*)(p + offs[1]);
-  ctx->ws.q_lin = (float*)(p + offs[2]);
-  ctx->ws.rope_freq = (double*)(p + offs[3]);
-  ctx->ws.qpack = (void*)(p + offs[4]);
-  ctx->ws.sel_hist = (uint32_t*)(p + offs[5]);
-  ctx->ws.sel_state = (uint32_t*)(p + offs[6]);
-  ctx->ws.sel_eq = (uint32_t*)(p + offs[7]);
+  ctx->ws.proj1_part = (float*)(p + offs[kPart1]);
+  ctx->ws.a_hat = (float*)(p + offs[kAHat]);
+  ctx->ws.q_lin = (float*)(p + offs[kQLin]);
+  ctx->ws.rope_freq = (double*)(p + offs[kFreq]);
+  ctx->ws.rope_cs = (float*)(p + offs[kCosSin]);
+  ctx->ws.qpack = (void*)(p + offs[kQPack]);
+  ctx->ws.sel_state = (uint32_t*)(p + offs[kSelState]);
+  ctx->ws.sel_cand = (void*)(p + offs[kSelCand]);
+  ctx->ws.sel_count = (uint32_t*)(p + offs[kSelCount]);
 
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
   e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(base);
     delete ctx;
-    return hip_fail(e, "upload of RoPE frequencies");
+    return hip_fail(e, "context initialisation");
   }
   *out = ctx;
   return FM_OK;

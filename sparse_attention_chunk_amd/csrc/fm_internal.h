@@ -22,10 +22,21 @@ constexpr int kRopeDim = 64;
 constexpr int kRecord = kHeadDim + 4;
 
 // First projection: wq_a rows [0, 1024) and weights_proj rows [1024, 1088)
-// share one pass over `hidden`, split over K in kSplitK1 slices whose
-// partial sums the RMSNorm kernel adds in a fixed order.
+// share one pass over `hidden`.  Both projections split K so that a launch
+// has a few thousand waves (the weights stream from HBM once, the partial
+// sums are added in slice order by the next kernel).  A wave covers up to
+// 32 batch rows; more rows go to further wave groups.
 constexpr int kProj1Out = kQLora + kHeads;
-constexpr int kSplitK1 = 4;
+constexpr int kProjRowsPerWave = 32;
+
+inline int proj_row_groups(int B) { return (B + kProjRowsPerWave - 1) / kProjRowsPerWave; }
+// K slices of the first projection (K = 4096): 16 for one row group, fewer for more.
+inline int proj1_splits(int B) {
+  const int g = proj_row_groups(B);
+  return g <= 1 ? 16 : (g <= 2 ? 8 : (g <= 4 ? 4 : (g <= 8 ? 2 : 1)));
+}
+// K slices of wq_b (K = 1024).
+inline int proj2_splits(int B) { return proj_row_groups(B) <= 1 ? 2 : 1; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves.
@@ -38,14 +49,15 @@ constexpr int kSelSlice = kSelThreads * kSelItems;
 constexpr int kSelBins = 2048;
 
 struct Workspace {
-  float* proj1_part = nullptr;   // [kSplitK1][3][max_batch][kProj1Out]
+  float* proj1_part = nullptr;   // [proj1_splits(B)][3][B][kProj1Out]
   float* a_hat = nullptr;        // [3][max_batch][kQLora]
-  float* q_lin = nullptr;        // [3][max_batch][kHeads * kHeadDim]
+  float* q_lin = nullptr;        // [proj2_splits(B)][3][B][kHeads * kHeadDim]
   double* rope_freq = nullptr;   // [kRopeDim / 2]
+  float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16
-  uint32_t* sel_hist = nullptr;  // [max_batch][kSelBins]
   uint32_t* sel_state = nullptr; // [max_batch][4]
-  uint32_t* sel_eq = nullptr;    // [max_batch][ceil(max_n / kSelSlice)]
+  void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
+  uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
 };
 
 // Launchers.  Shapes are validated by the caller; each returns the launch

@@ -18,7 +18,6 @@ namespace fm {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 struct ProjArgs {
   const float* w0[kLayers];  // rows [0, rows0) of the stacked weight, per layer
@@ -29,76 +28,87 @@ struct ProjArgs {
   int rows0, rows1, K, k_split, B;
 };
 
-// C[b][o] = sum_k x[b][k] W[o][k] on 16x16x4 fp32 MFMA tiles.  A wave owns
-// OT column tiles (16 outputs each) x BT row tiles (16 batch rows each) over
-// one K slice; a 256-thread block holds 4 waves on consecutive column groups.
+// C[b][o] = sum_k x[b][k] W[o][k] on 16x16x4 fp32 MFMA tiles.  A block of
+// 4 waves owns 4 consecutive column tiles (64 outputs) x 32 batch rows over
+// one K slice; the 32 activation rows of each kKChunk-wide piece of the
+// slice are staged in LDS once and shared by the 4 waves, while each wave
+// streams its own 16 weight rows from HBM.
 //
 // MFMA operand layout (16x16x4 f32): lane l supplies A[l%16][l/16] and
 // B[l/16][l%16] and receives C[4(l/16)+r][l%16], r = 0..3.  Each lane loads
 // 4 consecutive k of one row (a float4); MFMA e of a 16-k step takes element
 // e, so the four MFMAs of a step cover the 16 k exactly once.
-template <int OT, int BT>
+constexpr int kKChunk = 256;
+constexpr int kXStride = kKChunk + 4;  // padded LDS row (floats): rows start in different banks
+
 __global__ __launch_bounds__(256) void proj_kernel(ProjArgs p) {
+  constexpr int BT = kProjRowsPerWave / 16;
+  __shared__ f32x4 xs4[kProjRowsPerWave * kXStride / 4];
+  float* xs = (float*)xs4;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = p.rows0 + p.rows1;
-  const int o_base = (blockIdx.x * 4 + wave) * 16 * OT;
-  if (o_base >= rows) return;
+  const int o_base = (blockIdx.x * 4 + wave) * 16;
+  const bool active = o_base < rows;  // every wave still helps stage the activations
   const int layer = blockIdx.y / p.k_split;
   const int split = blockIdx.y % p.k_split;
   const int k_len = p.K / p.k_split;
   const int k_begin = split * k_len;
-  const int b_base = blockIdx.z * 16 * BT;
+  const int b_base = blockIdx.z * kProjRowsPerWave;
   const int i = lane & 15;
   const int g = lane >> 4;
 
-  const float* wrow[OT];
-#pragma unroll
-  for (int ot = 0; ot < OT; ++ot) {
-    const int o = o_base + 16 * ot + i;
-    wrow[ot] = o < p.rows0 ? p.w0[layer] + (size_t)o * p.K
-                           : (o < rows ? p.w1[layer] + (size_t)(o - p.rows0) * p.K : nullptr);
-  }
-  const float* xrow[BT];
-#pragma unroll
-  for (int bt = 0; bt < BT; ++bt) {
-    const int b = b_base + 16 * bt + i;
-    xrow[bt] = b < p.B ? p.x + layer * p.x_layer_stride + (size_t)b * p.K : nullptr;
-  }
+  const int o = o_base + i;
+  const float* wrow = o < p.rows0 ? p.w0[layer] + (size_t)o * p.K
+                                  : (o < rows ? p.w1[layer] + (size_t)(o - p.rows0) * p.K : nullptr);
+  const float* xlayer = p.x + layer * p.x_layer_stride;
 
-  f32x4 acc[OT][BT];
+  f32x4 acc[BT];
 #pragma unroll
-  for (int ot = 0; ot < OT; ++ot)
-#pragma unroll
-    for (int bt = 0; bt < BT; ++bt) acc[ot][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int k = k_begin + 4 * g; k < k_begin + k_len; k += 16) {
-    f32x4 wv[OT], xv[BT];
+
+  for (int kc = k_begin; kc < k_begin + k_len; kc += kKChunk) {
+    // This wave's weights for the whole chunk are requested first, so their
+    // HBM latency overlaps the staging of the activations.
+    constexpr int kSteps = kKChunk / 16;
+    f32x4 wv[kSteps];
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot) wv[ot] = wrow[ot] ? *(const f32x4*)(wrow[ot] + k) : zero;
+    for (int u = 0; u < kSteps; ++u)
+      wv[u] = (active && wrow) ? __builtin_nontemporal_load((const f32x4*)(wrow + kc + 4 * g + 16 * u)) : zero;
+    // Stage x[b_base .. b_base + 32)[kc .. kc + kKChunk) (rows past B are zero).
+    for (int idx = threadIdx.x; idx < kProjRowsPerWave * kKChunk / 4; idx += 256) {
+      const int r = idx / (kKChunk / 4);
+      const int c4 = idx % (kKChunk / 4);
+      const int b = b_base + r;
+      const f32x4 v = b < p.B ? *(const f32x4*)(xlayer + (size_t)b * p.K + kc + 4 * c4) : zero;
+      *(f32x4*)(xs + r * kXStride + 4 * c4) = v;
+    }
+    __syncthreads();
+    if (active) {
 #pragma unroll
-    for (int bt = 0; bt < BT; ++bt) xv[bt] = xrow[bt] ? *(const f32x4*)(xrow[bt] + k) : zero;
+      for (int u = 0; u < kSteps; ++u) {
+        f32x4 xv[BT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int bt = 0; bt < BT; ++bt) xv[bt] = *(const f32x4*)(xs + (16 * bt + i) * kXStride + 4 * g + 16 * u);
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int bt = 0; bt < BT; ++bt)
-          acc[ot][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[bt][e], wv[ot][e], acc[ot][bt], 0, 0, 0);
+          for (int bt = 0; bt < BT; ++bt)
+            acc[bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[bt][e], wv[u][e], acc[bt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
   }
 
   // C rows are batch rows, C columns outputs: lane l holds b = 4(l/16)+r, o = l%16.
-#pragma unroll
-  for (int ot = 0; ot < OT; ++ot) {
-    const int o = o_base + 16 * ot + i;
-    if (o >= rows) continue;
+  if (active && o < rows) {
 #pragma unroll
     for (int bt = 0; bt < BT; ++bt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int b = b_base + 16 * bt + 4 * g + r;
-        if (b < p.B) p.out[(((size_t)split * kLayers + layer) * p.B + b) * rows + o] = acc[ot][bt][r];
+        if (b < p.B) p.out[(((size_t)split * kLayers + layer) * p.B + b) * rows + o] = acc[bt][r];
       }
   }
 }
@@ -109,92 +119,123 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// One wave per (layer, row): adds the K-slice partials in slice order, then
-// RMSNorm (a / sqrt(mean(a^2) + eps) * gain) of the Q_LORA_RANK vector, and
-// finishes the weight branch (weights_proj rows times weight_scale).
 struct GainPtrs {
   const float* g[kLayers];
 };
 
-__global__ __launch_bounds__(64) void rmsnorm_kernel(const float* part, GainPtrs gains, int B, float eps,
-                                                     float w_scale, float* a_hat, float* w_out) {
+// cos and sin of phi = pos * freq.  phi reaches about 1e6 rad (positions up
+// to 2^20, first frequency 1 rad/token), so it is formed and reduced to
+// |r| <= pi in double precision: n = rint(phi / 2 pi), r = phi - n 2 pi with
+// 2 pi split into a double (2PI_HI) and its remainder (2PI_LO), each product
+// subtracted by one fused multiply-add (two-constant Cody-Waite reduction;
+// n stays below 2^20, far inside the exact range).  The cosine and sine of
+// the small r are then taken in single precision.
+__device__ inline void rope_cos_sin(int64_t pos, double freq, float* out2) {
+  const double two_pi_hi = 6.283185307179586;       // 2 pi rounded to double
+  const double two_pi_lo = 2.4492935982947064e-16;  // 2 pi - two_pi_hi
+  const double phi = (double)pos * freq;
+  const double n = rint(phi * 0.15915494309189535);  // 1 / (2 pi)
+  double r = fma(-n, two_pi_hi, phi);
+  r = fma(-n, two_pi_lo, r);
+  const float rf = (float)r;
+  out2[0] = cosf(rf);
+  out2[1] = sinf(rf);
+}
+
+// One 256-thread block per (layer, row): adds the K-slice partials in slice
+// order, then RMSNorm (a / sqrt(mean(a^2) + eps) * gain) of the
+// Q_LORA_RANK vector, and finishes the weight branch (weights_proj rows
+// times weight_scale).  The layer-0 block of a row also stores the cosine
+// and sine of the row's RoPE angles.
+template <int S>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* part, GainPtrs gains, int B, float eps,
+                                                      float w_scale, const int64_t* positions, const double* freq,
+                                                      float* rope_cs, float* a_hat, float* w_out) {
   const int layer = blockIdx.x / B;
   const int b = blockIdx.x % B;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
   const size_t split_stride = (size_t)kLayers * B * kProj1Out;
   const float* src = part + ((size_t)layer * B + b) * kProj1Out;
-  float a[kQLora / 64];
+  constexpr int kPer = kQLora / 256;
+  float a[kPer];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kQLora / 64; ++i) {
-    const int o = lane + 64 * i;
+  for (int i = 0; i < kPer; ++i) {
+    const int o = t + 256 * i;
     float v = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSplitK1; ++s) v += src[s * split_stride + o];
+    for (int s = 0; s < S; ++s) v += src[s * split_stride + o];
     a[i] = v;
     ss = fmaf(v, v, ss);
   }
   ss = wave_sum(ss);
+  __shared__ float red[4];
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
   const float rs = 1.0f / sqrtf(ss * (1.0f / kQLora) + eps);
   const float* gain = gains.g[layer];
   float* dst = a_hat + ((size_t)layer * B + b) * kQLora;
 #pragma unroll
-  for (int i = 0; i < kQLora / 64; ++i) {
-    const int o = lane + 64 * i;
+  for (int i = 0; i < kPer; ++i) {
+    const int o = t + 256 * i;
     dst[o] = a[i] * rs * gain[o];
   }
-  float wv = 0.f;
+  if (t < kHeads) {
+    float wv = 0.f;
 #pragma unroll
-  for (int s = 0; s < kSplitK1; ++s) wv += src[s * split_stride + kQLora + lane];
-  w_out[((size_t)layer * B + b) * kHeads + lane] = wv * w_scale;
+    for (int s = 0; s < S; ++s) wv += src[s * split_stride + kQLora + t];
+    w_out[((size_t)layer * B + b) * kHeads + t] = wv * w_scale;
+  } else if (layer == 0 && t >= 64 && t < 64 + kRopeDim / 2) {
+    const int j = t - 64;
+    rope_cos_sin(positions[b], freq[j], rope_cs + ((size_t)b * (kRopeDim / 2) + j) * 2);
+  }
 }
 
-// One block per (layer, row), 4 waves of 16 heads.  Lane l holds dims 2l and
-// 2l+1 of a head.  RoPE: lanes 32..63 hold the rotated dims 64..127, pair
-// j = l - 32 is turned counter-clockwise by pos * freq[j]; the angle and its
-// cosine/sine are formed in double precision (positions reach 2^20 and the
-// first frequency is 1 rad/token), the rotation itself in fp32.  Then the
-// 128-point Walsh-Hadamard butterfly in Sylvester order, scaled by 128^-0.5.
-__global__ __launch_bounds__(256) void rope_hadamard_kernel(const float* q_lin, const int64_t* positions,
-                                                            const double* freq, int B, float* q_out) {
-  const int layer = blockIdx.x / B;
-  const int b = blockIdx.x % B;
+// One wave per (layer, row, head), 4 heads per block.  Lane l holds dims 2l
+// and 2l+1 of the head (the wq_b K-slice partials added in slice order).
+// RoPE: lanes 32..63 hold the rotated dims 64..127; pair j = l - 32 is
+// turned counter-clockwise by pos * freq[j] (cosine and sine from the
+// RMSNorm kernel), the rotation in fp32.  Then the 128-point Walsh-Hadamard
+// butterfly in Sylvester order, scaled by 128^-0.5.
+__global__ __launch_bounds__(256) void rope_hadamard_kernel(const float* q_lin, int splits, const float* rope_cs, int B,
+                                                            float* q_out) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  float cs = 1.f, sn = 0.f;
+  const int gh = blockIdx.x * 4 + (threadIdx.x >> 6);  // (layer * B + b) * 64 + h
+  const int h = gh % kHeads;
+  const int lb = gh / kHeads;
+  const int b = lb % B;
+  const size_t off = (size_t)lb * kHeads * kHeadDim + (size_t)h * kHeadDim + 2 * lane;
+  const size_t split_stride = (size_t)kLayers * B * kHeads * kHeadDim;
+  float x = 0.f, y = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float2 v = *(const float2*)(q_lin + s * split_stride + off);
+    x += v.x;
+    y += v.y;
+  }
   if (lane >= 32) {
-    const double phi = (double)positions[b] * freq[lane - 32];
-    cs = (float)cos(phi);
-    sn = (float)sin(phi);
+    const float2 c = *(const float2*)(rope_cs + ((size_t)b * (kRopeDim / 2) + (lane - 32)) * 2);
+    const float rx = x * c.x - y * c.y;
+    const float ry = x * c.y + y * c.x;
+    x = rx;
+    y = ry;
+  }
+  float a0 = x + y;
+  float a1 = x - y;
+#pragma unroll
+  for (int m = 1; m <= 32; m <<= 1) {
+    const float p0 = __shfl_xor(a0, m, 64);
+    const float p1 = __shfl_xor(a1, m, 64);
+    if (lane & m) {
+      a0 = p0 - a0;
+      a1 = p1 - a1;
+    } else {
+      a0 = a0 + p0;
+      a1 = a1 + p1;
+    }
   }
   const float inv_sqrt = 0.08838834764831845f;  // 128^-0.5
-  const size_t base = ((size_t)layer * B + b) * kHeads * kHeadDim;
-  for (int hh = 0; hh < 16; ++hh) {
-    const int h = wave * 16 + hh;
-    const float2 v = *(const float2*)(q_lin + base + (size_t)h * kHeadDim + 2 * lane);
-    float x = v.x, y = v.y;
-    if (lane >= 32) {
-      const float rx = x * cs - y * sn;
-      const float ry = x * sn + y * cs;
-      x = rx;
-      y = ry;
-    }
-    float a0 = x + y;
-    float a1 = x - y;
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) {
-      const float p0 = __shfl_xor(a0, m, 64);
-      const float p1 = __shfl_xor(a1, m, 64);
-      if (lane & m) {
-        a0 = p0 - a0;
-        a1 = p1 - a1;
-      } else {
-        a0 = a0 + p0;
-        a1 = a1 + p1;
-      }
-    }
-    *(float2*)(q_out + base + (size_t)h * kHeadDim + 2 * lane) = make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
-  }
+  *(float2*)(q_out + off) = make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
 }
 
 }  // namespace
@@ -203,8 +244,9 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
                                 const float* hidden, const int64_t* positions, int B, float* q_out, float* w_out,
                                 hipStream_t stream) {
   (void)max_batch;
-  constexpr int kBT = 2;  // 32 batch rows per wave; more rows go to grid.z
-  const int b_groups = (B + 16 * kBT - 1) / (16 * kBT);
+  const int row_groups = proj_row_groups(B);
+  const int s1 = proj1_splits(B);
+  const int s2 = proj2_splits(B);
 
   // wq_a | weights_proj, split over K.
   {
@@ -219,22 +261,24 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     p.rows0 = kQLora;
     p.rows1 = kHeads;
     p.K = kHidden;
-    p.k_split = kSplitK1;
+    p.k_split = s1;
     p.B = B;
-    constexpr int kOT = 1;
-    const int col_groups = (kProj1Out + 16 * kOT - 1) / (16 * kOT);
-    dim3 grid((col_groups + 3) / 4, kLayers * kSplitK1, b_groups);
-    hipLaunchKernelGGL((proj_kernel<kOT, kBT>), grid, dim3(256), 0, stream, p);
+    const int col_tiles = (kProj1Out + 15) / 16;
+    dim3 grid((col_tiles + 3) / 4, kLayers * s1, row_groups);
+    hipLaunchKernelGGL(proj_kernel, grid, dim3(256), 0, stream, p);
   }
-  // RMSNorm + weight-branch finish.
+  // RMSNorm + weight-branch finish + RoPE angles.
   {
     GainPtrs gp{};
     for (int l = 0; l < kLayers; ++l) gp.g[l] = wts.q_norm[l];
     const float w_scale = (float)(1.0 / std::sqrt((double)cfg.head_dim * (double)cfg.n_heads));
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(kLayers * B), dim3(64), 0, stream, ws.proj1_part, gp, B, cfg.rms_eps,
-                       w_scale, ws.a_hat, w_out);
+    auto kern = s1 == 16 ? rmsnorm_kernel<16>
+                         : (s1 == 8 ? rmsnorm_kernel<8>
+                                    : (s1 == 4 ? rmsnorm_kernel<4> : (s1 == 2 ? rmsnorm_kernel<2> : rmsnorm_kernel<1>)));
+    hipLaunchKernelGGL(kern, dim3(kLayers * B), dim3(256), 0, stream, ws.proj1_part, gp, B, cfg.rms_eps, w_scale,
+                       positions, ws.rope_freq, ws.rope_cs, ws.a_hat, w_out);
   }
-  // wq_b.
+  // wq_b, split over K.
   {
     ProjArgs p{};
     for (int l = 0; l < kLayers; ++l) {
@@ -247,16 +291,15 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     p.rows0 = kHeads * kHeadDim;
     p.rows1 = 0;
     p.K = kQLora;
-    p.k_split = 1;
+    p.k_split = s2;
     p.B = B;
-    constexpr int kOT = 2;
-    const int col_groups = (kHeads * kHeadDim + 16 * kOT - 1) / (16 * kOT);
-    dim3 grid((col_groups + 3) / 4, kLayers, b_groups);
-    hipLaunchKernelGGL((proj_kernel<kOT, kBT>), grid, dim3(256), 0, stream, p);
+    const int col_tiles = kHeads * kHeadDim / 16;
+    dim3 grid((col_tiles + 3) / 4, kLayers * s2, row_groups);
+    hipLaunchKernelGGL(proj_kernel, grid, dim3(256), 0, stream, p);
   }
-  // RoPE (YaRN) + normalized Hadamard.
-  hipLaunchKernelGGL(rope_hadamard_kernel, dim3(kLayers * B), dim3(256), 0, stream, ws.q_lin, positions,
-                     ws.rope_freq, B, q_out);
+  // Split-K sum, RoPE (YaRN) + normalized Hadamard.
+  hipLaunchKernelGGL(rope_hadamard_kernel, dim3(kLayers * B * kHeads / 4), dim3(256), 0, stream, ws.q_lin, s2,
+                     ws.rope_cs, B, q_out);
   return hipGetLastError();
 }
 

@@ -187,3 +187,35 @@ def test_threshold_strict_exact(retr, tau):
     m = host(retr.keep_threshold(dev(s), tau, dev(vn)))
     for b in range(4):
         assert np.array_equal(m[b].astype(np.uint8), oracle.select_threshold(s[b].astype(np.float64), int(vn[b]), tau))
+
+
+def test_topk_sample_miss_falls_back_to_whole_row(retr):
+    """The top-K cut-off comes from 64 sampled runs of 128 chunks; here the
+    sampled chunks hold the largest scores and the rest are low, so fewer than
+    K chunks reach the cut-off and the selection must fall back to the whole
+    row.  The result is still the exact top-K."""
+    n, k = 65536, 512
+    s = np.full((2, n), 0.1, np.float32)
+    rng = np.random.default_rng(21)
+    s[:, :] = rng.uniform(0.05, 0.2, (2, n)).astype(np.float32)
+    starts = [r * (n - 128) // 63 for r in range(64)]
+    vals = np.linspace(0.9, 0.99, 64 * 128).astype(np.float32)
+    i = 0
+    for st in starts:
+        s[0, st:st + 128] = vals[i:i + 128]
+        i += 128
+    s[1] = s[0][::-1]                       # second row: a different layout, same values
+    m = host(retr.keep_topk(dev(s), k))
+    for b in range(2):
+        assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), n, k)), b
+
+
+def test_topk_large_candidate_lists(retr):
+    """All-equal rows longer than the LDS staging: every chunk is a candidate."""
+    n = 100000
+    s = np.full((2, n), 0.5, np.float32)
+    s[1, ::3] = 0.25
+    for k in (5000, 30000):
+        m = host(retr.keep_topk(dev(s), k))
+        for b in range(2):
+            assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), n, k)), (b, k)
