@@ -131,6 +131,10 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  if (cus < 1 || cus > kMaxScoreBlocks) return fail(FM_EUNSUPPORTED, "device reports %d compute units", cus);
 
   // One allocation, each buffer 256-byte aligned.  The split-K partial
   // buffers hold splits(B) * B rows, largest at B = max_batch or at the
@@ -143,7 +147,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
     p2_rows = std::max(p2_rows, (size_t)proj2_splits(b) * b);
   }
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
-  enum { kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kSelState, kSelCand, kSelCount, kNumBuffers };
+  enum {
+    kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kRowTiles, kWaveRow, kSelState, kSelCand, kSelCount, kNumBuffers
+  };
   size_t sizes[kNumBuffers];
   sizes[kPart1] = sizeof(float) * kLayers * p1_rows * kProj1Out;
   sizes[kAHat] = sizeof(float) * kLayers * mb * kQLora;
@@ -151,6 +157,8 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kFreq] = sizeof(double) * (kRopeDim / 2);
   sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
   sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
+  sizes[kRowTiles] = sizeof(int64_t) * (mb + 1);
+  sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
   sizes[kSelState] = sizeof(uint32_t) * mb * 4;
   sizes[kSelCand] = 2 * sizeof(uint32_t) * mb * (size_t)max_n;  // (key, index) pairs
   sizes[kSelCount] = sizeof(uint32_t) * mb * sel_blocks;
@@ -179,6 +187,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.rope_freq = (double*)(p + offs[kFreq]);
   ctx->ws.rope_cs = (float*)(p + offs[kCosSin]);
   ctx->ws.qpack = (void*)(p + offs[kQPack]);
+  ctx->ws.row_tiles = (int64_t*)(p + offs[kRowTiles]);
+  ctx->ws.wave_row = (int32_t*)(p + offs[kWaveRow]);
+  ctx->ws.score_blocks = cus;
   ctx->ws.sel_state = (uint32_t*)(p + offs[kSelState]);
   ctx->ws.sel_cand = (void*)(p + offs[kSelCand]);
   ctx->ws.sel_count = (uint32_t*)(p + offs[kSelCount]);

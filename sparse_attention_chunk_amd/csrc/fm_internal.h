@@ -39,8 +39,13 @@ inline int proj1_splits(int B) {
 inline int proj2_splits(int B) { return proj_row_groups(B) <= 1 ? 2 : 1; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
-// fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves.
-constexpr int kQFrags = kLayers * 4 * 4;
+// fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,
+// then 4 fragments (one per k-step) of the per-layer weighted query sums.
+constexpr int kQHeadFrags = kLayers * 4 * 4;
+constexpr int kQFrags = kQHeadFrags + 4;
+// The score kernel runs one block of 4 waves per compute unit; each wave
+// takes an equal share of the row-major list of 16-chunk tiles.
+constexpr int kMaxScoreBlocks = 1024;
 
 // Top-K selection: a block covers kSelSlice consecutive chunks of one row.
 constexpr int kSelThreads = 256;
@@ -55,6 +60,9 @@ struct Workspace {
   double* rope_freq = nullptr;   // [kRopeDim / 2]
   float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16
+  int64_t* row_tiles = nullptr;  // [max_batch + 1]: first tile of each row in the list of valid tiles
+  int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
+  int score_blocks = 0;          // compute units of the device
   uint32_t* sel_state = nullptr; // [max_batch][4]
   void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
   uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice

@@ -6,17 +6,25 @@
 //   E       = max_l S_l  or  mean_l S_l
 //
 // Per request row this is a [N x 128] x [128 x 192] contraction (3 layers x
-// 64 heads), 49152 flop per 132-byte chunk, on the 16x16x32 f16 MFMA.
+// 64 heads), 49152 flop per 132-byte chunk, on the 16x16x32 f16 MFMA
+// (plus 4096 flop per chunk for the linear term below).
 //
 // Exact-algebra choices that keep it within the fp64 result:
 //   - the e4m3 codes are converted exactly to f16 (every finite e4m3 value
-//     is an f16 value) and the fp32 scale s multiplies the fp32 head sum
-//     instead of the operand.  With x_h = code . q_h:
-//       sum_h w_h relu(s x_h) = s * sum_h w_h med3(x_h, 0, B),
-//     B = +inf for s >= 0 (relu) and -inf for s < 0 (min(x, 0)), so a scale
-//     of either sign costs nothing extra;
+//     is an f16 value) and the fp32 scale s multiplies fp32 head sums
+//     instead of the operand;
 //   - q is rounded once to f16 (11-bit significand);
+//   - relu(y) = (y + |y|) / 2.  With x_h = code . q_h (q_h in f16) and
+//     y_h = s x_h:
+//       sum_h w_h relu(y_h) = s/2 * sum_h w_h x_h + |s|/2 * sum_h w_h |x_h|.
+//     The first sum is linear in the codes: it is (sum_h w_h q_h) . code,
+//     four more MFMAs per tile on spare A rows holding the weighted query
+//     sum of each layer split into two f16 parts (hi + lo, about 22
+//     significant bits).  The second is one fused multiply-add per head with
+//     an absolute-value operand, and a scale of either sign costs nothing;
 //   - max ensemble: max_l sigmoid(t_l) = sigmoid(max_l t_l), one sigmoid.
+#include <algorithm>
+
 #include "fm_internal.h"
 
 namespace fm {
@@ -30,8 +38,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kTile = 16;                        // chunks per MFMA column tile
 constexpr int kTileBytes = kTile * kRecord;      // 2112
-constexpr int kTilesPerWave = 65;                // 8 m + 1: the pipeline below runs in groups of 8
-constexpr int kCPW = kTilesPerWave * kTile;      // 1040 chunks per wave
+constexpr int64_t kMaxSegTiles = 1 << 16;        // tiles per pipeline run: buffer offsets stay below 2^31
 constexpr int kRing = 8;                         // register ring of record tiles
 constexpr int kAhead = 6;                        // tile i + 6 is requested in the phase of tile i
 
@@ -40,24 +47,54 @@ constexpr int kAhead = 6;                        // tile i + 6 is requested in t
 // A = queries (rows = 16 heads of a head tile), B = keys (columns = 16
 // chunks).  For k-step t (t = 0..3) lane l's eight k slots are the dims
 // 32(l/16) + 8t + e, so each lane reads one contiguous 32-byte run of its
-// chunk's codes.  Fragment f = (layer * 4 + head_tile) * 4 + t.
-__global__ __launch_bounds__(256) void pack_q_kernel(const float* q, int B, f16x8* qpack) {
+// chunk's codes.  Fragment f = (layer * 4 + head_tile) * 4 + t for the
+// heads; fragment 48 + t holds the linear-term rows for k-step t: row l
+// (l < 3) is the high f16 part of v_l = 1/2 sum_h w_{l,h} q_{l,h} (with q
+// already rounded to f16, the sum in fp32), row 4 + l the low part
+// v_l - hi, other rows zero.  The MFMA output of that tile then holds, in
+// lane group 0, the high part of layer r's term in element r, and in lane
+// group 1 the low part.
+__global__ __launch_bounds__(256) void pack_q_kernel(const float* q, const float* w, int B, f16x8* qpack) {
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= B * kQFrags * 64) return;
   const int lane = gid & 63;
   const int f = (gid >> 6) % kQFrags;
   const int b = gid / (64 * kQFrags);
   const int t = f & 3;
-  const int mt = (f >> 2) & 3;
-  const int layer = f >> 4;
-  const int head = 16 * mt + (lane & 15);
-  const int d0 = 32 * (lane >> 4) + 8 * t;
-  const float* src = q + (((size_t)layer * B + b) * kHeads + head) * kHeadDim + d0;
-  const float4 v0 = *(const float4*)src;
-  const float4 v1 = *(const float4*)(src + 4);
-  f16x8 v = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
-             (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
-  qpack[gid] = v;
+  if (f < kQHeadFrags) {
+    const int mt = (f >> 2) & 3;
+    const int layer = f >> 4;
+    const int head = 16 * mt + (lane & 15);
+    const int d0 = 32 * (lane >> 4) + 8 * t;
+    const float* src = q + (((size_t)layer * B + b) * kHeads + head) * kHeadDim + d0;
+    const float4 v0 = *(const float4*)src;
+    const float4 v1 = *(const float4*)(src + 4);
+    f16x8 v = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
+               (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
+    qpack[gid] = v;
+    return;
+  }
+  const int row = lane & 15;
+  const int layer = row & 3;
+  f16x8 out = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (layer < kLayers && row < 8) {
+    const int d0 = 32 * (lane >> 4) + 8 * t;
+    const float* qb = q + ((size_t)layer * B + b) * kHeads * kHeadDim + d0;
+    const float* wb = w + ((size_t)layer * B + b) * kHeads;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int h = 0; h < kHeads; ++h) {
+      const float wh = wb[h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(wh, (float)(_Float16)qb[h * kHeadDim + e], v[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float half = 0.5f * v[e];
+      const _Float16 hi = (_Float16)half;
+      out[e] = row < 4 ? hi : (_Float16)(half - (float)hi);
+    }
+  }
+  qpack[gid] = out;
 }
 
 __device__ __forceinline__ f16x8 decode8(uint32_t lo, uint32_t hi) {
@@ -102,8 +139,9 @@ struct Ctx {
   int c, g;
 };
 
-// An offset past every buffer of one wave (they hold at most 4 * kCPW bytes
-// of scores): the store is dropped by the range check, with no branch.
+// An offset past every buffer of one pipeline run (they hold at most
+// 16 kMaxSegTiles + 8 tiles of records): the store is dropped by the range
+// check, with no branch.
 constexpr uint32_t kDropOffset = 0x40000000u;
 
 // Offsets go in the per-lane voffset (the range check covers voffset).
@@ -121,28 +159,29 @@ __device__ __forceinline__ void decode_tile(const RawTile& t, f16x8 (&kf)[4]) {
   kf[3] = decode8(t.hi[2], t.hi[3]);
 }
 
-__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const f16x8 (&kf)[4],
-                                          f32x4 (&acc)[kLayers][4]) {
+__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const f16x8 (&ql)[4], const f16x8 (&kf)[4],
+                                          f32x4 (&acc)[kLayers][4], f32x4& lin) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][0], kf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    for (int mt = 0; mt < 4; ++mt) acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][0], kf[0], zero, 0, 0, 0);
+  lin = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[0], kf[0], zero, 0, 0, 0);
 #pragma unroll
-  for (int t = 1; t < 4; ++t)
+  for (int t = 1; t < 4; ++t) {
 #pragma unroll
     for (int l = 0; l < kLayers; ++l)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][t], kf[t], acc[l][mt], 0, 0, 0);
+    lin = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[t], kf[t], lin, 0, 0, 0);
+  }
 }
 
-// Head reduction, sigmoid, ensemble and store of one tile.
+// Head reduction, sigmoid, ensemble and store of one tile.  wh = w / 2.
 template <bool MEAN, bool PER_LAYER>
-__device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4],
-                                            const f32x4 (&wv)[kLayers][4], float s, int tile) {
-  // B = copysign(inf, s): med3(x, 0, B) is relu(x) for s >= 0 and min(x, 0) for s < 0.
-  const float bound = __uint_as_float((__float_as_uint(s) & 0x80000000u) | 0x7f800000u);
+__device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
+                                            const f32x4 (&wh)[kLayers][4], float s, int tile) {
   float t[kLayers];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -150,8 +189,10 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p = fmaf(__builtin_amdgcn_fmed3f(acc[l][mt][r], 0.f, bound), wv[l][mt][r], p);
-    t[l] = s * sum4groups(p);  // the layer's logit
+      for (int r = 0; r < 4; ++r) p = fmaf(fabsf(acc[l][mt][r]), wh[l][mt][r], p);
+    // |s| p + s lin: lane group 0 adds the high part of the linear term,
+    // group 1 the low part, groups 2 and 3 hold zeros there.
+    t[l] = sum4groups(fmaf(s, lin[l], fabsf(s) * p));  // the layer's logit
   }
   float e;
   float sl[kLayers];
@@ -172,15 +213,15 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
 }
 
 // Instruction order of one phase for the scheduler: every MFMA followed by
-// three vector-ALU instructions (a wave issues in order, so the vector work
+// two vector-ALU instructions (a wave issues in order, so the vector work
 // of the reduction and decode must sit between the MFMAs to overlap them),
 // then the phase's requests (after the decode has consumed the ring slot
 // they refill) and its stores.
 __device__ __forceinline__ void interleave_phase() {
 #pragma unroll
-  for (int k = 0; k < kLayers * 4 * 4; ++k) {
+  for (int k = 0; k < kLayers * 4 * 4 + 4; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
   }
   __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);    // VMEM read: codes, scale
   __builtin_amdgcn_sched_group_barrier(0x040, 4, 0);    // VMEM write
@@ -189,44 +230,19 @@ __device__ __forceinline__ void interleave_phase() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// grid = (ceil(N / (4 * kCPW)), B), block = 256: wave w of block x scores
-// chunks [(4x + w) kCPW, +kCPW) of row blockIdx.y in tiles of 16.
+// One pipeline run: tiles of chunks [start, start + count) of row b, every
+// chunk below the row's valid_n.
 //
 // Software pipeline, one wave per SIMD: in the phase of tile i the wave
-// issues the 48 MFMAs of tile i while the vector unit reduces tile i-1 and
-// decodes tile i+1; the records of tile i+4 are requested in the same
-// phase (4 tiles in flight).  Tiles past the wave's valid chunks read as
-// zeros and their stores are dropped by the buffer range checks.
+// issues the 52 MFMAs of tile i, interleaved with the reduction of tile i-1
+// and the decode of tile i+1; the records of tile i+6 are requested in the
+// same phase (6 tiles in flight).  Tiles past the run's chunks read as zeros
+// and their stores are dropped by the buffer range checks.
 template <bool MEAN, bool PER_LAYER>
-__global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
-                                                       const uint8_t* __restrict__ comp_k, int B, int64_t N,
-                                                       const int32_t* __restrict__ valid_n,
-                                                       float* __restrict__ scores, float* __restrict__ per_layer) {
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps descriptors scalar
-  const int64_t start = ((int64_t)blockIdx.x * 4 + wave) * kCPW;
-  if (start >= N) return;
-  const int64_t end = start + kCPW < N ? start + kCPW : N;
-  int64_t vn = N;
-  if (valid_n) {
-    const int64_t v = valid_n[b];
-    vn = v < 0 ? 0 : (v > N ? N : v);
-  }
-  const int64_t vend = end < vn ? end : vn;
-
-  // Tail at or beyond valid_n: -inf, bytes not read.
-  {
-    const float ninf = -__builtin_huge_valf();
-    for (int64_t n = (start > vn ? start : vn) + lane; n < end; n += 64) {
-      scores[(size_t)b * N + n] = ninf;
-      if (PER_LAYER)
-        for (int l = 0; l < kLayers; ++l) per_layer[((size_t)l * B + b) * N + n] = ninf;
-    }
-  }
-  if (start >= vend) return;
-  const int64_t count = vend - start;
-
+__device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const float* __restrict__ w,
+                                          const uint8_t* __restrict__ comp_k, int B, int64_t N, int b, int64_t start,
+                                          int64_t count, int lane, float* __restrict__ scores,
+                                          float* __restrict__ per_layer) {
   Ctx cx;
   cx.c = lane & 15;
   cx.g = lane >> 4;
@@ -249,7 +265,12 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) load_tile(cx, k, ring[k]);
 
+  // Query fragments, linear-term fragments and w: every load is issued
+  // before the first use, so the wave pays one memory latency here, not one
+  // per fragment.
   f16x8 qf[kLayers][4][4];
+  f16x8 ql[4];
+  f32x4 wv[kLayers][4];  // w / 2 of the heads this lane's accumulators hold: 16 mt + 4 g + r
   {
     const f16x8* qp = qpack + (size_t)b * kQFrags * 64 + lane;
 #pragma unroll
@@ -257,23 +278,32 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
-          // Keep the query fragments in accumulation registers: the MFMA reads
-          // its A operand from there, leaving the vector registers to the
-          // accumulators, decoded keys and records in flight.
-          asm volatile("" : "+a"(qf[l][mt][t]));
-        }
+        for (int t = 0; t < 4; ++t) qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ql[t] = qp[(kQHeadFrags + t) * 64];
+#pragma unroll
+    for (int l = 0; l < kLayers; ++l)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) wv[l][mt] = *(const f32x4*)(w + ((size_t)l * B + b) * kHeads + 16 * mt + 4 * cx.g);
   }
-  // w of the heads this lane's accumulators hold: 16 mt + 4 g + r.
-  f32x4 wv[kLayers][4];
+  // Keep the query fragments in accumulation registers: the MFMA reads its A
+  // operand from there, leaving the vector registers to the accumulators,
+  // decoded keys and records in flight.
+#pragma unroll
+  for (int l = 0; l < kLayers; ++l)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(qf[l][mt][t]));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(ql[t]));
+  // Consume w here, so its wait is paid before the loop; a wait inside the
+  // loop would also drain the records in flight.
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      wv[l][mt] = *(const f32x4*)(w + ((size_t)l * B + b) * kHeads + 16 * mt + 4 * cx.g);
-      // Consume the loaded value here, so its wait is paid once, before the
-      // loop; a wait inside the loop would also drain the records in flight.
+      wv[l][mt] = 0.5f * wv[l][mt];
       asm volatile("" : "+v"(wv[l][mt]));
     }
 
@@ -281,6 +311,7 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
 
   f16x8 kf[2][4];
   f32x4 acc[2][kLayers][4];
+  f32x4 lin[2];
 
   // Phase of tile i, P = i mod 8 (compile-time, so every register index is
   // static): MFMAs of tile i; finish tile i-1 (its scale still in its ring
@@ -288,8 +319,9 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
   // into the slot of tile i-2, finished in the previous phase.
 #define FM_PHASE(P, I)                                                                                \
   {                                                                                                   \
-    mfma_tile(qf, kf[(P) & 1], acc[(P) & 1]);                                                         \
-    finish_tile<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], wv, ring[((P) + 7) & 7].s, (I) - 1);         \
+    mfma_tile(qf, ql, kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                                       \
+    finish_tile<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ring[((P) + 7) & 7].s,  \
+                                 (I) - 1);                                                            \
     decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
     interleave_phase();                                                                               \
@@ -297,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
 
   // Tile 0 (nothing to finish yet).
   decode_tile(ring[0], kf[0]);
-  mfma_tile(qf, kf[0], acc[0]);
+  mfma_tile(qf, ql, kf[0], acc[0], lin[0]);
   decode_tile(ring[1], kf[1]);
   load_tile(cx, kAhead, ring[kAhead]);
 
@@ -316,8 +348,132 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
     FM_PHASE(0, i + 7)
     i += 8;
   } while (i < tiles);
-  finish_tile<MEAN, PER_LAYER>(cx, acc[0], wv, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
+  finish_tile<MEAN, PER_LAYER>(cx, acc[0], lin[0], wv, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
 #undef FM_PHASE
+}
+
+// grid = number of compute units, block = 256 (one wave per SIMD).  The
+// valid tiles of all rows, in row-major order, are split into equal
+// contiguous shares, one per wave: with row_tiles (prefix of the rows'
+// valid tile counts, from the plan kernel) when rows are ragged, else every
+// row has ceil(N / 16) tiles.  A share may end in the next row (or, for
+// short rows, several rows later): each row's part is its own pipeline run.
+template <bool MEAN, bool PER_LAYER>
+__global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
+                                                       const uint8_t* __restrict__ comp_k, int B, int64_t N,
+                                                       const int32_t* __restrict__ valid_n,
+                                                       const int64_t* __restrict__ row_tiles,
+                                                       const int32_t* __restrict__ wave_row,
+                                                       int64_t total_tiles,  // used when row_tiles is null
+                                                       float* __restrict__ scores, float* __restrict__ per_layer) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps descriptors scalar
+  const int64_t waves = 4 * (int64_t)gridDim.x;
+  const int64_t gw = 4 * (int64_t)blockIdx.x + wave;
+  const int64_t total = row_tiles ? row_tiles[B] : total_tiles;
+  int64_t t = gw * total / waves;
+  const int64_t t_end = (gw + 1) * total / waves;
+  if (t >= t_end) return;
+  const int64_t row_full = (N + kTile - 1) / kTile;
+  int b;
+  int64_t first;  // list index of row b's first tile
+  if (row_tiles) {
+    b = wave_row[gw];
+    first = row_tiles[b];
+  } else {
+    b = (int)(t / row_full);
+    first = (int64_t)b * row_full;
+  }
+  while (t < t_end) {
+    const int64_t last = row_tiles ? row_tiles[b + 1] : first + row_full;
+    int64_t run_end = t_end < last ? t_end : last;
+    if (run_end - t > kMaxSegTiles) run_end = t + kMaxSegTiles;
+    if (run_end > t) {
+      int64_t vn = N;
+      if (valid_n) {
+        const int64_t v = valid_n[b];
+        vn = v < 0 ? 0 : (v > N ? N : v);
+      }
+      const int64_t start = (t - first) * kTile;
+      const int64_t end = run_end - first == last - first ? vn : (run_end - first) * kTile;
+      score_run<MEAN, PER_LAYER>(qpack, w, comp_k, B, N, b, start, end - start, lane, scores, per_layer);
+    }
+    t = run_end;
+    if (t >= last) {
+      ++b;
+      first = last;
+    }
+  }
+}
+
+// Plan for ragged rows (one block of 1024 threads): row_tiles[b] = sum of
+// ceil(valid_n / 16) over the rows before b (row_tiles[B] = all tiles), and
+// for each wave the row holding its first tile.
+__global__ __launch_bounds__(1024) void score_plan_kernel(const int32_t* __restrict__ valid_n, int B, int64_t N,
+                                                          int waves, int64_t* __restrict__ row_tiles,
+                                                          int32_t* __restrict__ wave_row) {
+  __shared__ int64_t s_pre[4096 + 1];
+  __shared__ int64_t s_wsum[16];
+  const int t = threadIdx.x;
+  const int per = (B + 1023) / 1024;  // rows per thread, consecutive
+  int64_t cnt[4] = {0, 0, 0, 0};
+  int64_t tot = 0;
+  for (int j = 0; j < per; ++j) {
+    const int r = t * per + j;
+    if (r < B) {
+      const int64_t v = valid_n[r];
+      const int64_t vn = v < 0 ? 0 : (v > N ? N : v);
+      cnt[j] = (vn + kTile - 1) / kTile;
+      tot += cnt[j];
+    }
+  }
+  // Exclusive scan of the per-thread totals: wave shuffles, then across waves.
+  int64_t incl = tot;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t v = __shfl_up(incl, off, 64);
+    if ((t & 63) >= off) incl += v;
+  }
+  if ((t & 63) == 63) s_wsum[t >> 6] = incl;
+  __syncthreads();
+  int64_t before = 0;
+  for (int wv = 0; wv < (t >> 6); ++wv) before += s_wsum[wv];
+  int64_t acc = before + incl - tot;
+  for (int j = 0; j < per; ++j) {
+    const int r = t * per + j;
+    if (r < B) {
+      s_pre[r] = acc;
+      acc += cnt[j];
+    }
+  }
+  if (t == 1023) s_pre[B] = before + incl;  // the last thread's inclusive total is the grand total
+  __syncthreads();
+  const int64_t total = s_pre[B];
+  for (int r = t; r <= B; r += 1024) row_tiles[r] = s_pre[r];
+  for (int g = t; g < waves; g += 1024) {
+    const int64_t first = (int64_t)g * total / waves;
+    int lo = 0, hi = B - 1;  // largest row with s_pre[row] <= first
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= first) lo = mid;
+      else hi = mid - 1;
+    }
+    wave_row[g] = lo;
+  }
+}
+
+// -inf for the chunks of each row at or beyond its valid_n.
+template <bool PER_LAYER>
+__global__ __launch_bounds__(256) void score_tail_kernel(const int32_t* __restrict__ valid_n, int B, int64_t N,
+                                                         float* __restrict__ scores, float* __restrict__ per_layer) {
+  const int b = blockIdx.y;
+  const int64_t v = valid_n[b];
+  const int64_t vn = v < 0 ? 0 : (v > N ? N : v);
+  const float ninf = -__builtin_huge_valf();
+  for (int64_t n = vn + (int64_t)blockIdx.x * 256 + threadIdx.x; n < N; n += (int64_t)gridDim.x * 256) {
+    scores[(size_t)b * N + n] = ninf;
+    if (PER_LAYER)
+      for (int l = 0; l < kLayers; ++l) per_layer[((size_t)l * B + b) * N + n] = ninf;
+  }
 }
 
 }  // namespace
@@ -327,15 +483,27 @@ hipError_t launch_score(const Workspace& ws, const float* q, const float* w, con
   f16x8* qpack = (f16x8*)ws.qpack;
   {
     const int total = B * kQFrags * 64;
-    hipLaunchKernelGGL(pack_q_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, q, B, qpack);
+    hipLaunchKernelGGL(pack_q_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, q, w, B, qpack);
   }
-  const int64_t per_block = 4 * (int64_t)kCPW;
-  dim3 grid((unsigned)((N + per_block - 1) / per_block), (unsigned)B);
+  const int blocks = ws.score_blocks;
+  const int waves = 4 * blocks;
+  int64_t total_tiles = (int64_t)B * ((N + kTile - 1) / kTile);
+  const int64_t* row_tiles = nullptr;
+  if (valid_n) {
+    hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(1024), 0, stream, valid_n, B, N, waves, ws.row_tiles,
+                       ws.wave_row);
+    row_tiles = ws.row_tiles;
+    const unsigned gx = (unsigned)std::min<int64_t>((N + 255) / 256, 64);
+    if (per_layer)
+      hipLaunchKernelGGL(score_tail_kernel<true>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores, per_layer);
+    else
+      hipLaunchKernelGGL(score_tail_kernel<false>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores, per_layer);
+  }
   const bool mean = mode == FM_ENSEMBLE_MEAN;
   auto kern = mean ? (per_layer ? score_kernel<true, true> : score_kernel<true, false>)
                    : (per_layer ? score_kernel<false, true> : score_kernel<false, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n, scores,
-                     per_layer);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n, row_tiles,
+                     (const int32_t*)ws.wave_row, total_tiles, scores, per_layer);
   return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ enum : uint32_t { kSelect = 0, kKeepAll = 1, kKeepNone = 2 };
 constexpr int kSampleRuns = 64;
 constexpr int kSampleRun = 128;
 constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 8192
-constexpr int kSampleThreads = 256;
+constexpr int kSampleThreads = 1024;
+constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 8
 
 // Block-wide: the digit (bin) holding the k-th element (1-based) of a
 // histogram, counting from the top bin down (largest) or from bin 0 up, and
@@ -100,7 +101,7 @@ __device__ void block_find(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
 // T (1-based k <= stream size) and the largest index kept among the keys
 // equal to T when ties go to the lowest indices.  Digit passes: key bits
 // 31..21, 20..10, 9..0, then the same over the index of keys equal to T.
-template <int THREADS, typename Each>
+template <int THREADS, bool WITH_INDEX = true, typename Each>
 __device__ void radix_select(Each each, uint32_t k, uint32_t* h, uint32_t* s_wtot, uint32_t* s_out, uint32_t* T_out,
                              uint32_t* last_out) {
   uint32_t prefix = 0;
@@ -120,6 +121,8 @@ __device__ void radix_select(Each each, uint32_t k, uint32_t* h, uint32_t* s_wto
     __syncthreads();
   }
   const uint32_t T = prefix;  // k = keys equal to T still to keep (>= 1)
+  *T_out = T;
+  if (!WITH_INDEX) return;
   uint32_t iprefix = 0;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -136,7 +139,6 @@ __device__ void radix_select(Each each, uint32_t k, uint32_t* h, uint32_t* s_wto
     k -= s_out[1];
     __syncthreads();
   }
-  *T_out = T;
   *last_out = iprefix;
 }
 
@@ -163,13 +165,25 @@ __global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float*
   const float* row = scores + (size_t)b * N;
   const bool whole = vn <= kSampleSize;
   const uint32_t S = whole ? (uint32_t)vn : (uint32_t)kSampleSize;
-  for (uint32_t i = threadIdx.x; i < S; i += kSampleThreads) {
+  // Sample i = t + kSampleThreads * j sits in run r = i / kSampleRun at
+  // offset t % kSampleRun; run r starts at r (vn - kSampleRun) / 63.  All
+  // loads are issued before the first LDS store.
+  const int t = threadIdx.x;
+  float v[kSamplePerThread];
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) {
+    const uint32_t i = (uint32_t)t + kSampleThreads * j;
     int64_t n = i;
     if (!whole) {
-      const int64_t r = i / kSampleRun;
+      const int64_t r = (int64_t)(i / kSampleRun);
       n = r * (vn - kSampleRun) / (kSampleRuns - 1) + (i % kSampleRun);
     }
-    s_keys[i] = order_key(row[n]);
+    v[j] = i < S ? row[n] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) {
+    const uint32_t i = (uint32_t)t + kSampleThreads * j;
+    if (i < S) s_keys[i] = order_key(v[j]);
   }
   __syncthreads();
   uint32_t m;
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float*
     m = mm >= (double)S ? S : (uint32_t)mm;
   }
   uint32_t L, unused;
-  radix_select<kSampleThreads>(
+  radix_select<kSampleThreads, false>(
       [&](auto f) {
         for (uint32_t i = threadIdx.x; i < S; i += kSampleThreads) f(make_uint2(s_keys[i], i));
       },

@@ -96,6 +96,27 @@ def test_ragged_sizes_match_oracle(retr, qw, n):
     assert e <= SCORE_TOL
 
 
+def test_many_ragged_rows_share_waves(retr, qw):
+    """40 rows of assorted valid lengths (empty, sub-tile, one tile plus one,
+    full): the valid tiles of all rows are split evenly over the waves, so
+    waves start and end inside rows and step over empty ones."""
+    q, w = qw
+    B, n = 40, 3000
+    pick = [i % 4 for i in range(B)]
+    qb, wb = q[:, pick], w[:, pick]
+    vn = np.array([0, 1, 15, 16, 17, 100, 2999, 3000, 0, 0] * 4, np.int32)
+    vn[10:20] = np.random.default_rng(31).integers(0, n + 1, 10)
+    ck = records(n, 30, rows=B)
+    for b in range(B):
+        ck[b, vn[b]:] = 0xFF
+    for mode in ("max", "mean"):
+        s, p = run(retr, qb, wb, ck, vn, mode)
+        per_ref, ens_ref = oracle_scores(ck, qb, wb, vn, mode)
+        e = max(max_score_err(s, ens_ref), max_score_err(p, per_ref))
+        report(f"40 ragged rows {mode}", max_abs=e)
+        assert e <= SCORE_TOL
+
+
 def test_empty_rows_and_zero_valid(retr, qw, fm_lib):
     q, w = qw
     ck = records(64, 5, rows=2)
