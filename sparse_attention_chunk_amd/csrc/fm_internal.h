@@ -22,21 +22,23 @@ constexpr int kRopeDim = 64;
 constexpr int kRecord = kHeadDim + 4;
 
 // First projection: wq_a rows [0, 1024) and weights_proj rows [1024, 1088)
-// share one pass over `hidden`.  Both projections split K so that a launch
-// has a few thousand waves (the weights stream from HBM once, the partial
-// sums are added in slice order by the next kernel).  A wave covers up to
-// 32 batch rows; more rows go to further wave groups.
+// share one pass over `hidden`.  A wave covers 16 outputs x up to 32 batch
+// rows over a K slice of at least four 256-wide chunks (more rows go to
+// further wave groups); the first projection splits K so that one row group
+// still has about one wave per SIMD (the weights stream from HBM once, the
+// partial sums are added in slice order by the next kernel).
 constexpr int kProj1Out = kQLora + kHeads;
 constexpr int kProjRowsPerWave = 32;
 
 inline int proj_row_groups(int B) { return (B + kProjRowsPerWave - 1) / kProjRowsPerWave; }
-// K slices of the first projection (K = 4096): 16 for one row group, fewer for more.
+// K slices of the first projection (K = 4096): 4 for one row group, 2 for
+// two, 1 beyond.
 inline int proj1_splits(int B) {
   const int g = proj_row_groups(B);
-  return g <= 1 ? 16 : (g <= 2 ? 8 : (g <= 4 ? 4 : (g <= 8 ? 2 : 1)));
+  return g <= 1 ? 4 : (g <= 2 ? 2 : 1);
 }
 // K slices of wq_b (K = 1024).
-inline int proj2_splits(int B) { return proj_row_groups(B) <= 1 ? 2 : 1; }
+inline int proj2_splits(int) { return 1; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,

@@ -54,47 +54,72 @@ constexpr int kAhead = 6;                        // tile i + 6 is requested in t
 // v_l - hi, other rows zero.  The MFMA output of that tile then holds, in
 // lane group 0, the high part of layer r's term in element r, and in lane
 // group 1 the low part.
-__global__ __launch_bounds__(256) void pack_q_kernel(const float* q, const float* w, int B, f16x8* qpack) {
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= B * kQFrags * 64) return;
-  const int lane = gid & 63;
-  const int f = (gid >> 6) % kQFrags;
-  const int b = gid / (64 * kQFrags);
-  const int t = f & 3;
-  if (f < kQHeadFrags) {
-    const int mt = (f >> 2) & 3;
-    const int layer = f >> 4;
-    const int head = 16 * mt + (lane & 15);
-    const int d0 = 32 * (lane >> 4) + 8 * t;
-    const float* src = q + (((size_t)layer * B + b) * kHeads + head) * kHeadDim + d0;
-    const float4 v0 = *(const float4*)src;
-    const float4 v1 = *(const float4*)(src + 4);
-    f16x8 v = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
-               (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
-    qpack[gid] = v;
-    return;
-  }
-  const int row = lane & 15;
-  const int layer = row & 3;
-  f16x8 out = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (layer < kLayers && row < 8) {
-    const int d0 = 32 * (lane >> 4) + 8 * t;
-    const float* qb = q + ((size_t)layer * B + b) * kHeads * kHeadDim + d0;
-    const float* wb = w + ((size_t)layer * B + b) * kHeads;
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int h = 0; h < kHeads; ++h) {
-      const float wh = wb[h];
+// One block per (row, layer), 256 threads.  Thread t packs the head
+// fragments o = t + 256 j (j = 0..3; fragment o / 64, lane o % 64) from two
+// float4 loads each, all issued first, and keeps the f16 queries in LDS;
+// then v_d = 1/2 sum_h w_h q_hd is summed in two head halves (fp32), split
+// into hi + lo f16 parts and scattered to the linear-term rows of this
+// layer.  The layer-0 block also writes the zero rows.
+__global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q, const float* __restrict__ w, int B,
+                                                     f16x8* __restrict__ qpack) {
+  __shared__ __attribute__((aligned(16))) _Float16 qs[kHeads][kHeadDim + 8];
+  __shared__ float red[2][kHeadDim];
+  __shared__ __attribute__((aligned(16))) _Float16 lin[4][4][2][8];  // [t][g][hi, lo][e]
+  const int b = blockIdx.x / kLayers;
+  const int layer = blockIdx.x % kLayers;
+  const int t = threadIdx.x;
+  const float* qb = q + ((size_t)layer * B + b) * kHeads * kHeadDim;
+  f16x8* out = qpack + (size_t)b * kQFrags * 64;
+  float4 v[4][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = fmaf(wh, (float)(_Float16)qb[h * kHeadDim + e], v[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float half = 0.5f * v[e];
-      const _Float16 hi = (_Float16)half;
-      out[e] = row < 4 ? hi : (_Float16)(half - (float)hi);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int o = t + 256 * j;
+    const int f = o >> 6, lane = o & 63;
+    const int head = 16 * (f >> 2) + (lane & 15);
+    const int d0 = 32 * (lane >> 4) + 8 * (f & 3);
+    v[j][0] = *(const float4*)(qb + head * kHeadDim + d0);
+    v[j][1] = *(const float4*)(qb + head * kHeadDim + d0 + 4);
   }
-  qpack[gid] = out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int o = t + 256 * j;
+    const int f = o >> 6, lane = o & 63;
+    const int head = 16 * (f >> 2) + (lane & 15);
+    const int d0 = 32 * (lane >> 4) + 8 * (f & 3);
+    const f16x8 h = {(_Float16)v[j][0].x, (_Float16)v[j][0].y, (_Float16)v[j][0].z, (_Float16)v[j][0].w,
+                     (_Float16)v[j][1].x, (_Float16)v[j][1].y, (_Float16)v[j][1].z, (_Float16)v[j][1].w};
+    out[(layer * 16 + f) * 64 + lane] = h;
+    *(f16x8*)&qs[head][d0] = h;
+  }
+  __syncthreads();
+  {
+    const int d = t & (kHeadDim - 1), half = t >> 7;
+    const float* wb = w + ((size_t)layer * B + b) * kHeads + 32 * half;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int h = 0; h < 32; ++h) acc = fmaf(wb[h], (float)qs[32 * half + h][d], acc);
+    red[half][d] = acc;
+  }
+  __syncthreads();
+  if (t < kHeadDim) {
+    const float vd = 0.5f * (red[0][t] + red[1][t]);
+    const _Float16 hi = (_Float16)vd;
+    const _Float16 lo = (_Float16)(vd - (float)hi);
+    const int g = t >> 5, ks = (t >> 3) & 3, e = t & 7;  // dim t = 32 g + 8 ks + e
+    lin[ks][g][0][e] = hi;
+    lin[ks][g][1][e] = lo;
+  }
+  __syncthreads();
+  if (t < 32) {
+    const int ks = t >> 3, g = (t >> 1) & 3, part = t & 1;
+    const int row = part ? 4 + layer : layer;
+    out[(kQHeadFrags + ks) * 64 + row + 16 * g] = *(const f16x8*)&lin[ks][g][part][0];
+  }
+  if (layer == 0 && t < 4 * 4 * 10) {  // rows 3, 7, 8 .. 15 of every (k-step, lane group)
+    const int ks = t / 40, g = (t / 10) & 3, z = t % 10;
+    const int row = z == 0 ? 3 : (z == 1 ? 7 : 6 + z);
+    out[(kQHeadFrags + ks) * 64 + row + 16 * g] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
 }
 
 __device__ __forceinline__ f16x8 decode8(uint32_t lo, uint32_t hi) {
@@ -481,10 +506,7 @@ __global__ __launch_bounds__(256) void score_tail_kernel(const int32_t* __restri
 hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
                         const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream) {
   f16x8* qpack = (f16x8*)ws.qpack;
-  {
-    const int total = B * kQFrags * 64;
-    hipLaunchKernelGGL(pack_q_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, q, w, B, qpack);
-  }
+  hipLaunchKernelGGL(pack_q_kernel, dim3(B * kLayers), dim3(256), 0, stream, q, w, B, qpack);
   const int blocks = ws.score_blocks;
   const int waves = 4 * blocks;
   int64_t total_tiles = (int64_t)B * ((N + kTile - 1) / kTile);
