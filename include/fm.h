@@ -22,8 +22,9 @@
  * Conventions shared by every call:
  *   - Pointers named as device pointers must be device memory of the GPU
  *     that was current when the context was created; host pointers are
- *     named as such.  The caller owns every buffer.  Weights are borrowed
- *     by the context and must outlive it.
+ *     named as such.  The caller owns every buffer.  fm_create copies the
+ *     weights into the context (in its own packed form): the weight buffers
+ *     are not used after fm_create returns.
  *   - Row-major layouts, no padding: [B, N] has row stride N.
  *   - Float buffers must be 4-byte aligned, positions 8-byte aligned,
  *     comp_k 4-byte aligned (its records sit at a 132-byte stride).
@@ -102,9 +103,13 @@ typedef struct {
 void fm_config_default(fm_config* cfg);
 
 /* Creates a context on the current HIP device.  Checks cfg, derives the
- * RoPE/YaRN frequencies (in double precision) and allocates the workspace
- * for up to max_batch rows of up to max_n chunks.  max_batch in [1, 4096],
- * max_n in [1, 2^26].  On success *out receives the context. */
+ * RoPE/YaRN frequencies (in double precision), allocates the workspace for
+ * up to max_batch rows of up to max_n chunks and packs the weights into it:
+ * every weight row is scaled by a power of two and split into two f16
+ * parts (hi + lo, 4 bytes per weight), so that the projections run on the
+ * f16 MFMA at about fp32 accuracy.  Synchronises the device before
+ * returning.  max_batch in [1, 4096], max_n in [1, 2^26].  On success *out
+ * receives the context. */
 fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max_batch, int64_t max_n,
                     fm_ctx** out);
 

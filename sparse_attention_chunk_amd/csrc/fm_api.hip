@@ -148,9 +148,15 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   }
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
   enum {
-    kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kRowTiles, kWaveRow, kSelState, kSelCand, kSelCount, kNumBuffers
+    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kRowTiles, kWaveRow, kSelState,
+    kSelCand, kSelCount, kNumBuffers
   };
   size_t sizes[kNumBuffers];
+  sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
+  sizes[kW1Inv] = sizeof(float) * kLayers * kProj1Out;
+  sizes[kW2] = (size_t)4 * kLayers * kHeads * kHeadDim * kQLora;
+  sizes[kW2Inv] = sizeof(float) * kLayers * kHeads * kHeadDim;
+  sizes[kGain] = sizeof(float) * kLayers * kQLora;
   sizes[kPart1] = sizeof(float) * kLayers * p1_rows * kProj1Out;
   sizes[kAHat] = sizeof(float) * kLayers * mb * kQLora;
   sizes[kQLin] = sizeof(float) * kLayers * p2_rows * kHeads * kHeadDim;
@@ -181,6 +187,11 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws_base = base;
   ctx->ws_bytes = total;
   char* p = (char*)base;
+  ctx->ws.w1 = (_Float16*)(p + offs[kW1]);
+  ctx->ws.w1_inv = (float*)(p + offs[kW1Inv]);
+  ctx->ws.w2 = (_Float16*)(p + offs[kW2]);
+  ctx->ws.w2_inv = (float*)(p + offs[kW2Inv]);
+  ctx->ws.q_norm = (float*)(p + offs[kGain]);
   ctx->ws.proj1_part = (float*)(p + offs[kPart1]);
   ctx->ws.a_hat = (float*)(p + offs[kAHat]);
   ctx->ws.q_lin = (float*)(p + offs[kQLin]);
@@ -197,6 +208,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
   e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = launch_pack_weights(*weights, ctx->ws, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(base);

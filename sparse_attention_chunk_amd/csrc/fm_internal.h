@@ -23,22 +23,18 @@ constexpr int kRecord = kHeadDim + 4;
 
 // First projection: wq_a rows [0, 1024) and weights_proj rows [1024, 1088)
 // share one pass over `hidden`.  A wave covers 16 outputs x up to 32 batch
-// rows over a K slice of at least four 256-wide chunks (more rows go to
-// further wave groups); the first projection splits K so that one row group
-// still has about one wave per SIMD (the weights stream from HBM once, the
-// partial sums are added in slice order by the next kernel).
+// rows over one 512-wide K slice (more rows go to further wave groups); the
+// slice partial sums are added in slice order by the next kernel, so the
+// weights stream from HBM once.
 constexpr int kProj1Out = kQLora + kHeads;
 constexpr int kProjRowsPerWave = 32;
+constexpr int kSliceK = 512;
+constexpr int kSliceChunks = kSliceK / 128;
 
 inline int proj_row_groups(int B) { return (B + kProjRowsPerWave - 1) / kProjRowsPerWave; }
-// K slices of the first projection (K = 4096): 4 for one row group, 2 for
-// two, 1 beyond.
-inline int proj1_splits(int B) {
-  const int g = proj_row_groups(B);
-  return g <= 1 ? 4 : (g <= 2 ? 2 : 1);
-}
-// K slices of wq_b (K = 1024).
-inline int proj2_splits(int) { return 1; }
+// K slices of the first projection (K = 4096) and of wq_b (K = 1024).
+inline int proj1_splits(int) { return kHidden / kSliceK; }
+inline int proj2_splits(int) { return kQLora / kSliceK; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,
@@ -56,6 +52,14 @@ constexpr int kSelSlice = kSelThreads * kSelItems;
 constexpr int kSelBins = 2048;
 
 struct Workspace {
+  // Weights packed at context creation: each row scaled by a power of two
+  // and split into f16 hi + lo parts, in 16-row tiles of 2 KB k-steps (the
+  // projection kernel's operand order), with each row's 2^-e.
+  _Float16* w1 = nullptr;        // [3][kProj1Out * kHidden * 2]: wq_a rows, then weights_proj rows
+  float* w1_inv = nullptr;       // [3][kProj1Out]
+  _Float16* w2 = nullptr;        // [3][kHeads * kHeadDim * kQLora * 2]: wq_b
+  float* w2_inv = nullptr;       // [3][kHeads * kHeadDim]
+  float* q_norm = nullptr;       // [3][kQLora] RMSNorm gains
   float* proj1_part = nullptr;   // [proj1_splits(B)][3][B][kProj1Out]
   float* a_hat = nullptr;        // [3][max_batch][kQLora]
   float* q_lin = nullptr;        // [proj2_splits(B)][3][B][kHeads * kHeadDim]
@@ -72,6 +76,10 @@ struct Workspace {
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
 // status (hipGetLastError after the launches).
+
+// Packs the caller's fp32 weights into the workspace (hi/lo parts, row
+// scales, gains).
+hipError_t launch_pack_weights(const fm_weights& wts, const Workspace& ws, hipStream_t stream);
 hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, const Workspace& ws, int max_batch,
                                 const float* hidden, const int64_t* positions, int B, float* q_out, float* w_out,
                                 hipStream_t stream);

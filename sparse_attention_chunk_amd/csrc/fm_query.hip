@@ -7,9 +7,15 @@
 //   w      = weights_proj hidden * HEAD_DIM^-0.5 N_HEADS^-0.5
 //
 // The projections are skinny fp32 GEMMs (B <= a few dozen rows against up
-// to 8192 weight rows), bound by streaming the fp32 weights from HBM.  They
-// run on the fp32 MFMA (v_mfma_f32_16x16x4_f32): the vector unit without
-// packed fp32 would need ~2x the issue slots for the same flops.
+// to 8192 weight rows), bound by streaming the weights from HBM.  Each fp32
+// product x . w is formed on the f16 MFMA from two-part operands: at
+// context creation every weight row is scaled by a power of two (its
+// largest entry lands in [2^14, 2^15)) and split into f16 hi + lo parts (4
+// bytes per weight, like fp32); each 256-wide chunk of an activation row is
+// scaled and split the same way while it is staged.  Then
+//   x w = xh wh + xh wl + xl wh  (+ xl wl, about 2^-22 relative, dropped)
+// on three MFMAs, accumulated in fp32, and the scales are undone exactly.
+// The fp32 MFMA would do the same work in about five times the cycles.
 #include "fm_internal.h"
 
 #include <cmath>
@@ -18,169 +24,274 @@ namespace fm {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-struct ProjArgs {
-  const float* w0[kLayers];  // rows [0, rows0) of the stacked weight, per layer
-  const float* w1[kLayers];  // rows [rows0, rows0 + rows1), per layer (may be null when rows1 == 0)
-  const float* x;            // activations: x + layer * x_layer_stride + b * K
-  float* out;                // out[split][layer][b][rows0 + rows1]
-  long x_layer_stride;
-  int rows0, rows1, K, k_split, B;
-};
-
-// C[b][o] = sum_k x[b][k] W[o][k] on 16x16x4 fp32 MFMA tiles.  A block of
-// 4 waves owns 4 consecutive column tiles (64 outputs) x 32 batch rows over
-// one K slice, walked in kKChunk-wide chunks.  Each wave streams its own 16
-// weight rows from HBM, the weights of chunk c+1 requested before chunk c is
-// multiplied (two register buffers), so the weight stream and the MFMAs
-// overlap inside every wave.  The 32 activation rows of each chunk are
-// staged in LDS (two buffers) and shared by the 4 waves.
-//
-// MFMA operand layout (16x16x4 f32): lane l supplies A[l%16][l/16] and
-// B[l/16][l%16] and receives C[4(l/16)+r][l%16], r = 0..3.  Each lane loads
-// 4 consecutive k of one row (a float4); MFMA e of a 16-k step takes element
-// e, so the four MFMAs of a step cover the 16 k exactly once.
-constexpr int kKChunk = 256;
-constexpr int kXStride = kKChunk + 4;  // padded LDS row (floats): rows start in different banks
-constexpr int kWSteps = kKChunk / 16;  // float4 weight loads per lane per chunk
-constexpr int kStage = kProjRowsPerWave * kKChunk / 4 / 256;  // float4 activation loads per thread per chunk
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
-// Per-wave operand descriptors: reads past a descriptor's range return
-// zeros, which stands in for weight rows past the last output and batch
-// rows past B without a branch.
+// Power-of-two exponent e with m * 2^e in [2^14, 2^15) (0 for m == 0),
+// clamped so that 2^e and 2^-e stay normal floats.
+__device__ inline int split_exponent(float m) {
+  if (!(m > 0.f)) return 0;
+  int ex;
+  (void)frexpf(m, &ex);  // m = f 2^ex, f in [0.5, 1)
+  const int e = 15 - ex;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+// Packed weight layout, per layer: 16-row tiles; tile t holds K / 32
+// k-steps of 2 KB each, k-step s = the MFMA A operands of rows 16 t .. 16 t
+// + 15, k = 32 s .. 32 s + 31: 1 KB of hi parts then 1 KB of lo parts, lane
+// l = i + 16 g (row 16 t + i, k = 32 s + 8 g .. + 7) at 16 l.  A wave's
+// share of a tile is one contiguous stream.
+__device__ inline size_t packed_offset(int row, int k, int K) {  // in halves, of the hi part of 8 k
+  const int t = row >> 4, i = row & 15, s = k >> 5, g = (k >> 3) & 3;
+  return ((size_t)(t * (K >> 5) + s) * 2) * 512 + (size_t)(i + 16 * g) * 8;
+}
+
+// One block per weight row: row * 2^e split into hi/lo f16 parts, written
+// to the packed layout, and 2^-e.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const float* __restrict__ src, int K, int row0,
+                                                        _Float16* __restrict__ packed, float* __restrict__ inv) {
+  __shared__ float red[4];
+  const float* row = src + (size_t)blockIdx.x * K;
+  float m = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(row[k]));
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = split_exponent(m);
+  const float sc = ldexpf(1.f, e);
+  const int r = row0 + blockIdx.x;
+  for (int k8 = threadIdx.x * 8; k8 < K; k8 += 256 * 8) {
+    f16x8 h, l;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float v = row[k8 + q] * sc;
+      h[q] = (_Float16)v;
+      l[q] = (_Float16)(v - (float)h[q]);
+    }
+    const size_t o = packed_offset(r, k8, K);
+    *(f16x8*)(packed + o) = h;
+    *(f16x8*)(packed + o + 512) = l;
+  }
+  if (threadIdx.x == 0) inv[r] = ldexpf(1.f, -e);
+}
+
+struct ProjArgs {
+  const _Float16* w[kLayers];    // packed weights of each layer (layout above)
+  const float* winv[kLayers];    // [rows]: 2^-e of each row
+  const float* x;                // activations: x + layer * x_layer_stride + b * K
+  float* out;                    // out[split][layer][b][rows]
+  long x_layer_stride;
+  int rows, K, B;  // K slices of kSliceK (grid y = layers * K / kSliceK)
+};
+
+// C[o][b] = sum_k W[o][k] x[b][k] on 16x16x32 f16 MFMA tiles (A = weights,
+// rows = 16 outputs; B = activations, columns = 16 batch rows).  A block of
+// 4 waves owns 64 consecutive outputs x 32 batch rows over one 512-wide K
+// slice.  The slice's activations are staged once: all loads issued
+// together, each 128-wide chunk of a row scaled by its own power of two and
+// split into f16 hi/lo in LDS, one barrier.  Then each wave streams its own
+// 16 weight rows through a ring of three register buffers (the weights of
+// chunk c+2 requested before chunk c is multiplied), with no further
+// barrier.
+//
+// MFMA operand layout (16x16x32 f16): lane l supplies A[l%16][8(l/16) + e]
+// and B[8(l/16) + e][l%16], e = 0..7, and receives C[4(l/16) + r][l%16].
+// K-step s covers k = 32 s .. 32 s + 31; lane l's eight k slots are
+// 32 s + 8(l/16) + e, one 16-byte load of each part.
+constexpr int kKChunk = 128;
+constexpr int kKSteps = kKChunk / 32;                         // MFMA k-steps per chunk
+constexpr int kXsStride = kSliceK + 8;                        // padded LDS row (halves)
+constexpr int kStage = kProjRowsPerWave * kKChunk / 4 / 256;  // float4 activation loads per thread per chunk
+constexpr int kWRing = 3;                                     // weight chunks in registers (two in flight)
+constexpr int kProjLds = 2 * kProjRowsPerWave * kXsStride * 2 + kSliceChunks * kProjRowsPerWave * 4;
+
 struct ProjLane {
-  __amdgpu_buffer_rsrc_t w;  // this wave's 16 weight rows (fewer at the end)
+  __amdgpu_buffer_rsrc_t w;  // this wave's 16-row tile (empty past the last row)
   __amdgpu_buffer_rsrc_t x;  // activation rows [0, B) of the layer
-  uint32_t w_off;            // byte offset of lane's row, k = 4 g
   int K, b_base;
 };
 
-__device__ __forceinline__ void proj_load_w(const ProjLane& pl, int kc, f32x4 (&wv)[kWSteps]) {
-#pragma unroll
-  for (int u = 0; u < kWSteps; ++u)
-    wv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pl.w, pl.w_off + 4u * (kc + 16 * u), 0, 0));
-}
+struct WChunk {
+  f16x8 hi[kKSteps], lo[kKSteps];
+};
 
-// Activation rows b_base .. b_base + 32 of chunk kc, to registers.
-__device__ __forceinline__ void proj_load_x(const ProjLane& pl, int kc, f32x4 (&xr)[kStage]) {
+// K-step s of chunk kc is the 2 KB block kc / 32 + s of the wave's tile;
+// the wave-uniform block offset goes in the scalar offset.
+__device__ __forceinline__ void proj_load_w(const ProjLane& pl, int kc, WChunk& wc) {
+  const uint32_t lane_off = 16u * (threadIdx.x & 63);
 #pragma unroll
-  for (int j = 0; j < kStage; ++j) {
-    const int idx = threadIdx.x + 256 * j;
-    const uint32_t off = 4u * ((uint32_t)(pl.b_base + idx / (kKChunk / 4)) * pl.K + kc + 4 * (idx % (kKChunk / 4)));
-    xr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pl.x, off, 0, 0));
+  for (int s = 0; s < kKSteps; ++s) {
+    const int so = 2048 * ((kc >> 5) + s);
+    wc.hi[s] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(pl.w, lane_off, so, 0));
+    wc.lo[s] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(pl.w, lane_off + 1024, so, 0));
   }
 }
 
-__device__ __forceinline__ void proj_store_x(const f32x4 (&xr)[kStage], float* xs) {
+// Load j of wave v covers batch rows 8 j + 2 v (lanes 0..31) and
+// 8 j + 2 v + 1 (lanes 32..63), one float4 per lane.
+__device__ __forceinline__ int stage_row(int j) { return 8 * j + 2 * (int)(threadIdx.x >> 6) + ((threadIdx.x >> 5) & 1); }
+
+// Activation rows b_base .. b_base + 32 (zeros past B) of the slice's
+// chunk c, to registers.  The per-lane offset holds the row (so rows past B
+// read zeros), the scalar offset the slice column.
+__device__ __forceinline__ void proj_load_x(const ProjLane& pl, int k0, f32x4 (&xr)[kStage]) {
+  const int c4 = threadIdx.x & 31;
 #pragma unroll
   for (int j = 0; j < kStage; ++j) {
-    const int idx = threadIdx.x + 256 * j;
-    *(f32x4*)(xs + (idx / (kKChunk / 4)) * kXStride + 4 * (idx % (kKChunk / 4))) = xr[j];
+    const uint32_t off = 4u * ((uint32_t)(pl.b_base + stage_row(j)) * pl.K + 4 * c4);
+    xr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pl.x, off, 4 * k0, 0));
   }
 }
 
+// Chunk c of each staged row: scaled by its power of two (from its largest
+// entry, a reduction over the 32 lanes holding it), split into f16 hi/lo,
+// stored to LDS columns 128 c .. with the row's 2^-e.
+__device__ __forceinline__ void proj_store_x(const f32x4 (&xr)[kStage], int c, _Float16* xs_hi, _Float16* xs_lo,
+                                             float* xs_inv) {
+  const int c4 = threadIdx.x & 31;
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const f32x4 v = xr[j];
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int e = split_exponent(m);
+    const float sc = ldexpf(1.f, e);
+    f16x4 h, l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float y = v[q] * sc;
+      h[q] = (_Float16)y;
+      l[q] = (_Float16)(y - (float)h[q]);
+    }
+    const int row = stage_row(j);
+    *(f16x4*)(xs_hi + row * kXsStride + kKChunk * c + 4 * c4) = h;
+    *(f16x4*)(xs_lo + row * kXsStride + kKChunk * c + 4 * c4) = l;
+    if (c4 == 0) xs_inv[c * kProjRowsPerWave + row] = ldexpf(1.f, -e);
+  }
+}
+
+// Chunk c: three product terms on separate accumulators (six independent
+// MFMA chains), then the chunk's sum times the batch row's 2^-e into tot.
 template <int BT>
-__device__ __forceinline__ void proj_mfma(const f32x4 (&wv)[kWSteps], const float* xs, int i, int g,
-                                          f32x4 (&acc)[BT]) {
+__device__ __forceinline__ void proj_chunk(const WChunk& wc, int c, const _Float16* xs_hi, const _Float16* xs_lo,
+                                           const float* xs_inv, int i, int g, f32x4 (&tot)[BT]) {
+  f32x4 hh[BT], hl[BT], lh[BT];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < kWSteps; ++u) {
-    f32x4 xv[BT];
+  for (int bt = 0; bt < BT; ++bt) hh[bt] = hl[bt] = lh[bt] = zero;
 #pragma unroll
-    for (int bt = 0; bt < BT; ++bt) xv[bt] = *(const f32x4*)(xs + (16 * bt + i) * kXStride + 4 * g + 16 * u);
+  for (int s = 0; s < kKSteps; ++s) {
+    f16x8 xh[BT], xl[BT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int bt = 0; bt < BT; ++bt) {
+      const int o = (16 * bt + i) * kXsStride + kKChunk * c + 32 * s + 8 * g;
+      xh[bt] = *(const f16x8*)(xs_hi + o);
+      xl[bt] = *(const f16x8*)(xs_lo + o);
+    }
 #pragma unroll
-      for (int bt = 0; bt < BT; ++bt) acc[bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[bt][e], wv[u][e], acc[bt], 0, 0, 0);
+    for (int bt = 0; bt < BT; ++bt) hh[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc.hi[s], xh[bt], hh[bt], 0, 0, 0);
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) hl[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc.hi[s], xl[bt], hl[bt], 0, 0, 0);
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) lh[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc.lo[s], xh[bt], lh[bt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int bt = 0; bt < BT; ++bt) {
+    const float sx = xs_inv[c * kProjRowsPerWave + 16 * bt + i];  // C column = batch row 16 bt + l%16
+    tot[bt] += (hh[bt] + (hl[bt] + lh[bt])) * sx;
+    // Fold the chunk in here: left alone, the compiler sinks every chunk's
+    // update to the final store and keeps all the chunk sums alive.
+    asm volatile("" : "+v"(tot[bt]));
   }
 }
 
-// Workgroup barrier ordering LDS only: weight and activation loads of the
-// next chunk stay in flight across it (a full barrier would drain them).
+// Workgroup barrier ordering LDS only: weight loads already issued stay in
+// flight across it (a full barrier would drain them).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int CHUNKS>
-__global__ __launch_bounds__(256) void proj_kernel(ProjArgs p) {
+// grid = (outputs / 64, layers * K / 512, row groups), block = 256, dynamic
+// LDS kProjLds.
+__global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs p) {
   constexpr int BT = kProjRowsPerWave / 16;
-  __shared__ f32x4 xs4[kProjRowsPerWave * kXStride / 4];
-  float* xs = (float*)xs4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char proj_lds[];
+  _Float16* xs_hi = (_Float16*)proj_lds;
+  _Float16* xs_lo = xs_hi + kProjRowsPerWave * kXsStride;
+  float* xs_inv = (float*)(xs_lo + kProjRowsPerWave * kXsStride);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rows = p.rows0 + p.rows1;
   const int o_base = (blockIdx.x * 4 + wave) * 16;
-  const int layer = blockIdx.y / p.k_split;
-  const int split = blockIdx.y % p.k_split;
-  const int k_begin = split * (CHUNKS * kKChunk);
+  const int splits = p.K / kSliceK;
+  const int layer = blockIdx.y / splits;
+  const int split = blockIdx.y % splits;
+  const int k_begin = split * kSliceK;
   const int i = lane & 15;
-
   const int g = lane >> 4;
+
   ProjLane pl;
   {
-    // The wave's 16 rows lie in one of the two stacked weights (rows0 is a
-    // multiple of 16); past the last row the range is empty.
-    const bool second = o_base >= p.rows0;
-    const int r0 = second ? o_base - p.rows0 : o_base;
-    const int avail = (second ? p.rows1 : p.rows0) - r0;
-    const int nrows = avail < 0 ? 0 : (avail > 16 ? 16 : avail);
-    // Static indices keep the pointers in scalar registers.
-    const float* w0 = layer == 0 ? p.w0[0] : (layer == 1 ? p.w0[1] : p.w0[2]);
-    const float* w1 = layer == 0 ? p.w1[0] : (layer == 1 ? p.w1[1] : p.w1[2]);
-    const float* wbase = (second ? w1 : w0) + (size_t)r0 * p.K;  // never read when nrows is 0
-    // The values are wave-uniform; readfirstlane keeps the descriptor in
-    // scalar registers (a vector-register descriptor costs a loop per load).
-    const uint64_t wa = (uint64_t)(uintptr_t)wbase;
-    const uint64_t wu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(wa >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)wa);
-    pl.w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)wu, 0,
-                                             __builtin_amdgcn_readfirstlane(nrows * p.K * 4), kBufferWord3);
-    pl.w_off = 4u * ((uint32_t)i * p.K + 4 * g);
+    // Static indices and readfirstlane keep the descriptors in scalar
+    // registers (a vector-register descriptor costs a loop per load).
+    const _Float16* wl = layer == 0 ? p.w[0] : (layer == 1 ? p.w[1] : p.w[2]);
+    const size_t tile_halves = (size_t)16 * p.K * 2;
+    const uint64_t a = (uint64_t)(uintptr_t)(wl + (size_t)(o_base >> 4) * tile_halves);  // never read past the rows
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const int bytes = __builtin_amdgcn_readfirstlane(o_base < p.rows ? (int)(tile_halves * 2) : 0);
+    pl.w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, 0, bytes, kBufferWord3);
     pl.x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + layer * p.x_layer_stride), 0, p.B * p.K * 4, kBufferWord3);
     pl.K = p.K;
     pl.b_base = blockIdx.z * kProjRowsPerWave;
   }
-  const int o = o_base + i;
 
-  f32x4 acc[BT];
+  WChunk wbuf[kWRing];
 #pragma unroll
-  for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kWRing - 1; ++c) proj_load_w(pl, k_begin + c * kKChunk, wbuf[c]);
+  {
+    f32x4 xr[kSliceChunks][kStage];
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) proj_load_x(pl, k_begin + c * kKChunk, xr[c]);
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) proj_store_x(xr[c], c, xs_hi, xs_lo, xs_inv);
+  }
+  lds_barrier();
 
-  // Straight-line over the chunks (two static weight buffers): the weights
-  // and activations of chunk c+1 are requested before chunk c is
-  // multiplied; the activations reach LDS after the barrier that ends every
-  // wave's use of chunk c.
-  f32x4 wbuf[2][kWSteps], xr[kStage];
-  proj_load_w(pl, k_begin, wbuf[0]);
-  proj_load_x(pl, k_begin, xr);
-  proj_store_x(xr, xs);
+  f32x4 tot[BT];
 #pragma unroll
-  for (int c = 0; c < CHUNKS; ++c) {
-    if (c + 1 < CHUNKS) {
-      proj_load_w(pl, k_begin + (c + 1) * kKChunk, wbuf[(c + 1) & 1]);
-      proj_load_x(pl, k_begin + (c + 1) * kKChunk, xr);
-    }
-    lds_barrier();
-    proj_mfma<BT>(wbuf[c & 1], xs, i, g, acc);
-    if (c + 1 < CHUNKS) {
-      lds_barrier();
-      proj_store_x(xr, xs);
-    }
+  for (int bt = 0; bt < BT; ++bt) tot[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kSliceChunks; ++c) {
+    if (c + kWRing - 1 < kSliceChunks)
+      proj_load_w(pl, k_begin + (c + kWRing - 1) * kKChunk, wbuf[(c + kWRing - 1) % kWRing]);
+    proj_chunk<BT>(wbuf[c % kWRing], c, xs_hi, xs_lo, xs_inv, i, g, tot);
+    __builtin_amdgcn_sched_barrier(0);  // keep each chunk's loads with it (registers)
   }
 
-  // C rows are batch rows, C columns outputs: lane l holds b = 4(l/16)+r, o = l%16.
-  if (o < rows) {
+  // C rows are outputs, C columns batch rows: lane l holds o = o_base +
+  // 4(l/16) + r, r = 0..3, for batch row 16 bt + l%16.  Undo the weight
+  // rows' scales and store the four consecutive outputs.
+  const int o = o_base + 4 * g;
+  if (o < p.rows) {
+    const float* inv = layer == 0 ? p.winv[0] : (layer == 1 ? p.winv[1] : p.winv[2]);
+    const f32x4 sw = *(const f32x4*)(inv + o);
 #pragma unroll
-    for (int bt = 0; bt < BT; ++bt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int b = pl.b_base + 16 * bt + 4 * g + r;
-        if (b < p.B) p.out[(((size_t)split * kLayers + layer) * p.B + b) * rows + o] = acc[bt][r];
-      }
+    for (int bt = 0; bt < BT; ++bt) {
+      const int b = pl.b_base + 16 * bt + i;
+      if (b < p.B) *(f32x4*)(p.out + (((size_t)split * kLayers + layer) * p.B + b) * p.rows + o) = tot[bt] * sw;
+    }
   }
+}
+
+void launch_proj(const ProjArgs& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL(proj_kernel, grid, dim3(256), kProjLds, stream, p);
 }
 
 __device__ inline float wave_sum(float v) {
@@ -310,37 +421,29 @@ __global__ __launch_bounds__(256) void rope_hadamard_kernel(const float* q_lin, 
   *(float2*)(q_out + off) = make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
 }
 
-// K slice = 4, 8 or 16 chunks of 256 (the split counts keep it there).
-void launch_proj(const ProjArgs& p, dim3 grid, hipStream_t stream) {
-  const int chunks = p.K / p.k_split / kKChunk;
-  auto kern = chunks == 4 ? proj_kernel<4> : (chunks == 8 ? proj_kernel<8> : proj_kernel<16>);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, p);
-}
-
 }  // namespace
 
 hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, const Workspace& ws, int max_batch,
                                 const float* hidden, const int64_t* positions, int B, float* q_out, float* w_out,
                                 hipStream_t stream) {
   (void)max_batch;
+  (void)wts;  // packed into the workspace by fm_create
   const int row_groups = proj_row_groups(B);
-  const int s1 = proj1_splits(B);
-  const int s2 = proj2_splits(B);
+  const int s1 = kHidden / kSliceK;
+  const int s2 = kQLora / kSliceK;
 
-  // wq_a | weights_proj, split over K.
+  // wq_a | weights_proj (packed together), split over K.
   {
     ProjArgs p{};
     for (int l = 0; l < kLayers; ++l) {
-      p.w0[l] = wts.wq_a[l];
-      p.w1[l] = wts.w_proj[l];
+      p.w[l] = ws.w1 + (size_t)l * kProj1Out * kHidden * 2;
+      p.winv[l] = ws.w1_inv + (size_t)l * kProj1Out;
     }
     p.x = hidden;
     p.x_layer_stride = 0;
     p.out = ws.proj1_part;
-    p.rows0 = kQLora;
-    p.rows1 = kHeads;
+    p.rows = kProj1Out;
     p.K = kHidden;
-    p.k_split = s1;
     p.B = B;
     const int col_tiles = (kProj1Out + 15) / 16;
     dim3 grid((col_tiles + 3) / 4, kLayers * s1, row_groups);
@@ -349,9 +452,9 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
   // RMSNorm + weight-branch finish + RoPE angles.
   {
     GainPtrs gp{};
-    for (int l = 0; l < kLayers; ++l) gp.g[l] = wts.q_norm[l];
+    for (int l = 0; l < kLayers; ++l) gp.g[l] = ws.q_norm + (size_t)l * kQLora;
     const float w_scale = (float)(1.0 / std::sqrt((double)cfg.head_dim * (double)cfg.n_heads));
-    auto kern = s1 == 4 ? rmsnorm_kernel<4> : (s1 == 2 ? rmsnorm_kernel<2> : rmsnorm_kernel<1>);
+    auto kern = rmsnorm_kernel<kHidden / kSliceK>;
     hipLaunchKernelGGL(kern, dim3(kLayers * B), dim3(256), 0, stream, ws.proj1_part, gp, B, cfg.rms_eps, w_scale,
                        positions, ws.rope_freq, ws.rope_cs, ws.a_hat, w_out);
   }
@@ -359,16 +462,14 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
   {
     ProjArgs p{};
     for (int l = 0; l < kLayers; ++l) {
-      p.w0[l] = wts.wq_b[l];
-      p.w1[l] = nullptr;
+      p.w[l] = ws.w2 + (size_t)l * kHeads * kHeadDim * kQLora * 2;
+      p.winv[l] = ws.w2_inv + (size_t)l * kHeads * kHeadDim;
     }
     p.x = ws.a_hat;
     p.x_layer_stride = (long)B * kQLora;
     p.out = ws.q_lin;
-    p.rows0 = kHeads * kHeadDim;
-    p.rows1 = 0;
+    p.rows = kHeads * kHeadDim;
     p.K = kQLora;
-    p.k_split = s2;
     p.B = B;
     const int col_tiles = kHeads * kHeadDim / 16;
     dim3 grid((col_tiles + 3) / 4, kLayers * s2, row_groups);
@@ -377,6 +478,25 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
   // Split-K sum, RoPE (YaRN) + normalized Hadamard.
   hipLaunchKernelGGL(rope_hadamard_kernel, dim3(kLayers * B * kHeads / 4), dim3(256), 0, stream, ws.q_lin, s2,
                      ws.rope_cs, B, q_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const fm_weights& wts, const Workspace& ws, hipStream_t stream) {
+  // The projection kernel stages a 512-wide slice of 32 activation rows
+  // (about 66 KB of LDS, above the default dynamic limit).
+  hipError_t a = hipFuncSetAttribute((const void*)proj_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
+  if (a != hipSuccess) return a;
+  for (int l = 0; l < kLayers; ++l) {
+    _Float16* w1 = ws.w1 + (size_t)l * kProj1Out * kHidden * 2;
+    float* i1 = ws.w1_inv + (size_t)l * kProj1Out;
+    hipLaunchKernelGGL(pack_rows_kernel, dim3(kQLora), dim3(256), 0, stream, wts.wq_a[l], kHidden, 0, w1, i1);
+    hipLaunchKernelGGL(pack_rows_kernel, dim3(kHeads), dim3(256), 0, stream, wts.w_proj[l], kHidden, kQLora, w1, i1);
+    hipLaunchKernelGGL(pack_rows_kernel, dim3(kHeads * kHeadDim), dim3(256), 0, stream, wts.wq_b[l], kQLora, 0,
+                       ws.w2 + (size_t)l * kHeads * kHeadDim * kQLora * 2, ws.w2_inv + (size_t)l * kHeads * kHeadDim);
+    hipError_t e = hipMemcpyAsync(ws.q_norm + (size_t)l * kQLora, wts.q_norm[l], sizeof(float) * kQLora,
+                                  hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
