@@ -5,7 +5,7 @@
 // Top-K is an exact per-row selection on order-preserving 32-bit keys of the
 // fp32 scores; ties at the K-th key go to the lowest chunk indices, which
 // makes the mask unique.  Three kernels per call:
-//   1. sample: one block per row reads 8192 keys (64 runs of 128 chunks
+//   1. sample: one block per row reads 4096 keys (64 runs of 64 chunks
 //      spread over the row; the whole row when it is shorter) and picks a
 //      cut-off L, the m-th largest sampled key, with m chosen so that about
 //      K plus four standard deviations of the row's keys are expected at or
@@ -15,8 +15,9 @@
 //      pairs of keys >= L to the row's candidate list, one region per block;
 //   3. final: one block per row selects exactly among the candidates: radix
 //      passes over the key give the K-th largest key T and how many keys equal
-//      to T are kept, radix passes over the index of the keys equal to T give
-//      the last index kept; those candidates' mask bytes are set.  When fewer
+//      to T are kept, radix passes over the index of the keys equal to T (only
+//      when some are left out) give the last index kept; those candidates'
+//      mask bytes are set.  When fewer
 //      than K keys reached L (the sample was unrepresentative), the same
 //      passes run over the whole row instead, so the result is always exact.
 #include "fm_internal.h"
@@ -40,40 +41,77 @@ __device__ inline int64_t row_valid(const int32_t* valid_n, int b, int64_t N) {
 enum : uint32_t { kSelect = 0, kKeepAll = 1, kKeepNone = 2 };
 
 constexpr int kSampleRuns = 64;
-constexpr int kSampleRun = 128;
-constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 8192
-constexpr int kSampleThreads = 1024;
-constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 8
+constexpr int kSampleRun = 64;
+constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 4096
+constexpr int kSampleThreads = 256;
+constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 16
+
+// Wave64 inclusive prefix sum and max/min reductions on DPP lane moves
+// (gfx9 family): row shifts by 1, 2, 4, 8 within each row of 16 lanes, then
+// lane 15 of a row broadcast to the next row and lane 31 to the upper half.
+// A lane with no source lane adds the identity (`old`).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t identity, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  return wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// Reductions: the inclusive scan's last lane, read by every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_scan(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; }),
+                                   63);
+}
 
 // Block-wide: the digit (bin) holding the k-th element (1-based) of a
-// histogram, counting from the top bin down (largest) or from bin 0 up, and
-// the number of elements in the bins before it in that order.  Thread t owns
-// bins [t per, t per + per); prefix sums by wave shuffles plus one step
-// across the waves through LDS.
+// kSelBins-bin histogram, counting from the top bin down (largest) or from
+// bin 0 up, the number of elements in the bins before it in that order, and
+// the bin's own count (s_out[0..2]).  Thread t owns the PER consecutive bins
+// from t PER (read as 16-byte vectors); prefix sums by a wave scan plus one
+// step across the waves through LDS.  Ends with a barrier, after which every
+// thread sees s_out.
 template <int THREADS>
-__device__ void block_find(const uint32_t* h, int nbins, uint32_t k, uint32_t* s_wtot, uint32_t* s_out,
-                           bool largest) {
+__device__ void block_find(const uint32_t* h, uint32_t k, uint32_t* s_wtot, uint32_t* s_out, bool largest) {
+  constexpr int PER = kSelBins / THREADS;
+  static_assert(PER == 2 || PER % 4 == 0, "bins per thread");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int per = (nbins + THREADS - 1) / THREADS;
-  const int owners = nbins / per;
-  uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  uint32_t tot = 0;
-  if (t < owners)
-    for (int j = 0; j < per; ++j) {
-      cnt[j] = h[t * per + j];
-      tot += cnt[j];
-    }
-  uint32_t incl = tot;
+  uint32_t cnt[PER];
+  if constexpr (PER == 2) {
+    const uint2 v = *(const uint2*)(h + 2 * t);
+    cnt[0] = v.x;
+    cnt[1] = v.y;
+  } else {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
+    for (int q = 0; q < PER / 4; ++q) {
+      const uint4 v = *(const uint4*)(h + PER * t + 4 * q);
+      cnt[4 * q] = v.x;
+      cnt[4 * q + 1] = v.y;
+      cnt[4 * q + 2] = v.z;
+      cnt[4 * q + 3] = v.w;
+    }
   }
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) tot += cnt[j];
+  const uint32_t incl = wave_prefix_sum(tot);
   if (lane == 63) s_wtot[wave] = incl;
   __syncthreads();
   uint32_t below = 0, all = 0;
+#pragma unroll
   for (int w = 0; w < THREADS / 64; ++w) {
     const uint32_t v = s_wtot[w];
     below += w < wave ? v : 0u;
@@ -81,14 +119,18 @@ __device__ void block_find(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
   }
   const uint32_t prefix_incl = below + incl;
   const uint32_t before = largest ? all - prefix_incl : prefix_incl - tot;
-  if (t < owners && before < k && k <= before + tot) {
+  if (before < k && k <= before + tot) {
+    // This thread's bins hold the k-th element: walk them in order.
     uint32_t acc = before;
-    for (int jj = 0; jj < per; ++jj) {
-      const int j = largest ? per - 1 - jj : jj;
-      if (acc + cnt[j] >= k) {
-        s_out[0] = (uint32_t)(t * per + j);
+    bool found = false;
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int j = largest ? PER - 1 - jj : jj;
+      if (!found && acc + cnt[j] >= k) {
+        s_out[0] = (uint32_t)(t * PER + j);
         s_out[1] = acc;
-        break;
+        s_out[2] = cnt[j];
+        found = true;
       }
       acc += cnt[j];
     }
@@ -96,50 +138,121 @@ __device__ void block_find(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
   __syncthreads();
 }
 
+// Zeroes a kSelBins histogram with 16-byte stores.
+template <int THREADS>
+__device__ __forceinline__ void clear_bins(uint32_t* h) {
+#pragma unroll
+  for (int i = 4 * (int)threadIdx.x; i < kSelBins; i += 4 * THREADS) *(uint4*)(h + i) = make_uint4(0, 0, 0, 0);
+}
+
 // Radix selection over a stream of (key, index) pairs produced by `each`
 // (called once per pass with a functor taking a pair): the k-th largest key
 // T (1-based k <= stream size) and the largest index kept among the keys
-// equal to T when ties go to the lowest indices.  Digit passes: key bits
-// 31..21, 20..10, 9..0, then the same over the index of keys equal to T.
+// equal to T when ties go to the lowest indices (0xffffffff when every key
+// equal to T is kept).
+//
+// A first pass finds the smallest and largest key: their common high bits
+// are every key's, so the digit passes (at most 11 bits each) start below
+// them.  Concentrated keys (scores in a narrow range) would otherwise fall
+// into a few bins of the first pass and serialise its LDS atomics.  The
+// index passes cover the low idx_bits bits and run only when some key equal
+// to T is left out.
+//
+// Without WITH_INDEX (a cut-off, not a selection) at most two digit passes
+// run and T is the lowest key of the bin reached: a lower bound of the k-th
+// largest key, so at least k keys are >= T.
 template <int THREADS, bool WITH_INDEX = true, typename Each>
-__device__ void radix_select(Each each, uint32_t k, uint32_t* h, uint32_t* s_wtot, uint32_t* s_out, uint32_t* T_out,
-                             uint32_t* last_out) {
-  uint32_t prefix = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    const int hi = pass == 0 ? 32 : (pass == 1 ? 21 : 10);
-    for (int i = threadIdx.x; i < kSelBins; i += THREADS) h[i] = 0;
-    __syncthreads();
-    each([&](uint2 e) {
-      if (hi == 32 || (e.x >> hi) == prefix) atomicAdd(&h[(e.x >> shift) & (nb - 1)], 1u);
-    });
-    __syncthreads();
-    block_find<THREADS>(h, nb, k, s_wtot, s_out, true);
-    prefix = (prefix << (pass == 2 ? 10 : 11)) | s_out[0];
-    k -= s_out[1];
-    __syncthreads();
+__device__ void radix_select(Each each, uint32_t k, int idx_bits, uint32_t* h, uint32_t* s_wtot, uint32_t* s_out,
+                             uint32_t* T_out, uint32_t* last_out) {
+  __shared__ uint32_t s_mm[3 * (THREADS / 64)];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t kmin = 0xffffffffu, kmax = 0u, cnt = 0u;
+  each([&](uint2 e) {
+    kmin = e.x < kmin ? e.x : kmin;
+    kmax = e.x > kmax ? e.x : kmax;
+    ++cnt;
+  });
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  cnt = wave_sum_u32(cnt);
+  if (lane == 0) {
+    s_mm[3 * wave] = kmin;
+    s_mm[3 * wave + 1] = kmax;
+    s_mm[3 * wave + 2] = cnt;
   }
-  const uint32_t T = prefix;  // k = keys equal to T still to keep (>= 1)
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+  cnt = 0u;
+  for (int w = 0; w < THREADS / 64; ++w) {
+    kmin = s_mm[3 * w] < kmin ? s_mm[3 * w] : kmin;
+    kmax = s_mm[3 * w + 1] > kmax ? s_mm[3 * w + 1] : kmax;
+    cnt += s_mm[3 * w + 2];
+  }
+  // lo = number of low key bits still open; prefix = the bits above them.
+  // Two histogram buffers: a pass counts into one while the other is
+  // cleared for the next pass.
+  int lo = kmin == kmax ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  uint64_t prefix = (uint64_t)kmax >> lo;
+  uint32_t n_eq = cnt;  // keys equal to the prefix so far
+  int buf = 0;
+  int passes = 0;
+  clear_bins<THREADS>(h);
+  __syncthreads();
+  while (lo > 0 && (WITH_INDEX || passes < 2)) {
+    ++passes;
+    const int w = lo >= 11 ? 11 : lo;
+    const int shift = lo - w;
+    const int nb = 1 << w;
+    uint32_t* hb = h + buf * kSelBins;
+    each([&](uint2 e) {
+      if (((uint64_t)e.x >> lo) == prefix) atomicAdd(&hb[(e.x >> shift) & (nb - 1)], 1u);
+    });
+    clear_bins<THREADS>(h + (buf ^ 1) * kSelBins);
+    __syncthreads();
+    block_find<THREADS>(hb, k, s_wtot, s_out, true);
+    prefix = (prefix << w) | s_out[0];
+    k -= s_out[1];
+    n_eq = s_out[2];
+    lo = shift;
+    buf ^= 1;
+  }
+  if (!WITH_INDEX) {
+    *T_out = (uint32_t)(prefix << lo);  // lowest key of the bin reached
+    return;
+  }
+  const uint32_t T = (uint32_t)prefix;  // k = keys equal to T still to keep (>= 1)
   *T_out = T;
-  if (!WITH_INDEX) return;
-  uint32_t iprefix = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    const int hi = pass == 0 ? 32 : (pass == 1 ? 21 : 10);
-    for (int i = threadIdx.x; i < kSelBins; i += THREADS) h[i] = 0;
-    __syncthreads();
-    each([&](uint2 e) {
-      if (e.x == T && (hi == 32 || (e.y >> hi) == iprefix)) atomicAdd(&h[(e.y >> shift) & (nb - 1)], 1u);
-    });
-    __syncthreads();
-    block_find<THREADS>(h, nb, k, s_wtot, s_out, false);
-    iprefix = (iprefix << (pass == 2 ? 10 : 11)) | s_out[0];
-    k -= s_out[1];
-    __syncthreads();
+  if (n_eq == k) {  // every key equal to T is kept
+    *last_out = 0xffffffffu;
+    return;
   }
-  *last_out = iprefix;
+  uint64_t iprefix = 0;
+  lo = idx_bits;
+  while (lo > 0) {
+    const int w = lo >= 11 ? 11 : lo;
+    const int shift = lo - w;
+    const int nb = 1 << w;
+    uint32_t* hb = h + buf * kSelBins;
+    each([&](uint2 e) {
+      if (e.x == T && ((uint64_t)e.y >> lo) == iprefix) atomicAdd(&hb[(e.y >> shift) & (nb - 1)], 1u);
+    });
+    clear_bins<THREADS>(h + (buf ^ 1) * kSelBins);
+    __syncthreads();
+    block_find<THREADS>(hb, k, s_wtot, s_out, false);
+    iprefix = (iprefix << w) | s_out[0];
+    k -= s_out[1];
+    lo = shift;
+    buf ^= 1;
+  }
+  *last_out = (uint32_t)iprefix;
+}
+
+// Bits needed for chunk indices below n (at least 1).
+__device__ inline int index_bits(int64_t n) {
+  const uint32_t m = n > 1 ? (uint32_t)(n - 1) : 1u;
+  return 32 - __builtin_clz(m);
 }
 
 // 1. Cut-off per row from a sample.  grid = B, block = kSampleThreads.
@@ -158,34 +271,30 @@ __global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float*
     }
     return;
   }
-  __shared__ uint32_t s_keys[kSampleSize];
-  __shared__ uint32_t h[kSelBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
   __shared__ uint32_t s_wtot[kSampleThreads / 64];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[3];
   const float* row = scores + (size_t)b * N;
   const bool whole = vn <= kSampleSize;
   const uint32_t S = whole ? (uint32_t)vn : (uint32_t)kSampleSize;
   // Sample i = t + kSampleThreads * j sits in run r = i / kSampleRun at
-  // offset t % kSampleRun; run r starts at r (vn - kSampleRun) / 63.  All
-  // loads are issued before the first LDS store.
+  // offset t % kSampleRun; run r starts at r (vn - kSampleRun) / 63 (32-bit:
+  // 63 * 2^26 fits).  Loads go through a descriptor over the row's valid
+  // scores with no branch, all issued before the first use.
   const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, (int)(vn * 4), 0x00020000);
+  const uint32_t span = whole ? 0u : (uint32_t)(vn - kSampleRun);
   float v[kSamplePerThread];
 #pragma unroll
   for (int j = 0; j < kSamplePerThread; ++j) {
     const uint32_t i = (uint32_t)t + kSampleThreads * j;
-    int64_t n = i;
-    if (!whole) {
-      const int64_t r = (int64_t)(i / kSampleRun);
-      n = r * (vn - kSampleRun) / (kSampleRuns - 1) + (i % kSampleRun);
-    }
-    v[j] = i < S ? row[n] : 0.0f;
+    const uint32_t r = i / kSampleRun;
+    const uint32_t n = whole ? i : r * span / (kSampleRuns - 1) + (i % kSampleRun);
+    v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, 4u * n, 0, 0));
   }
+  uint32_t kr[kSamplePerThread];
 #pragma unroll
-  for (int j = 0; j < kSamplePerThread; ++j) {
-    const uint32_t i = (uint32_t)t + kSampleThreads * j;
-    if (i < S) s_keys[i] = order_key(v[j]);
-  }
-  __syncthreads();
+  for (int j = 0; j < kSamplePerThread; ++j) kr[j] = order_key(v[j]);
   uint32_t m;
   if (whole) {
     m = (uint32_t)top_k;  // the sample is the row: its K-th key exactly
@@ -197,9 +306,13 @@ __global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float*
   uint32_t L, unused;
   radix_select<kSampleThreads, false>(
       [&](auto f) {
-        for (uint32_t i = threadIdx.x; i < S; i += kSampleThreads) f(make_uint2(s_keys[i], i));
+#pragma unroll
+        for (int j = 0; j < kSamplePerThread; ++j) {
+          const uint32_t i = (uint32_t)t + kSampleThreads * j;
+          if (i < S) f(make_uint2(kr[j], i));
+        }
       },
-      m, h, s_wtot, s_out, &L, &unused);
+      m, 0, h, s_wtot, s_out, &L, &unused);
   if (threadIdx.x == 0) {
     state[4 * b + 0] = L;
     state[4 * b + 2] = mode;
@@ -259,14 +372,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const float* s
   // Candidates at each thread's prefix within the block.
   __shared__ uint32_t s_wave[kSelThreads / 64];
   const uint32_t mine = __popc(is_cand);
-  uint32_t incl = mine;
+  const uint32_t incl = wave_prefix_sum(mine);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
   if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -285,7 +393,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const float* s
 
 // 3. Exact selection among the candidates (or the whole row).  grid = B.
 constexpr int kFinThreads = 1024;
-constexpr int kFinLds = 8192;  // candidates staged in LDS; more are read from their regions each pass
+constexpr int kFinLds = 8192;  // candidates held in registers (8 per thread); more are read from their regions each pass
 
 __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* scores, int64_t N,
                                                                 const int32_t* valid_n, int blocks_per_row,
@@ -299,11 +407,10 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
   const uint2* crow = cand + (size_t)b * N;
   const uint32_t* counts = cand_count + (size_t)b * blocks_per_row;
   uint8_t* mrow = mask + (size_t)b * N;
-  __shared__ uint32_t h[kSelBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
   __shared__ uint32_t s_wtot[kFinThreads / 64];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[3];
   __shared__ uint32_t s_off[kFinThreads];
-  __shared__ uint2 s_cand[kFinLds];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -314,12 +421,7 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
   if (small_rows) {
     const int r = threadIdx.x;
     const uint32_t v = r < blocks_per_row ? counts[r] : 0u;
-    uint32_t incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t u = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += u;
-    }
+    const uint32_t incl = wave_prefix_sum(v);
     if (lane == 63) s_wtot[wave] = incl;
     __syncthreads();
     uint32_t below = 0;
@@ -331,8 +433,7 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
   } else {
     uint32_t part = 0;
     for (int r = threadIdx.x; r < blocks_per_row; r += kFinThreads) part += counts[r];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    part = wave_sum_u32(part);
     if (lane == 0) s_wtot[wave] = part;
     __syncthreads();
     for (int w = 0; w < kFinThreads / 64; ++w) C += s_wtot[w];
@@ -340,19 +441,34 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
   __syncthreads();
 
   const uint32_t k = (uint32_t)top_k;
+  const int ib = index_bits(vn);
   uint32_t T, last;
   if (C >= k && small_rows && C <= (uint32_t)kFinLds) {
-    // Stage the candidates; every pass then runs on LDS.
-    for (int r = wave; r < blocks_per_row; r += kFinThreads / 64) {
-      const uint32_t off = s_off[r];
-      const uint32_t n_r = counts[r];
-      for (uint32_t i = lane; i < n_r; i += 64) s_cand[off + i] = crow[(size_t)r * kSelSlice + i];
+    // The candidates stay in registers for every pass.  Candidate c lies in
+    // the slice r with s_off[r] <= c < s_off[r + 1] (binary search); all of a
+    // thread's loads are issued together.
+    constexpr int kPer = kFinLds / kFinThreads;
+    uint2 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t c = threadIdx.x + kFinThreads * j;
+      v[j] = make_uint2(0u, 0u);
+      if (c < C) {
+        int lo = 0, hi = blocks_per_row - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_off[mid] <= c) lo = mid;
+          else hi = mid - 1;
+        }
+        v[j] = crow[(size_t)lo * kSelSlice + (c - s_off[lo])];
+      }
     }
-    __syncthreads();
     auto each = [&](auto f) {
-      for (uint32_t c = threadIdx.x; c < C; c += kFinThreads) f(s_cand[c]);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (threadIdx.x + kFinThreads * j < C) f(v[j]);
     };
-    radix_select<kFinThreads>(each, k, h, s_wtot, s_out, &T, &last);
+    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
     each([&](uint2 e) {
       if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
     });
@@ -364,7 +480,7 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
         for (uint32_t i = lane; i < n_r; i += 64) f(crow[(size_t)r * kSelSlice + i]);
       }
     };
-    radix_select<kFinThreads>(each, k, h, s_wtot, s_out, &T, &last);
+    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
     each([&](uint2 e) {
       if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
     });
@@ -373,7 +489,7 @@ __global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* sco
     auto each = [&](auto f) {
       for (int64_t n = threadIdx.x; n < vn; n += kFinThreads) f(make_uint2(order_key(row[n]), (uint32_t)n));
     };
-    radix_select<kFinThreads>(each, k, h, s_wtot, s_out, &T, &last);
+    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
     each([&](uint2 e) {
       if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
     });

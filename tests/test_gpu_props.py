@@ -211,20 +211,20 @@ def test_threshold_strict_exact(retr, tau):
 
 
 def test_topk_sample_miss_falls_back_to_whole_row(retr):
-    """The top-K cut-off comes from 64 sampled runs of 128 chunks; here the
-    sampled chunks hold the largest scores and the rest are low, so fewer than
-    K chunks reach the cut-off and the selection must fall back to the whole
-    row.  The result is still the exact top-K."""
-    n, k = 65536, 512
+    """The top-K cut-off comes from 64 sampled runs of 64 chunks spread over
+    the row; here the sampled chunks hold the largest scores and the rest are
+    low, so fewer than K chunks reach the cut-off and the selection must fall
+    back to the whole row.  The result is still the exact top-K."""
+    n, k, run = 65536, 512, 64
     s = np.full((2, n), 0.1, np.float32)
     rng = np.random.default_rng(21)
     s[:, :] = rng.uniform(0.05, 0.2, (2, n)).astype(np.float32)
-    starts = [r * (n - 128) // 63 for r in range(64)]
-    vals = np.linspace(0.9, 0.99, 64 * 128).astype(np.float32)
+    starts = [r * (n - run) // 63 for r in range(64)]
+    vals = np.linspace(0.9, 0.99, 64 * run).astype(np.float32)
     i = 0
     for st in starts:
-        s[0, st:st + 128] = vals[i:i + 128]
-        i += 128
+        s[0, st:st + run] = vals[i:i + run]
+        i += run
     s[1] = s[0][::-1]                       # second row: a different layout, same values
     m = host(retr.keep_topk(dev(s), k))
     for b in range(2):
