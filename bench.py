@@ -110,6 +110,52 @@ def cpu_baseline(budget_s: float):
             "_cpu_model": _cpu_model()}
 
 
+def resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, steps):
+    """fm_resident_delta on this step's top-K mask against the previous
+    cycle's: HIP-event time per call on the launch stream, algorithmic HBM
+    bytes (both masks read, the three index lists and counts written), and
+    the oracle on the same masks."""
+    import numpy as np
+    import torch
+
+    import oracle
+    qp = torch.empty_like(q)
+    wp = torch.empty_like(w)
+    sp = torch.empty((B, N), device="cuda")
+    prev = torch.empty_like(mask)
+    L.fm_prepare_query(r.ctx, hidden, pos - 256, B, qp, wp, sh)
+    L.fm_score(r.ctx, qp, wp, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, sp, None, sh)
+    L.fm_select_topk(r.ctx, sp, B, N, None, TOP_K, prev, sh)
+    cap = TOP_K
+    lists = [torch.empty((B, cap), dtype=torch.int32, device="cuda") for _ in range(3)]
+    counts = [torch.empty((B,), dtype=torch.int32, device="cuda") for _ in range(3)]
+
+    def call():
+        L.fm_resident_delta(r.ctx, prev, mask, B, N, cap, lists[0], counts[0], lists[1], counts[1], lists[2],
+                            counts[2], sh)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    n = [c.cpu().numpy().astype(np.int64) for c in counts]
+    nbytes = 2 * B * N + 4 * int(n[0].sum() + n[1].sum() + n[2].sum()) + 3 * 4 * B
+    pm, cm = prev.cpu().numpy(), mask.cpu().numpy()
+    t0 = time.perf_counter()
+    for b in range(B):
+        oracle.resident_delta(cm[b], pm[b])
+    t_cpu = time.perf_counter() - t0
+    return {"us": t * 1e6, "hbm_gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
+            "bytes": nbytes, "resident_per_row": float(n[0].mean()), "entering_per_row": float(n[1].mean()),
+            "leaving_per_row": float(n[2].mean()), "oracle_us": t_cpu * 1e6}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -191,6 +237,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Next row of the path: the resident set and recall delta of this cycle's
+    # mask against the previous cycle's (the same pass for the decode token
+    # 64 steps earlier: positions - 256 at 4 tokens per chunk).
+    resident = resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps)
+
     prep = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
     score = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
     sel = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
@@ -235,6 +286,7 @@ def main(argv=None):
                          "score_p10": float(np.percentile(score, 10) * 1e6),
                          "score_p90": float(np.percentile(score, 90) * 1e6)},
         "score_only_chunks_per_s": chunks / t_score,
+        "next_rows": {"resident_delta": resident},
         "host_cpu": cpu_model,
     }
     print(json.dumps(out))

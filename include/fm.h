@@ -161,6 +161,27 @@ fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N,
 fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                               float threshold, uint8_t* mask, void* stream);
 
+/* Resident set and recall delta of a retrieval cycle (model card "How it
+ * works": the Memory Indexer's selection is the resident_set recalled from
+ * CPU to GPU every 64 decode steps; README "Inference flow": a cycle's keep
+ * mask holds for the next 64 steps).  Per row, in ascending chunk index:
+ *   resident = chunks set in mask
+ *   entering = chunks set in mask and not in prev_mask   (to recall)
+ *   leaving  = chunks set in prev_mask and not in mask   (to evict)
+ * A mask byte is set when it is non-zero.
+ *   prev_mask   device uint8 [B][N], the previous cycle's mask, or NULL
+ *               (first cycle: entering = resident, leaving empty)
+ *   mask        device uint8 [B][N], this cycle's mask
+ *   cap         capacity of each list per row (>= 0)
+ *   resident    device int32 [B][cap]; n_resident device int32 [B]
+ *   entering    device int32 [B][cap] or NULL; n_entering [B] (NULL with it)
+ *   leaving     device int32 [B][cap] or NULL; n_leaving [B] (NULL with it)
+ * The counts are the sets' full sizes; a list longer than cap holds its
+ * first cap indices.  B in [0, max_batch], N in [0, max_n]. */
+fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t* mask, int32_t B, int64_t N,
+                            int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
+                            int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, void* stream);
+
 /* Message of the last failing call on this thread ("" if none); valid until
  * the next fm_* call on this thread. */
 const char* fm_last_error(void);

@@ -313,6 +313,23 @@ def select_threshold(scores: np.ndarray, valid_n: int, threshold: float) -> np.n
     return mask
 
 
+def resident_delta(mask: np.ndarray, prev_mask: np.ndarray | None = None):
+    """Resident set and recall delta of one row's retrieval cycle.
+
+    Model card "How it works": every 64 decode steps the Memory Indexer's
+    selection becomes the resident_set, the chunks recalled from CPU to GPU;
+    README "Inference flow": a cycle's keep mask holds for the next 64 steps.
+    Returns ascending int64 index arrays (resident, entering, leaving):
+    chunks kept now, kept now but not in the previous cycle (to recall), and
+    kept in the previous cycle but not now (to evict).  A mask entry counts
+    as kept when it is non-zero; with no previous mask every kept chunk is
+    entering and none is leaving.
+    """
+    cur = np.asarray(mask) != 0
+    prev = np.zeros_like(cur) if prev_mask is None else (np.asarray(prev_mask) != 0)
+    return np.flatnonzero(cur), np.flatnonzero(cur & ~prev), np.flatnonzero(prev & ~cur)
+
+
 def score_row(comp_k_row: np.ndarray, q_row: np.ndarray, w_row: np.ndarray, valid_n: int | None = None,
               mode: str = "max", head_dim: int = 128):
     """Scores of one request row from prepared queries.

@@ -27,7 +27,7 @@ STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUN
 
 # Exported symbols, in header order.
 EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_select_topk",
-           "fm_select_threshold", "fm_last_error")
+           "fm_select_threshold", "fm_resident_delta", "fm_last_error")
 
 
 class FmConfig(ctypes.Structure):
@@ -81,6 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.fm_select_topk.restype = ctypes.c_int
     lib.fm_select_threshold.argtypes = [vp, vp, i32, i64, vp, ctypes.c_float, vp, vp]
     lib.fm_select_threshold.restype = ctypes.c_int
+    lib.fm_resident_delta.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fm_resident_delta.restype = ctypes.c_int
     lib.fm_last_error.argtypes = []
     lib.fm_last_error.restype = ctypes.c_char_p
     return lib
@@ -144,3 +146,11 @@ def fm_select_threshold(ctx, scores, B, N, valid_n, threshold, mask, stream=None
     s = current_stream() if stream is None else stream
     check(LIB.fm_select_threshold(ctx, ptr(scores), B, N, ptr(valid_n), threshold, ptr(mask), s),
           "fm_select_threshold")
+
+
+def fm_resident_delta(ctx, prev_mask, mask, B, N, cap, resident, n_resident, entering=None, n_entering=None,
+                      leaving=None, n_leaving=None, stream=None) -> None:
+    s = current_stream() if stream is None else stream
+    check(LIB.fm_resident_delta(ctx, ptr(prev_mask), ptr(mask), B, N, cap, ptr(resident), ptr(n_resident),
+                                ptr(entering), ptr(n_entering), ptr(leaving), ptr(n_leaving), s),
+          "fm_resident_delta")

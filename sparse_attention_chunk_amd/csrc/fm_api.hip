@@ -149,7 +149,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
   enum {
     kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kRowTiles, kWaveRow, kSelState,
-    kSelCand, kSelCount, kNumBuffers
+    kSelCand, kSelCount, kResCount, kNumBuffers
   };
   size_t sizes[kNumBuffers];
   sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
@@ -168,6 +168,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kSelState] = sizeof(uint32_t) * mb * 4;
   sizes[kSelCand] = 2 * sizeof(uint32_t) * mb * (size_t)max_n;  // (key, index) pairs
   sizes[kSelCount] = sizeof(uint32_t) * mb * sel_blocks;
+  sizes[kResCount] = 3 * sizeof(uint32_t) * mb * (size_t)((max_n + kResSlice - 1) / kResSlice);
   size_t offs[kNumBuffers];
   size_t total = 0;
   for (int i = 0; i < kNumBuffers; ++i) {
@@ -204,6 +205,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.sel_state = (uint32_t*)(p + offs[kSelState]);
   ctx->ws.sel_cand = (void*)(p + offs[kSelCand]);
   ctx->ws.sel_count = (uint32_t*)(p + offs[kSelCount]);
+  ctx->ws.res_count = (uint32_t*)(p + offs[kResCount]);
 
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
@@ -288,6 +290,27 @@ fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64
     return fail(FM_EINVAL, "scores and valid_n must be 4-byte aligned");
   hipError_t e = fm::launch_select_threshold(scores, B, N, valid_n, threshold, mask, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fm_select_threshold launch");
+  return FM_OK;
+}
+
+fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t* mask, int32_t B, int64_t N,
+                            int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
+                            int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (cap < 0) return fail(FM_EINVAL, "cap = %d must be >= 0", cap);
+  if ((entering == nullptr) != (n_entering == nullptr) || (leaving == nullptr) != (n_leaving == nullptr))
+    return fail(FM_EINVAL, "each optional list comes with its count array (both or neither)");
+  if (B == 0 || N == 0) return FM_OK;
+  if (!mask || !resident || !n_resident) return fail(FM_EINVAL, "null pointer to fm_resident_delta");
+  if (!aligned(resident, 4) || !aligned(n_resident, 4) || (entering && (!aligned(entering, 4) || !aligned(n_entering, 4))) ||
+      (leaving && (!aligned(leaving, 4) || !aligned(n_leaving, 4))))
+    return fail(FM_EINVAL, "index lists and counts must be 4-byte aligned");
+  hipError_t e = fm::launch_resident_delta(ctx->ws, prev_mask, mask, B, N, cap, resident, n_resident, entering,
+                                           n_entering, leaving, n_leaving, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_resident_delta launch");
   return FM_OK;
 }
 

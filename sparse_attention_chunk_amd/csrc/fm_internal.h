@@ -51,6 +51,9 @@ constexpr int kSelItems = 16;
 constexpr int kSelSlice = kSelThreads * kSelItems;
 constexpr int kSelBins = 2048;
 
+// Resident-set compaction: a block covers kResSlice chunks of one row.
+constexpr int kResSlice = 4096;
+
 struct Workspace {
   // Weights packed at context creation: each row scaled by a power of two
   // and split into f16 hi + lo parts, in 16-row tiles of 2 KB k-steps (the
@@ -72,6 +75,7 @@ struct Workspace {
   uint32_t* sel_state = nullptr; // [max_batch][4]
   void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
   uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
+  uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
 };
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
@@ -92,6 +96,10 @@ hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, i
 
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream);
+
+hipError_t launch_resident_delta(const Workspace& ws, const uint8_t* prev, const uint8_t* mask, int B, int64_t N,
+                                 int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
+                                 int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, hipStream_t stream);
 
 }  // namespace fm
 

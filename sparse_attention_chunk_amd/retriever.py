@@ -124,6 +124,27 @@ class FlashMemoryRetriever:
         _lib.fm_select_threshold(self._ctx, scores, B, N, valid_n, float(threshold), mask)
         return mask
 
+    def resident_delta(self, mask, prev_mask=None, cap=None):
+        """Resident set and recall delta of a retrieval cycle: per row the
+        ascending indices of the kept chunks, of those newly kept (to recall)
+        and of those no longer kept (to evict).  Returns three lists of
+        int32 index tensors (one per row, length = the set's size, at most
+        cap) via fm_resident_delta."""
+        _need(mask, torch.bool, "mask", 2)
+        B, N = mask.shape
+        if prev_mask is not None:
+            _need(prev_mask, torch.bool, "prev_mask", 2)
+            if tuple(prev_mask.shape) != (B, N):
+                raise ValueError("prev_mask shape differs from mask")
+        cap = N if cap is None else int(cap)
+        dev = mask.device
+        lists = [torch.empty((B, max(cap, 1)), dtype=torch.int32, device=dev) for _ in range(3)]
+        counts = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(3)]
+        _lib.fm_resident_delta(self._ctx, prev_mask, mask, B, N, cap, lists[0], counts[0], lists[1], counts[1],
+                               lists[2], counts[2])
+        n = [c.cpu() for c in counts]
+        return tuple([lists[k][b, :min(int(n[k][b]), cap)] for b in range(B)] for k in range(3))
+
     # ----------------------------------------------------- the pages' interface
     def __call__(self, hidden, comp_k, positions, valid_n=None):
         q, w = self.prepare_query(hidden, positions)

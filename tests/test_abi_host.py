@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score",
-                                  "fm_select_topk", "fm_select_threshold", "fm_last_error"])
+                                  "fm_select_topk", "fm_select_threshold", "fm_resident_delta", "fm_last_error"])
 
 
 def test_library_exports_every_declared_symbol():

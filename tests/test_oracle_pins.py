@@ -391,3 +391,50 @@ def test_run_row_modes_exclusive():
         oracle.run_row([lw], np.ones(2), 0, rec, cfg, top_k=1, threshold=0.5)
     r = oracle.run_row([lw], np.ones(2), 0, rec, cfg, top_k=2)
     assert list(r["mask"]) == [1, 1, 0]          # all scores 0.5: ties to the lowest indices
+
+
+# --------------------------------------------------------------------------- resident set and recall delta
+
+def _delta_by_sets(mask, prev):
+    """Brute force with Python sets and an explicit loop."""
+    cur_set = {n for n in range(len(mask)) if mask[n]}
+    prev_set = set() if prev is None else {n for n in range(len(prev)) if prev[n]}
+    return sorted(cur_set), sorted(cur_set - prev_set), sorted(prev_set - cur_set)
+
+
+def test_resident_delta_brute_force_tiny():
+    rng = np.random.default_rng(40)
+    for n in (0, 1, 2, 7, 33):
+        for _ in range(20):
+            cur = (rng.uniform(size=n) < rng.uniform()).astype(np.uint8)
+            prev = (rng.uniform(size=n) < rng.uniform()).astype(np.uint8)
+            for p in (None, prev):
+                got = oracle.resident_delta(cur, p)
+                want = _delta_by_sets(cur, p)
+                for g, w in zip(got, want):
+                    assert list(g) == w
+
+
+def test_resident_delta_identities():
+    rng = np.random.default_rng(41)
+    cur = (rng.uniform(size=5000) < 0.1).astype(np.uint8)
+    prev = (rng.uniform(size=5000) < 0.1).astype(np.uint8)
+    res, ent, lea = oracle.resident_delta(cur, prev)
+    prev_res, _, _ = oracle.resident_delta(prev)
+    # the new resident set is the previous one plus entering minus leaving
+    assert sorted((set(prev_res) | set(ent)) - set(lea)) == list(res)
+    assert len(res) == len(prev_res) + len(ent) - len(lea)
+    assert not set(ent) & set(prev_res) and set(lea) <= set(prev_res)
+    assert all(np.all(np.diff(x) > 0) for x in (res, ent, lea) if len(x) > 1)
+    # same mask twice: nothing moves; no previous mask: everything enters
+    r2, e2, l2 = oracle.resident_delta(cur, cur)
+    assert len(e2) == 0 and len(l2) == 0 and list(r2) == list(res)
+    r3, e3, l3 = oracle.resident_delta(cur)
+    assert list(e3) == list(res) and len(l3) == 0
+
+
+def test_resident_delta_counts_nonzero_bytes():
+    cur = np.array([0, 1, 2, 255, 0], np.uint8)
+    prev = np.array([7, 0, 1, 0, 0], np.uint8)
+    res, ent, lea = oracle.resident_delta(cur, prev)
+    assert list(res) == [1, 2, 3] and list(ent) == [1, 3] and list(lea) == [0]
