@@ -35,6 +35,7 @@ FLOP_PER_CHUNK = 3 * 64 * 128 * 2      # 49152 MFMA flop
 SCORE_BYTES_PER_CHUNK = 132 + 4        # record read + ensemble score written
 PEAK_F16_TFLOPS = 2500.0               # MI355X dense f16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0               # MI355X dense fp8 MFMA
 SCORE_SRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc", "fm_score.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_b30_n262144_pmc.txt")
 
@@ -156,6 +157,81 @@ def resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stre
             "leaving_per_row": float(n[2].mean()), "oracle_us": t_cpu * 1e6}
 
 
+def score_fp8_leg(L, r, q, w, comp_k, scores, B, N, sh, stream, steps):
+    """fm_score_fp8 on the same prepared queries: HIP-event time per call on
+    the launch stream, the method's 49152 flop per chunk against the fp8
+    MFMA peak, and the MFMA work it issues (two e4m3 query parts per head,
+    plus the linear-term fragment: 102400 flop per chunk)."""
+    import torch
+
+    def call():
+        L.fm_score_fp8(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    chunks = B * N
+    achieved = FLOP_PER_CHUNK * chunks / t / 1e12
+    issued = (2 * FLOP_PER_CHUNK + 16 * 128 * 2) * chunks / t / 1e12
+    return {"us": t * 1e6, "chunks_per_s": chunks / t, "achieved_tflops": achieved, "peak_tflops": PEAK_FP8_TFLOPS,
+            "frac": achieved / PEAK_FP8_TFLOPS, "issued_mfma_tflops": issued,
+            "issued_frac": issued / PEAK_FP8_TFLOPS,
+            "hbm_gbs": SCORE_BYTES_PER_CHUNK * chunks / t / 1e9,
+            "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t / 1e9 / PEAK_HBM_GBS}
+
+
+def subset_topk_leg(fm, L, r, scores, B, N, sh, stream, steps, resident_k=32768):
+    """fm_select_topk_subset: a decode step's top-512 within each row's
+    resident set.  The resident set is this pass's top-32768 chunks per row
+    (12.5% of N, the share of the compressed cache the model card keeps on
+    the GPU); the step's scores are seeded uniform stand-ins (the pages do
+    not define the step's score function).  HIP-event time per call on the
+    launch stream; bytes = the list and the gathered scores (4 B each per
+    entry) plus the chosen indices; the oracle timed on the same inputs."""
+    import numpy as np
+    import torch
+
+    import oracle
+    keep = torch.empty((B, N), dtype=torch.bool, device="cuda")
+    L.fm_select_topk(r.ctx, scores, B, N, None, resident_k, keep, sh)
+    sub = torch.empty((B, resident_k), dtype=torch.int32, device="cuda")
+    n_sub = torch.empty((B,), dtype=torch.int32, device="cuda")
+    L.fm_resident_delta(r.ctx, None, keep, B, N, resident_k, sub, n_sub, None, None, None, None, sh)
+    g = torch.Generator().manual_seed(77)
+    step = torch.rand((B, N), generator=g).cuda()
+    out = torch.empty((B, TOP_K), dtype=torch.int32, device="cuda")
+    n_out = torch.empty((B,), dtype=torch.int32, device="cuda")
+
+    def call():
+        L.fm_select_topk_subset(r.ctx, step, B, N, sub, n_sub, resident_k, TOP_K, out, n_out, sh)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    nbytes = B * (8 * resident_k + 4 * TOP_K + 8)
+    st, sb = step.cpu().numpy(), sub.cpu().numpy()
+    t0 = time.perf_counter()
+    for b in range(B):
+        oracle.select_topk_subset(st[b], sb[b], TOP_K)
+    t_cpu = time.perf_counter() - t0
+    return {"us": t * 1e6, "resident_per_row": resident_k, "top_k": TOP_K, "entries_per_s": B * resident_k / t,
+            "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9, "oracle_us": t_cpu * 1e6}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -241,6 +317,8 @@ def main(argv=None):
     # mask against the previous cycle's (the same pass for the decode token
     # 64 steps earlier: positions - 256 at 4 tokens per chunk).
     resident = resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps)
+    score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
+    subset = subset_topk_leg(fm, L, r, scores, B, N, sh, stream, args.steps)
 
     prep = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
     score = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
@@ -286,7 +364,7 @@ def main(argv=None):
                          "score_p10": float(np.percentile(score, 10) * 1e6),
                          "score_p90": float(np.percentile(score, 90) * 1e6)},
         "score_only_chunks_per_s": chunks / t_score,
-        "next_rows": {"resident_delta": resident},
+        "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset},
         "host_cpu": cpu_model,
     }
     print(json.dumps(out))

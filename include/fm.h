@@ -144,6 +144,17 @@ fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* posi
 fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
                    const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream);
 
+/* fm_score on the fp8 matrix cores: the native-FP8 indexer form that the
+ * model card's "It is / isn't" section names for production.  Same
+ * arguments, outputs and error behaviour as fm_score.  The stored e4m3
+ * codes enter the fp8 MFMA directly; each head's query is scaled by a power
+ * of two and split into two e4m3 parts (hi + lo, about 8 significant bits;
+ * relative error at most 2^-8 per element), so the scores are less precise
+ * than fm_score's (measured within 6e-4 of the fp64 result on the synthetic
+ * workloads, against 2.3e-4) and stay within the same 2e-3 bound. */
+fm_status fm_score_fp8(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                       const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream);
+
 /* Keep mask of the top_k highest scores of each row ("Usage" top_k=...;
  * "Inference flow" top-K).  Ties are broken towards the lower chunk index,
  * so the mask is unique; top_k >= valid_n keeps every valid chunk; top_k 0
@@ -154,6 +165,29 @@ fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* c
  * top_k >= 0. */
 fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                          int32_t top_k, uint8_t* mask, void* stream);
+
+/* Per-step top-K confined to a subset of the chunks (model card "How it
+ * works", Level 2: the Lightning Indexer's top-512 runs only over the
+ * resident_set that the Memory Indexer recalled).  The pages define the
+ * selection, not the step's score function: the scores are an input.
+ *   scores    device fp32 [B][N], the step's score of every chunk (finite or
+ *             -inf; NaN is not ordered)
+ *   subset    device int32 [B][cap]: row b's chunk indices (its resident
+ *             set, e.g. fm_resident_delta's list), distinct; entries outside
+ *             [0, N) are never chosen.  May be NULL when cap is 0
+ *   n_subset  device int32 [B] or NULL (= cap): entries used per row,
+ *             clamped to [0, cap]
+ *   top_k     entries to choose per row (>= 0)
+ *   out       device int32 [B][top_k]: the chosen chunk indices in subset
+ *             order (ascending when the subset is); entries past n_out[b]
+ *             are not written
+ *   n_out     device int32 [B]: min(top_k, valid entries of row b)
+ * The chosen entries are the top_k by score; ties go to the earlier subset
+ * position (the lower chunk index for an ascending subset), so the result
+ * is unique.  B in [0, max_batch], N in [0, max_n], cap >= 0. */
+fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* subset,
+                                const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out, int32_t* n_out,
+                                void* stream);
 
 /* Keep mask score > threshold, strictly ("Usage" threshold=...;
  * "Inference flow" sigmoid > thresh).  Chunks at or beyond valid_n are

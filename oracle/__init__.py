@@ -37,6 +37,7 @@ from .fm_oracle import (  # noqa: F401
     ensemble,
     select_topk,
     select_threshold,
+    select_topk_subset,
     resident_delta,
     score_row,
     run_row,

@@ -330,6 +330,26 @@ def resident_delta(mask: np.ndarray, prev_mask: np.ndarray | None = None):
     return np.flatnonzero(cur), np.flatnonzero(cur & ~prev), np.flatnonzero(prev & ~cur)
 
 
+def select_topk_subset(scores: np.ndarray, subset: np.ndarray, top_k: int) -> np.ndarray:
+    """One decode step's top-K confined to the resident set, for one row.
+
+    Model card "How it works", Level 2: the Lightning Indexer's native
+    top-512 runs every step but only over the resident_set.  The pages give
+    the selection, not the step's score function, so the scores are an
+    input.  Readings: the subset is a list of chunk indices; entries outside
+    [0, N) are never chosen; the top_k entries by score are chosen, ties
+    going to the earlier list position; fewer valid entries than top_k
+    chooses them all.  Returns the chosen chunk indices in list order.
+    """
+    scores = np.asarray(scores, np.float64)
+    subset = np.asarray(subset, np.int64)
+    n = scores.shape[0]
+    pos = np.flatnonzero((subset >= 0) & (subset < n))
+    k = min(int(top_k), len(pos))
+    order = np.lexsort((pos, -scores[subset[pos]]))  # primary: score desc; secondary: position asc
+    return subset[np.sort(pos[order[:k]])]
+
+
 def score_row(comp_k_row: np.ndarray, q_row: np.ndarray, w_row: np.ndarray, valid_n: int | None = None,
               mode: str = "max", head_dim: int = 128):
     """Scores of one request row from prepared queries.

@@ -26,8 +26,8 @@ STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUN
                 FM_ENOMEM: "FM_ENOMEM", FM_EHIP: "FM_EHIP"}
 
 # Exported symbols, in header order.
-EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_select_topk",
-           "fm_select_threshold", "fm_resident_delta", "fm_last_error")
+EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_fp8",
+           "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta", "fm_last_error")
 
 
 class FmConfig(ctypes.Structure):
@@ -64,7 +64,7 @@ class FmError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libfm.so is not built at {LIB_PATH}: run `python -m sparse_attention_chunk_amd.build`")
+        raise ImportError(f"libfm.so is not built at {LIB_PATH}: run `python sparse_attention_chunk_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.fm_config_default.argtypes = [ctypes.POINTER(FmConfig)]
@@ -77,8 +77,12 @@ def _load() -> ctypes.CDLL:
     lib.fm_prepare_query.restype = ctypes.c_int
     lib.fm_score.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, vp, vp, vp]
     lib.fm_score.restype = ctypes.c_int
+    lib.fm_score_fp8.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, vp, vp, vp]
+    lib.fm_score_fp8.restype = ctypes.c_int
     lib.fm_select_topk.argtypes = [vp, vp, i32, i64, vp, i32, vp, vp]
     lib.fm_select_topk.restype = ctypes.c_int
+    lib.fm_select_topk_subset.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, vp, vp, vp]
+    lib.fm_select_topk_subset.restype = ctypes.c_int
     lib.fm_select_threshold.argtypes = [vp, vp, i32, i64, vp, ctypes.c_float, vp, vp]
     lib.fm_select_threshold.restype = ctypes.c_int
     lib.fm_resident_delta.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -137,9 +141,21 @@ def fm_score(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer=None, str
           "fm_score")
 
 
+def fm_score_fp8(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer=None, stream=None) -> None:
+    s = current_stream() if stream is None else stream
+    check(LIB.fm_score_fp8(ctx, ptr(q), ptr(w), ptr(comp_k), B, N, ptr(valid_n), mode, ptr(scores), ptr(per_layer),
+                           s), "fm_score_fp8")
+
+
 def fm_select_topk(ctx, scores, B, N, valid_n, top_k, mask, stream=None) -> None:
     s = current_stream() if stream is None else stream
     check(LIB.fm_select_topk(ctx, ptr(scores), B, N, ptr(valid_n), top_k, ptr(mask), s), "fm_select_topk")
+
+
+def fm_select_topk_subset(ctx, scores, B, N, subset, n_subset, cap, top_k, out, n_out, stream=None) -> None:
+    s = current_stream() if stream is None else stream
+    check(LIB.fm_select_topk_subset(ctx, ptr(scores), B, N, ptr(subset), ptr(n_subset), cap, top_k, ptr(out),
+                                    ptr(n_out), s), "fm_select_topk_subset")
 
 
 def fm_select_threshold(ctx, scores, B, N, valid_n, threshold, mask, stream=None) -> None:

@@ -1,6 +1,8 @@
 """Builds libfm.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-python -m sparse_attention_chunk_amd.build [--isa DIR]
+python sparse_attention_chunk_amd/build.py [--isa DIR]
+
+(run as a script: importing the package needs a built, current libfm.so)
 
 --isa DIR also writes the device assembly of every source into DIR (for
 register/spill inspection); the library itself is built the same way.
@@ -19,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfm.so")
-SOURCES = ["fm_api.hip", "fm_query.hip", "fm_score.hip", "fm_select.hip", "fm_resident.hip"]
+SOURCES = ["fm_api.hip", "fm_query.hip", "fm_score.hip", "fm_score_fp8.hip", "fm_select.hip", "fm_subset.hip", "fm_resident.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 vector ops stay off for every HIP file.

@@ -148,8 +148,8 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   }
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
   enum {
-    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kRowTiles, kWaveRow, kSelState,
-    kSelCand, kSelCount, kResCount, kNumBuffers
+    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
+    kSelState, kSelCand, kSelCount, kResCount, kNumBuffers
   };
   size_t sizes[kNumBuffers];
   sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
@@ -163,6 +163,8 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kFreq] = sizeof(double) * (kRopeDim / 2);
   sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
   sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
+  sizes[kQPack8] = (size_t)32 * kQ8Frags * 64 * mb;      // 32 e4m3 bytes per lane
+  sizes[kW8] = sizeof(float) * kLayers * kW8Stride * mb;
   sizes[kRowTiles] = sizeof(int64_t) * (mb + 1);
   sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
   sizes[kSelState] = sizeof(uint32_t) * mb * 4;
@@ -199,6 +201,8 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.rope_freq = (double*)(p + offs[kFreq]);
   ctx->ws.rope_cs = (float*)(p + offs[kCosSin]);
   ctx->ws.qpack = (void*)(p + offs[kQPack]);
+  ctx->ws.qpack8 = (void*)(p + offs[kQPack8]);
+  ctx->ws.w8 = (float*)(p + offs[kW8]);
   ctx->ws.row_tiles = (int64_t*)(p + offs[kRowTiles]);
   ctx->ws.wave_row = (int32_t*)(p + offs[kWaveRow]);
   ctx->ws.score_blocks = cus;
@@ -210,6 +214,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
   e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = init_select_topk_subset(dev, &ctx->ws.subset_lds);
   if (e == hipSuccess) e = launch_pack_weights(*weights, ctx->ws, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -243,22 +248,36 @@ fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* posi
   return FM_OK;
 }
 
-fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
-                   const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream) {
+static fm_status score_common(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                              const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream,
+                              bool fp8) {
   g_err.clear();
+  const char* name = fp8 ? "fm_score_fp8" : "fm_score";
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
   if (mode != FM_ENSEMBLE_MAX && mode != FM_ENSEMBLE_MEAN) return fail(FM_EINVAL, "unknown ensemble mode %d", (int)mode);
   if (B == 0 || N == 0) return FM_OK;
-  if (!q || !w || !comp_k || !scores) return fail(FM_EINVAL, "null pointer to fm_score");
+  if (!q || !w || !comp_k || !scores) return fail(FM_EINVAL, "null pointer to %s", name);
   if (!aligned(q, 16) || !aligned(w, 16) || !aligned(comp_k, 4) || !aligned(scores, 4) ||
       (per_layer && !aligned(per_layer, 4)) || (valid_n && !aligned(valid_n, 4)))
     return fail(FM_EINVAL, "q, w must be 16-byte aligned; comp_k, scores, per_layer, valid_n 4-byte aligned");
-  hipError_t e = fm::launch_score(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, scores, per_layer,
-                                  (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "fm_score launch");
+  hipError_t e = fp8 ? fm::launch_score_fp8(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, scores, per_layer,
+                                            (hipStream_t)stream)
+                     : fm::launch_score(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, scores, per_layer,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fp8 ? "fm_score_fp8 launch" : "fm_score launch");
   return FM_OK;
+}
+
+fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                   const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream) {
+  return score_common(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer, stream, false);
+}
+
+fm_status fm_score_fp8(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                       const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream) {
+  return score_common(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer, stream, true);
 }
 
 fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
@@ -274,6 +293,25 @@ fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N,
     return fail(FM_EINVAL, "scores and valid_n must be 4-byte aligned");
   hipError_t e = fm::launch_select_topk(ctx->ws, scores, B, N, valid_n, top_k, mask, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fm_select_topk launch");
+  return FM_OK;
+}
+
+fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* subset,
+                                const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out, int32_t* n_out,
+                                void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (cap < 0 || top_k < 0) return fail(FM_EINVAL, "cap (%d) and top_k (%d) must be >= 0", cap, top_k);
+  if (B == 0) return FM_OK;
+  if (!n_out || (N > 0 && !scores) || (cap > 0 && !subset) || (top_k > 0 && !out))
+    return fail(FM_EINVAL, "null pointer to fm_select_topk_subset");
+  if (!aligned(scores, 4) || !aligned(subset, 4) || !aligned(n_subset, 4) || !aligned(out, 4) || !aligned(n_out, 4))
+    return fail(FM_EINVAL, "scores, subset, n_subset, out, n_out must be 4-byte aligned");
+  hipError_t e = fm::launch_select_topk_subset(scores, B, N, subset, n_subset, cap, top_k, out, n_out,
+                                               ctx->ws.subset_lds, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_select_topk_subset launch");
   return FM_OK;
 }
 

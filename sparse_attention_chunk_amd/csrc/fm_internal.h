@@ -41,6 +41,14 @@ inline int proj2_splits(int) { return kQLora / kSliceK; }
 // then 4 fragments (one per k-step) of the per-layer weighted query sums.
 constexpr int kQHeadFrags = kLayers * 4 * 4;
 constexpr int kQFrags = kQHeadFrags + 4;
+// fp8 score path: per request row 24 fragments of 64 lanes x 32 e4m3 bytes
+// (3 layers x 4 head tiles x {hi, lo} parts), then one fragment of the
+// per-layer weighted query sums in three parts; per (row, layer) the halved
+// head weights with each head's query scale folded in, then the layer's
+// linear-term scale (kW8Stride floats).
+constexpr int kQ8HeadFrags = kLayers * 4 * 2;
+constexpr int kQ8Frags = kQ8HeadFrags + 1;
+constexpr int kW8Stride = kHeads + 4;
 // The score kernel runs one block of 4 waves per compute unit; each wave
 // takes an equal share of the row-major list of 16-chunk tiles.
 constexpr int kMaxScoreBlocks = 1024;
@@ -69,6 +77,8 @@ struct Workspace {
   double* rope_freq = nullptr;   // [kRopeDim / 2]
   float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16
+  void* qpack8 = nullptr;        // [max_batch][kQ8Frags][64][32] e4m3
+  float* w8 = nullptr;           // [max_batch][3][kW8Stride]
   int64_t* row_tiles = nullptr;  // [max_batch + 1]: first tile of each row in the list of valid tiles
   int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
   int score_blocks = 0;          // compute units of the device
@@ -76,6 +86,7 @@ struct Workspace {
   void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
   uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
+  size_t subset_lds = 0;         // dynamic LDS available to the subset top-K kernel
 };
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
@@ -90,9 +101,24 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
 
 hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
                         const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream);
+hipError_t launch_score_fp8(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
+                            int64_t N, const int32_t* valid_n, int mode, float* scores, float* per_layer,
+                            hipStream_t stream);
+// Shared by both score launchers: with valid_n, plans the ragged tile list
+// (row_tiles, wave_row) and writes -inf past each row's valid_n; returns the
+// tile list to walk (row_tiles, or null and total_tiles for full rows).
+hipError_t launch_score_plan(const Workspace& ws, const int32_t* valid_n, int B, int64_t N, float* scores,
+                             float* per_layer, hipStream_t stream, const int64_t** row_tiles, int64_t* total_tiles);
 
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream);
+
+// Subset top-K: the dynamic LDS limit of the in-LDS variant is set once per
+// device (init) and passed to every launch.
+hipError_t init_select_topk_subset(int device, size_t* max_dynamic_lds);
+hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, const int32_t* subset,
+                                     const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out,
+                                     int32_t* n_out, size_t max_dynamic_lds, hipStream_t stream);
 
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream);

@@ -25,22 +25,15 @@
 //   - max ensemble: max_l sigmoid(t_l) = sigmoid(max_l t_l), one sigmoid.
 #include <algorithm>
 
-#include "fm_internal.h"
+#include "fm_score_common.h"
 
 namespace fm {
 namespace {
 
+using namespace score;
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kTile = 16;                        // chunks per MFMA column tile
-constexpr int kTileBytes = kTile * kRecord;      // 2112
-constexpr int64_t kMaxSegTiles = 1 << 16;        // tiles per pipeline run: buffer offsets stay below 2^31
-constexpr int kRing = 8;                         // register ring of record tiles
-constexpr int kAhead = 6;                        // tile i + 6 is requested in the phase of tile i
 
 // MFMA 16x16x32 f16 operand layout: lane l supplies A[l%16][8(l/16) + e] and
 // B[8(l/16) + e][l%16], e = 0..7, and receives C[4(l/16) + r][l%16].
@@ -131,52 +124,6 @@ __device__ __forceinline__ f16x8 decode8(uint32_t lo, uint32_t hi) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Sum over the four lane groups {l, l^16, l^32, l^48} (every lane gets it).
-__device__ __forceinline__ float sum4groups(float v) {
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return v;
-}
-
-__device__ __forceinline__ float sigmoid(float x) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
-}
-
-struct RawTile {
-  u32x4 lo, hi;  // this lane's 32 code bytes
-  float s;       // the chunk's scale
-};
-
-struct Ctx {
-  __amdgpu_buffer_rsrc_t rec;            // records of this wave's chunks; reads past them return 0
-  __amdgpu_buffer_rsrc_t out;            // scores of this wave's chunks; writes past them are dropped
-  __amdgpu_buffer_rsrc_t pl[kLayers];    // per-layer scores of this wave's chunks (when requested)
-  uint32_t lane_rec_off;                 // 132 c + 32 g
-  uint32_t lane_scale_off;               // 132 c + 128
-  uint32_t lane_out_off;                 // 4 c in lane group 0, out of range elsewhere
-  uint32_t lane_pl_off[kLayers];         // 4 c in lane group l, out of range elsewhere
-  int c, g;
-};
-
-// An offset past every buffer of one pipeline run (they hold at most
-// 16 kMaxSegTiles + 8 tiles of records): the store is dropped by the range
-// check, with no branch.
-constexpr uint32_t kDropOffset = 0x40000000u;
-
-// Offsets go in the per-lane voffset (the range check covers voffset).
-__device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
-  const uint32_t so = (uint32_t)tile * kTileBytes;
-  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so, 0, 0));
-  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so + 16, 0, 0));
-  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cx.rec, cx.lane_scale_off + so, 0, 0));
-}
-
 __device__ __forceinline__ void decode_tile(const RawTile& t, f16x8 (&kf)[4]) {
   kf[0] = decode8(t.lo[0], t.lo[1]);
   kf[1] = decode8(t.lo[2], t.lo[3]);
@@ -219,22 +166,7 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
     // group 1 the low part, groups 2 and 3 hold zeros there.
     t[l] = sum4groups(fmaf(s, lin[l], fabsf(s) * p));  // the layer's logit
   }
-  float e;
-  float sl[kLayers];
-  if (MEAN || PER_LAYER) {
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l) sl[l] = sigmoid(t[l]);
-    e = MEAN ? (sl[0] + sl[1] + sl[2]) * (1.0f / 3.0f) : fmaxf(fmaxf(sl[0], sl[1]), sl[2]);
-  } else {
-    e = sigmoid(fmaxf(fmaxf(t[0], t[1]), t[2]));
-  }
-  const uint32_t to = (uint32_t)tile * (kTile * 4);
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), cx.out, cx.lane_out_off + to, 0, 0);
-  if (PER_LAYER) {
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl[l]), cx.pl[l], cx.lane_pl_off[l] + to, 0, 0);
-  }
+  store_tile<MEAN, PER_LAYER>(cx, t, tile);
 }
 
 // Instruction order of one phase for the scheduler: every MFMA followed by
@@ -268,27 +200,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
                                           const uint8_t* __restrict__ comp_k, int B, int64_t N, int b, int64_t start,
                                           int64_t count, int lane, float* __restrict__ scores,
                                           float* __restrict__ per_layer) {
-  Ctx cx;
-  cx.c = lane & 15;
-  cx.g = lane >> 4;
-  cx.lane_rec_off = (uint32_t)(cx.c * kRecord + 32 * cx.g);
-  cx.lane_scale_off = (uint32_t)(cx.c * kRecord + kHeadDim);
-  cx.lane_out_off = cx.g == 0 ? (uint32_t)(cx.c * 4) : kDropOffset;
-  cx.rec = __builtin_amdgcn_make_buffer_rsrc((void*)(comp_k + ((size_t)b * N + start) * kRecord), 0,
-                                             (int)(count * kRecord), kBufferWord3);
-  cx.out = __builtin_amdgcn_make_buffer_rsrc((void*)(scores + (size_t)b * N + start), 0, (int)(count * 4),
-                                             kBufferWord3);
-#pragma unroll
-  for (int l = 0; l < kLayers; ++l) {
-    cx.lane_pl_off[l] = cx.g == l ? (uint32_t)(cx.c * 4) : kDropOffset;
-    cx.pl[l] = __builtin_amdgcn_make_buffer_rsrc(
-        PER_LAYER ? (void*)(per_layer + ((size_t)l * B + b) * N + start) : (void*)scores, 0,
-        PER_LAYER ? (int)(count * 4) : 0, kBufferWord3);
-  }
-
-  RawTile ring[kRing];
-#pragma unroll
-  for (int k = 0; k < kAhead; ++k) load_tile(cx, k, ring[k]);
+  const Ctx cx = make_ctx<PER_LAYER>(comp_k, B, N, b, start, count, lane, scores, per_layer);
 
   // Query fragments, linear-term fragments and w: every load is issued
   // before the first use, so the wave pays one memory latency here, not one
@@ -310,6 +222,16 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
     for (int l = 0; l < kLayers; ++l)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) wv[l][mt] = *(const f32x4*)(w + ((size_t)l * B + b) * kHeads + 16 * mt + 4 * cx.g);
+  }
+  // The first records are requested after the queries and weights, one tile
+  // at a time in tile order: the waits before the loop then cover only the
+  // queries and weights, and those in the loop count record loads alone.
+  __builtin_amdgcn_sched_barrier(0);
+  RawTile ring[kRing];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    load_tile(cx, k, ring[k]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Keep the query fragments in accumulation registers: the MFMA reads its A
   // operand from there, leaving the vector registers to the accumulators,
@@ -377,12 +299,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 #undef FM_PHASE
 }
 
-// grid = number of compute units, block = 256 (one wave per SIMD).  The
-// valid tiles of all rows, in row-major order, are split into equal
-// contiguous shares, one per wave: with row_tiles (prefix of the rows'
-// valid tile counts, from the plan kernel) when rows are ragged, else every
-// row has ceil(N / 16) tiles.  A share may end in the next row (or, for
-// short rows, several rows later): each row's part is its own pipeline run.
+// grid = number of compute units, block = 256 (one wave per SIMD); each wave
+// scores its share of the tile list (walk_share).
 template <bool MEAN, bool PER_LAYER>
 __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
                                                        const uint8_t* __restrict__ comp_k, int B, int64_t N,
@@ -392,43 +310,9 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
                                                        int64_t total_tiles,  // used when row_tiles is null
                                                        float* __restrict__ scores, float* __restrict__ per_layer) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps descriptors scalar
-  const int64_t waves = 4 * (int64_t)gridDim.x;
-  const int64_t gw = 4 * (int64_t)blockIdx.x + wave;
-  const int64_t total = row_tiles ? row_tiles[B] : total_tiles;
-  int64_t t = gw * total / waves;
-  const int64_t t_end = (gw + 1) * total / waves;
-  if (t >= t_end) return;
-  const int64_t row_full = (N + kTile - 1) / kTile;
-  int b;
-  int64_t first;  // list index of row b's first tile
-  if (row_tiles) {
-    b = wave_row[gw];
-    first = row_tiles[b];
-  } else {
-    b = (int)(t / row_full);
-    first = (int64_t)b * row_full;
-  }
-  while (t < t_end) {
-    const int64_t last = row_tiles ? row_tiles[b + 1] : first + row_full;
-    int64_t run_end = t_end < last ? t_end : last;
-    if (run_end - t > kMaxSegTiles) run_end = t + kMaxSegTiles;
-    if (run_end > t) {
-      int64_t vn = N;
-      if (valid_n) {
-        const int64_t v = valid_n[b];
-        vn = v < 0 ? 0 : (v > N ? N : v);
-      }
-      const int64_t start = (t - first) * kTile;
-      const int64_t end = run_end - first == last - first ? vn : (run_end - first) * kTile;
-      score_run<MEAN, PER_LAYER>(qpack, w, comp_k, B, N, b, start, end - start, lane, scores, per_layer);
-    }
-    t = run_end;
-    if (t >= last) {
-      ++b;
-      first = last;
-    }
-  }
+  walk_share(B, N, valid_n, row_tiles, wave_row, total_tiles, [&](int b, int64_t start, int64_t count) {
+    score_run<MEAN, PER_LAYER>(qpack, w, comp_k, B, N, b, start, count, lane, scores, per_layer);
+  });
 }
 
 // Plan for ragged rows (one block of 1024 threads): row_tiles[b] = sum of
@@ -503,29 +387,36 @@ __global__ __launch_bounds__(256) void score_tail_kernel(const int32_t* __restri
 
 }  // namespace
 
-hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
-                        const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream) {
-  f16x8* qpack = (f16x8*)ws.qpack;
-  hipLaunchKernelGGL(pack_q_kernel, dim3(B * kLayers), dim3(256), 0, stream, q, w, B, qpack);
-  const int blocks = ws.score_blocks;
-  const int waves = 4 * blocks;
-  int64_t total_tiles = (int64_t)B * ((N + kTile - 1) / kTile);
-  const int64_t* row_tiles = nullptr;
+hipError_t launch_score_plan(const Workspace& ws, const int32_t* valid_n, int B, int64_t N, float* scores,
+                             float* per_layer, hipStream_t stream, const int64_t** row_tiles, int64_t* total_tiles) {
+  *total_tiles = (int64_t)B * ((N + kTile - 1) / kTile);
+  *row_tiles = nullptr;
   if (valid_n) {
-    hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(1024), 0, stream, valid_n, B, N, waves, ws.row_tiles,
-                       ws.wave_row);
-    row_tiles = ws.row_tiles;
+    hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(1024), 0, stream, valid_n, B, N, 4 * ws.score_blocks,
+                       ws.row_tiles, ws.wave_row);
+    *row_tiles = ws.row_tiles;
     const unsigned gx = (unsigned)std::min<int64_t>((N + 255) / 256, 64);
     if (per_layer)
       hipLaunchKernelGGL(score_tail_kernel<true>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores, per_layer);
     else
       hipLaunchKernelGGL(score_tail_kernel<false>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores, per_layer);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
+                        const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream) {
+  f16x8* qpack = (f16x8*)ws.qpack;
+  hipLaunchKernelGGL(pack_q_kernel, dim3(B * kLayers), dim3(256), 0, stream, q, w, B, qpack);
+  const int64_t* row_tiles;
+  int64_t total_tiles;
+  hipError_t e = launch_score_plan(ws, valid_n, B, N, scores, per_layer, stream, &row_tiles, &total_tiles);
+  if (e != hipSuccess) return e;
   const bool mean = mode == FM_ENSEMBLE_MEAN;
   auto kern = mean ? (per_layer ? score_kernel<true, true> : score_kernel<true, false>)
                    : (per_layer ? score_kernel<false, true> : score_kernel<false, false>);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n, row_tiles,
-                     (const int32_t*)ws.wave_row, total_tiles, scores, per_layer);
+  hipLaunchKernelGGL(kern, dim3(ws.score_blocks), dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N, valid_n,
+                     row_tiles, (const int32_t*)ws.wave_row, total_tiles, scores, per_layer);
   return hipGetLastError();
 }
 

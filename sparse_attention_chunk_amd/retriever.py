@@ -96,7 +96,9 @@ class FlashMemoryRetriever:
         _lib.fm_prepare_query(self._ctx, hidden, positions, B, q, w)
         return q, w
 
-    def score(self, q, w, comp_k, valid_n=None, mode="max", per_layer=False):
+    def score(self, q, w, comp_k, valid_n=None, mode="max", per_layer=False, fp8=False):
+        """Per-layer and ensemble scores (fm_score); fp8=True runs the
+        fp8-MFMA form (fm_score_fp8)."""
         _need(comp_k, torch.uint8, "comp_k", 3)
         _need(q, torch.float32, "q", 4)
         _need(w, torch.float32, "w", 3)
@@ -107,7 +109,8 @@ class FlashMemoryRetriever:
             _need(valid_n, torch.int32, "valid_n", 1)
         scores = torch.empty((B, N), dtype=torch.float32, device=comp_k.device)
         pl = torch.empty((3, B, N), dtype=torch.float32, device=comp_k.device) if per_layer else None
-        _lib.fm_score(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], scores, pl)
+        fn = _lib.fm_score_fp8 if fp8 else _lib.fm_score
+        fn(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], scores, pl)
         return (scores, pl) if per_layer else scores
 
     def keep_topk(self, scores, top_k: int, valid_n=None):
@@ -144,6 +147,25 @@ class FlashMemoryRetriever:
                                lists[2], counts[2])
         n = [c.cpu() for c in counts]
         return tuple([lists[k][b, :min(int(n[k][b]), cap)] for b in range(B)] for k in range(3))
+
+    def topk_in_subset(self, scores, subset, top_k: int, n_subset=None):
+        """One decode step's top-K confined to each row's resident set
+        (fm_select_topk_subset): scores [B, N] fp32 (the step's scores of
+        every chunk), subset [B, cap] int32 chunk indices, n_subset [B] int32
+        or None (= cap).  Returns (out [B, top_k] int32, n_out [B] int32):
+        row b's chosen indices are out[b, :n_out[b]], in subset order."""
+        _need(scores, torch.float32, "scores", 2)
+        _need(subset, torch.int32, "subset", 2)
+        B, N = scores.shape
+        if subset.shape[0] != B:
+            raise ValueError("subset has a different number of rows than scores")
+        if n_subset is not None:
+            _need(n_subset, torch.int32, "n_subset", 1)
+        cap = subset.shape[1]
+        out = torch.empty((B, max(int(top_k), 1)), dtype=torch.int32, device=scores.device)
+        n_out = torch.empty((B,), dtype=torch.int32, device=scores.device)
+        _lib.fm_select_topk_subset(self._ctx, scores, B, N, subset, n_subset, cap, int(top_k), out, n_out)
+        return out[:, :int(top_k)], n_out
 
     # ----------------------------------------------------- the pages' interface
     def __call__(self, hidden, comp_k, positions, valid_n=None):

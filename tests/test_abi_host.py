@@ -15,12 +15,13 @@ HEADER = os.path.join(ROOT, "include", "fm.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score",
-                                  "fm_select_topk", "fm_select_threshold", "fm_resident_delta", "fm_last_error"])
+                                  "fm_score_fp8", "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold",
+                                  "fm_resident_delta", "fm_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -52,8 +53,10 @@ def test_null_context_is_rejected_before_any_launch():
     assert L.fm_prepare_query(None, None, None, 1, None, None, None) == _lib.FM_EINVAL
     assert "null context" in _lib.last_error()
     assert L.fm_score(None, None, None, None, 1, 1, None, 0, None, None, None) == _lib.FM_EINVAL
+    assert L.fm_score_fp8(None, None, None, None, 1, 1, None, 0, None, None, None) == _lib.FM_EINVAL
     assert L.fm_select_topk(None, None, 1, 1, None, 1, None, None) == _lib.FM_EINVAL
     assert L.fm_select_threshold(None, None, 1, 1, None, 0.5, None, None) == _lib.FM_EINVAL
+    assert L.fm_select_topk_subset(None, None, 1, 1, None, None, 1, 1, None, None, None) == _lib.FM_EINVAL
     L.fm_destroy(None)  # no-op
 
 

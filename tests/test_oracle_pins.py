@@ -8,6 +8,7 @@ Retriever README, sections "compressed_k format", "Architecture", "Joint
 checkpoint + ensemble", "Usage" and the "Inference flow" figure.
 """
 
+import itertools
 import json
 import math
 import os
@@ -438,3 +439,54 @@ def test_resident_delta_counts_nonzero_bytes():
     prev = np.array([7, 0, 1, 0, 0], np.uint8)
     res, ent, lea = oracle.resident_delta(cur, prev)
     assert list(res) == [1, 2, 3] and list(ent) == [1, 3] and list(lea) == [0]
+
+
+# --------------------------------------------------------------------------- per-step top-K within the resident set
+
+def _subset_topk_by_exchange(scores, subset, k):
+    """Brute force: among all k-sets of valid list positions, the one set S
+    where every chosen entry beats every left-out one (higher score, or the
+    same score at an earlier position).  Returned in list order."""
+    n = len(scores)
+    valid = [p for p in range(len(subset)) if 0 <= subset[p] < n]
+    k = min(k, len(valid))
+    found = []
+    for S in itertools.combinations(valid, k):
+        rest = [u for u in valid if u not in S]
+        if all(scores[subset[s]] > scores[subset[u]] or (scores[subset[s]] == scores[subset[u]] and s < u)
+               for s in S for u in rest):
+            found.append([subset[p] for p in S])
+    assert len(found) == 1  # the rule makes the choice unique
+    return found[0]
+
+
+def test_subset_topk_brute_force_tiny():
+    rng = np.random.default_rng(50)
+    for _ in range(60):
+        n = int(rng.integers(1, 12))
+        scores = rng.integers(0, 4, n).astype(np.float64) / 4  # many ties
+        scores[rng.uniform(size=n) < 0.1] = -np.inf
+        m = int(rng.integers(0, 9))
+        subset = rng.integers(-2, n + 2, m)                    # some entries out of range
+        subset = np.array([x for i, x in enumerate(subset) if x < 0 or x >= n or x not in subset[:i]], np.int64)
+        for k in (0, 1, 2, 5, 20):
+            got = list(oracle.select_topk_subset(scores, subset, k))
+            assert got == _subset_topk_by_exchange(scores, subset, k)
+
+
+def test_subset_topk_over_all_chunks_is_the_row_top_k():
+    rng = np.random.default_rng(51)
+    scores = np.round(rng.uniform(size=3000), 2)                # ties
+    for k in (0, 1, 512, 2999, 3000, 4000):
+        mask = oracle.select_topk(scores, 3000, k)
+        assert np.array_equal(oracle.select_topk_subset(scores, np.arange(3000), k), np.flatnonzero(mask))
+
+
+def test_subset_topk_order_and_range():
+    scores = np.array([0.1, 0.9, 0.5, 0.9, 0.3])
+    # list order is kept (not score order); out-of-range entries are skipped
+    assert list(oracle.select_topk_subset(scores, np.array([4, 3, 7, 1, -1, 0]), 3)) == [4, 3, 1]
+    # tie at 0.9 between positions 1 and 3 of the list: the earlier one wins
+    assert list(oracle.select_topk_subset(scores, np.array([0, 3, 2, 1]), 1)) == [3]
+    assert list(oracle.select_topk_subset(scores, np.array([5, 6]), 2)) == []
+    assert list(oracle.select_topk_subset(scores, np.array([2, 0]), 9)) == [2, 0]
