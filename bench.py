@@ -232,6 +232,41 @@ def subset_topk_leg(fm, L, r, scores, B, N, sh, stream, steps, resident_k=32768)
             "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9, "oracle_us": t_cpu * 1e6}
 
 
+def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
+    """fm_mask_logits: this step's top-512 keep mask applied to bf16 attention
+    logits [B, 64 heads, N] in place (synthetic values).  HIP-event time per
+    call on the launch stream; algorithmic bytes per call = the mask, plus per
+    (row, head) 16-chunk group: nothing when all 16 chunks are kept, one
+    write when none is, a read and a write when some are."""
+    import numpy as np
+    import torch
+
+    logits = torch.empty((B, heads, N), dtype=torch.bfloat16, device="cuda")
+    logits.normal_(generator=torch.Generator(device="cuda").manual_seed(5))
+
+    def call():
+        L.fm_mask_logits(r.ctx, logits, L.FM_DTYPE_BF16, B, heads, N, mask, sh)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    m = mask.cpu().numpy().astype(bool)
+    full = (N // 16) * 16
+    g = m[:, :full].reshape(B, -1, 16).sum(axis=2)
+    none_kept, mixed = int((g == 0).sum()), int(((g > 0) & (g < 16)).sum())
+    nbytes = B * N + heads * 2 * 16 * (none_kept + 2 * mixed)
+    del logits
+    return {"us": t * 1e6, "heads": heads, "dtype": "bf16", "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9,
+            "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -319,6 +354,7 @@ def main(argv=None):
     resident = resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps)
     score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
     subset = subset_topk_leg(fm, L, r, scores, B, N, sh, stream, args.steps)
+    masking = mask_logits_leg(L, r, mask, B, N, sh, stream, args.steps)
 
     prep = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
     score = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
@@ -364,7 +400,8 @@ def main(argv=None):
                          "score_p10": float(np.percentile(score, 10) * 1e6),
                          "score_p90": float(np.percentile(score, 90) * 1e6)},
         "score_only_chunks_per_s": chunks / t_score,
-        "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset},
+        "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
+                      "mask_logits": masking},
         "host_cpu": cpu_model,
     }
     print(json.dumps(out))

@@ -62,6 +62,9 @@ typedef enum {
  * and the default; mean is the arithmetic mean of the three sigmoid scores. */
 typedef enum { FM_ENSEMBLE_MAX = 0, FM_ENSEMBLE_MEAN = 1 } fm_ensemble;
 
+/* Element type of attention logits (fm_mask_logits). */
+typedef enum { FM_DTYPE_F32 = 0, FM_DTYPE_BF16 = 1 } fm_dtype;
+
 /* Layer dimensions and constants ("Architecture").  The compiled kernels
  * support exactly n_layers 3, hidden 4096, q_lora_rank 1024, n_heads 64,
  * head_dim 128, rope_dim 64; other values give FM_EUNSUPPORTED.
@@ -215,6 +218,19 @@ fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64
 fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t* mask, int32_t B, int64_t N,
                             int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
                             int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, void* stream);
+
+/* Attention-logit masking over a retrieval cycle (README "Inference flow":
+ * for the next 64 decode steps the attention logits of unselected chunks
+ * are -inf; "What this simulates": a masked chunk contributes nothing to
+ * attention, as if its KV were not loaded).  In place:
+ *   logits  device [B][R][N] of dtype (fp32 or bf16): R logit rows per
+ *           request row (heads, query positions); set to -inf where
+ *           mask[b][n] == 0, untouched where it is non-zero
+ *   mask    device uint8 [B][N], e.g. fm_select_topk's keep mask
+ * B in [0, max_batch], N in [0, max_n], R >= 0; logits aligned to its
+ * element size. */
+fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, int32_t R, int64_t N,
+                         const uint8_t* mask, void* stream);
 
 /* Message of the last failing call on this thread ("" if none); valid until
  * the next fm_* call on this thread. */

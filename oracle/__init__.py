@@ -39,6 +39,7 @@ from .fm_oracle import (  # noqa: F401
     select_threshold,
     select_topk_subset,
     resident_delta,
+    mask_logits,
     score_row,
     run_row,
 )

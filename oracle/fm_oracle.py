@@ -350,6 +350,20 @@ def select_topk_subset(scores: np.ndarray, subset: np.ndarray, top_k: int) -> np
     return subset[np.sort(pos[order[:k]])]
 
 
+def mask_logits(logits: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Attention logits of one request row with the dropped chunks masked.
+
+    README "Inference flow": for the 64 decode steps after a retrieval cycle
+    the attention logits of the chunks not selected are set to -inf; "What
+    this simulates": such a chunk then contributes nothing to attention.
+    logits [R, N] (R logit rows: heads, query positions), mask [N]; a mask
+    entry keeps its chunk when it is non-zero.  Returns a new array.
+    """
+    out = np.array(logits, copy=True)
+    out[:, np.asarray(mask) == 0] = -np.inf
+    return out
+
+
 def score_row(comp_k_row: np.ndarray, q_row: np.ndarray, w_row: np.ndarray, valid_n: int | None = None,
               mode: str = "max", head_dim: int = 128):
     """Scores of one request row from prepared queries.

@@ -21,13 +21,16 @@ FM_ENOMEM = -3
 FM_EHIP = -4
 FM_ENSEMBLE_MAX = 0
 FM_ENSEMBLE_MEAN = 1
+FM_DTYPE_F32 = 0
+FM_DTYPE_BF16 = 1
 
 STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUNSUPPORTED",
                 FM_ENOMEM: "FM_ENOMEM", FM_EHIP: "FM_EHIP"}
 
 # Exported symbols, in header order.
 EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_fp8",
-           "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta", "fm_last_error")
+           "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold", "fm_mask_logits", "fm_resident_delta",
+           "fm_last_error")
 
 
 class FmConfig(ctypes.Structure):
@@ -85,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.fm_select_topk_subset.restype = ctypes.c_int
     lib.fm_select_threshold.argtypes = [vp, vp, i32, i64, vp, ctypes.c_float, vp, vp]
     lib.fm_select_threshold.restype = ctypes.c_int
+    lib.fm_mask_logits.argtypes = [vp, vp, ctypes.c_int, i32, i32, i64, vp, vp]
+    lib.fm_mask_logits.restype = ctypes.c_int
     lib.fm_resident_delta.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.fm_resident_delta.restype = ctypes.c_int
     lib.fm_last_error.argtypes = []
@@ -162,6 +167,11 @@ def fm_select_threshold(ctx, scores, B, N, valid_n, threshold, mask, stream=None
     s = current_stream() if stream is None else stream
     check(LIB.fm_select_threshold(ctx, ptr(scores), B, N, ptr(valid_n), threshold, ptr(mask), s),
           "fm_select_threshold")
+
+
+def fm_mask_logits(ctx, logits, dtype, B, R, N, mask, stream=None) -> None:
+    s = current_stream() if stream is None else stream
+    check(LIB.fm_mask_logits(ctx, ptr(logits), dtype, B, R, N, ptr(mask), s), "fm_mask_logits")
 
 
 def fm_resident_delta(ctx, prev_mask, mask, B, N, cap, resident, n_resident, entering=None, n_entering=None,

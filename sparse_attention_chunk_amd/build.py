@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfm.so")
-SOURCES = ["fm_api.hip", "fm_query.hip", "fm_score.hip", "fm_score_fp8.hip", "fm_select.hip", "fm_subset.hip", "fm_resident.hip"]
+SOURCES = ["fm_api.hip", "fm_query.hip", "fm_score.hip", "fm_score_fp8.hip", "fm_select.hip", "fm_subset.hip", "fm_resident.hip", "fm_mask.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 vector ops stay off for every HIP file.

@@ -331,6 +331,22 @@ fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64
   return FM_OK;
 }
 
+fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, int32_t R, int64_t N,
+                         const uint8_t* mask, void* stream) {
+  g_err.clear();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
+  if (dtype != FM_DTYPE_F32 && dtype != FM_DTYPE_BF16) return fail(FM_EINVAL, "unknown logit dtype %d", (int)dtype);
+  if (R < 0) return fail(FM_EINVAL, "R (%d) must be >= 0", R);
+  if (B == 0 || N == 0 || R == 0) return FM_OK;
+  if (!logits || !mask) return fail(FM_EINVAL, "null pointer to fm_mask_logits");
+  if (!aligned(logits, dtype == FM_DTYPE_F32 ? 4 : 2)) return fail(FM_EINVAL, "logits must be aligned to its element");
+  hipError_t e = fm::launch_mask_logits(logits, (int)dtype, B, R, N, mask, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_mask_logits launch");
+  return FM_OK;
+}
+
 fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t* mask, int32_t B, int64_t N,
                             int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
                             int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, void* stream) {

@@ -123,6 +123,9 @@ hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, cons
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream);
 
+hipError_t launch_mask_logits(void* logits, int dtype, int B, int R, int64_t N, const uint8_t* mask,
+                              hipStream_t stream);
+
 hipError_t launch_resident_delta(const Workspace& ws, const uint8_t* prev, const uint8_t* mask, int B, int64_t N,
                                  int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
                                  int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, hipStream_t stream);

@@ -167,6 +167,21 @@ class FlashMemoryRetriever:
         _lib.fm_select_topk_subset(self._ctx, scores, B, N, subset, n_subset, cap, int(top_k), out, n_out)
         return out[:, :int(top_k)], n_out
 
+    def mask_logits(self, logits, mask):
+        """Sets the attention logits of the chunks a keep mask drops to -inf,
+        in place (fm_mask_logits).  logits [B, R, N] float32 or bfloat16,
+        mask [B, N] bool.  Returns logits."""
+        if logits.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("logits must be float32 or bfloat16")
+        _need(logits, logits.dtype, "logits", 3)
+        _need(mask, torch.bool, "mask", 2)
+        B, R, N = logits.shape
+        if tuple(mask.shape) != (B, N):
+            raise ValueError("mask must be [B, N] of the logits' B and N")
+        dt = _lib.FM_DTYPE_F32 if logits.dtype == torch.float32 else _lib.FM_DTYPE_BF16
+        _lib.fm_mask_logits(self._ctx, logits, dt, B, R, N, mask)
+        return logits
+
     # ----------------------------------------------------- the pages' interface
     def __call__(self, hidden, comp_k, positions, valid_n=None):
         q, w = self.prepare_query(hidden, positions)

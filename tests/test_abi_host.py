@@ -21,7 +21,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score",
                                   "fm_score_fp8", "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold",
-                                  "fm_resident_delta", "fm_last_error"])
+                                  "fm_mask_logits", "fm_resident_delta", "fm_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -57,6 +57,7 @@ def test_null_context_is_rejected_before_any_launch():
     assert L.fm_select_topk(None, None, 1, 1, None, 1, None, None) == _lib.FM_EINVAL
     assert L.fm_select_threshold(None, None, 1, 1, None, 0.5, None, None) == _lib.FM_EINVAL
     assert L.fm_select_topk_subset(None, None, 1, 1, None, None, 1, 1, None, None, None) == _lib.FM_EINVAL
+    assert L.fm_mask_logits(None, None, 0, 1, 1, 1, None, None) == _lib.FM_EINVAL
     L.fm_destroy(None)  # no-op
 
 

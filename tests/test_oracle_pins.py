@@ -490,3 +490,24 @@ def test_subset_topk_order_and_range():
     assert list(oracle.select_topk_subset(scores, np.array([0, 3, 2, 1]), 1)) == [3]
     assert list(oracle.select_topk_subset(scores, np.array([5, 6]), 2)) == []
     assert list(oracle.select_topk_subset(scores, np.array([2, 0]), 9)) == [2, 0]
+
+
+# --------------------------------------------------------------------------- attention-logit masking
+
+def test_mask_logits_loop_and_softmax():
+    rng = np.random.default_rng(60)
+    logits = rng.normal(size=(3, 40))
+    mask = (rng.uniform(size=40) < 0.3).astype(np.uint8)
+    mask[[0, 7]] = [2, 255]                                   # any non-zero byte keeps
+    got = oracle.mask_logits(logits, mask)
+    for r in range(3):
+        for n in range(40):
+            assert got[r, n] == (logits[r, n] if mask[n] else -np.inf)
+    # a masked chunk gets zero attention weight; the kept ones share all of it
+    kept = mask != 0
+    p = scipy.special.softmax(got, axis=1)
+    assert np.all(p[:, ~kept] == 0)
+    assert np.allclose(p[:, kept], scipy.special.softmax(logits[:, kept], axis=1), rtol=1e-12, atol=0)
+    assert np.array_equal(oracle.mask_logits(logits, np.ones(40)), logits)
+    assert np.all(np.isneginf(oracle.mask_logits(logits, np.zeros(40))))
+    assert not np.any(np.isneginf(logits))  # the input is not modified
