@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch first: libfm.so then binds to the HIP runtime torch has loaded (same
+# soname), so torch's streams and device pointers are valid in libfm.  Loaded
+# the other way round, the process holds two HIP runtimes and libfm's finds
+# no device.
+import torch  # noqa: F401
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfm.so")
 
@@ -115,7 +121,6 @@ def ptr(t) -> int | None:
 
 
 def current_stream() -> int:
-    import torch
     return torch.cuda.current_stream().cuda_stream
 
 

@@ -77,3 +77,15 @@ def test_create_rejects_bad_config_before_touching_the_device():
     assert "null weight" in _lib.last_error()
     assert _lib.LIB.fm_create(None, ctypes.byref(w), 8, 1024, ctypes.byref(out)) == _lib.FM_EINVAL
     assert out.value is None
+
+
+def test_binding_loads_torch_before_libfm():
+    """libfm.so must bind to torch's HIP runtime: the binding imports torch
+    before it loads the library (checked in a fresh interpreter)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import sparse_attention_chunk_amd._lib as L; "
+            "import sys as s; print('torch' in s.modules)" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-500:]
+    assert out.stdout.strip().endswith("True")

@@ -92,3 +92,17 @@ def test_create_unsupported_and_bad_sizes(env):
     assert L.LIB.fm_create(ctypes.byref(cfg), ctypes.byref(w), 4, 10, ctypes.byref(out)) == L.FM_EUNSUPPORTED
     assert out.value is None
     np.testing.assert_equal(L.FM_OK, 0)
+
+
+def test_package_imported_before_torch_creates_a_context():
+    """Importing the package before torch still gives libfm a device (the
+    binding loads torch's HIP runtime first)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r); import sparse_attention_chunk_amd as fm; import synth; "
+            "r = fm.FlashMemoryRetriever(fm.weights_to_device(synth.make_weights()), max_batch=1, max_n=16); "
+            "r.close(); print('ok')" % root)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-800:]
