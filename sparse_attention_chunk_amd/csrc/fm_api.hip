@@ -214,7 +214,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
   e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = init_select_topk_subset(dev, &ctx->ws.subset_lds);
+  if (e == hipSuccess) e = init_select_topk_subset();
   if (e == hipSuccess) e = launch_pack_weights(*weights, ctx->ws, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -310,7 +310,7 @@ fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int
   if (!aligned(scores, 4) || !aligned(subset, 4) || !aligned(n_subset, 4) || !aligned(out, 4) || !aligned(n_out, 4))
     return fail(FM_EINVAL, "scores, subset, n_subset, out, n_out must be 4-byte aligned");
   hipError_t e = fm::launch_select_topk_subset(scores, B, N, subset, n_subset, cap, top_k, out, n_out,
-                                               ctx->ws.subset_lds, (hipStream_t)stream);
+                                               (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fm_select_topk_subset launch");
   return FM_OK;
 }

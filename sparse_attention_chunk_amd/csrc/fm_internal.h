@@ -86,7 +86,6 @@ struct Workspace {
   void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
   uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
-  size_t subset_lds = 0;         // dynamic LDS available to the subset top-K kernel
 };
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
@@ -113,12 +112,12 @@ hipError_t launch_score_plan(const Workspace& ws, const int32_t* valid_n, int B,
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream);
 
-// Subset top-K: the dynamic LDS limit of the in-LDS variant is set once per
-// device (init) and passed to every launch.
-hipError_t init_select_topk_subset(int device, size_t* max_dynamic_lds);
+// Subset top-K: init raises the LDS limit of the in-LDS variant (once, at
+// context creation).
+hipError_t init_select_topk_subset();
 hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, const int32_t* subset,
                                      const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out,
-                                     int32_t* n_out, size_t max_dynamic_lds, hipStream_t stream);
+                                     int32_t* n_out, hipStream_t stream);
 
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream);

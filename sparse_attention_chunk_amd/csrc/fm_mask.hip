@@ -6,19 +6,22 @@
 //
 // logits [B][R][N] (R logit rows per request row: heads, query positions)
 // are changed in place: -inf where mask[b][n] == 0, untouched elsewhere.
-// grid = (ceil(N / 4096), B), 256 threads; thread t covers 16 consecutive
-// chunks of its slice for every one of the row's R logit rows.  Per group of
-// 16 chunks: all kept -> nothing; none kept -> one vector store of -inf (no
-// read); mixed -> load, select, store.  Unaligned rows and the row tail use
-// element stores.
+// Stores are the cost, and they stream fastest as long contiguous runs per
+// block: a block takes one segment of kMaskVecs x 256 16-byte vectors of a
+// request row's chunks and kMaskRows of its logit rows; instruction i of
+// thread t handles vector i * 256 + t, so every store instruction of a block
+// covers 4 KB.  The mask bits of the segment are read once per block.  Per
+// vector: all kept -> nothing; none kept -> a store of -inf, no read; mixed
+// -> load, select, store, with the loads of a logit row issued together.  Rows whose length is not a whole number of
+// vectors use element stores.
 #include "fm_internal.h"
 
 namespace fm {
 namespace {
 
 constexpr int kMaskThreads = 256;
-constexpr int kMaskPer = 16;
-constexpr int kMaskSlice = kMaskThreads * kMaskPer;
+constexpr int kMaskVecs = 8;   // 16-byte vectors per thread per logit row
+constexpr int kMaskRows = 8;   // logit rows per block
 
 template <typename E>
 struct Elem;
@@ -33,58 +36,77 @@ struct Elem<uint16_t> {  // bf16
   typedef uint16_t Bits;
 };
 
-__device__ __forceinline__ uint32_t kept_bits16(const uint8_t* m, int bytes) {
-  if (bytes == kMaskPer && (((uintptr_t)m) & 15) == 0) {
-    const uint4 w = *(const uint4*)m;
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
-    uint32_t bits = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t hi = (((a[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | a[q]) & 0x80808080u;  // byte != 0
-      bits |= ((hi >> 7) & 1u) << (4 * q);
-      bits |= ((hi >> 15) & 1u) << (4 * q + 1);
-      bits |= ((hi >> 23) & 1u) << (4 * q + 2);
-      bits |= ((hi >> 31) & 1u) << (4 * q + 3);
-    }
-    return bits;
+// Bit j: mask byte j of the V bytes at m is non-zero.
+template <int V>
+__device__ __forceinline__ uint32_t kept_bits(const uint8_t* m) {
+  uint32_t w[2];
+  if constexpr (V == 8) {
+    const uint2 x = *(const uint2*)m;
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    w[0] = *(const uint32_t*)m;
+    w[1] = 0;
   }
   uint32_t bits = 0;
-  for (int j = 0; j < bytes; ++j) bits |= (m[j] != 0 ? 1u : 0u) << j;
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q) {
+    const uint32_t hi = (((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q]) & 0x80808080u;  // byte != 0
+    bits |= ((hi >> 7) & 1u) << (4 * q);
+    bits |= ((hi >> 15) & 1u) << (4 * q + 1);
+    bits |= ((hi >> 23) & 1u) << (4 * q + 2);
+    bits |= ((hi >> 31) & 1u) << (4 * q + 3);
+  }
   return bits;
 }
 
-template <typename E>
+// grid = (segments, row groups of kMaskRows, B).  VEC: every row holds a
+// whole number of vectors and the buffers are aligned (N % V == 0).
+template <typename E, bool VEC>
 __global__ __launch_bounds__(kMaskThreads) void mask_logits_kernel(E* __restrict__ logits, int R, int64_t N,
                                                                    const uint8_t* __restrict__ mask) {
   typedef typename Elem<E>::Bits Bits;
-  constexpr int kVec = 16 / sizeof(E);  // elements per 16-byte vector
-  const int b = blockIdx.y;
-  const int64_t n0 = (int64_t)blockIdx.x * kMaskSlice + (int64_t)threadIdx.x * kMaskPer;
-  if (n0 >= N) return;
-  const int cnt = N - n0 >= kMaskPer ? kMaskPer : (int)(N - n0);
-  const uint32_t kept = kept_bits16(mask + (size_t)b * N + n0, cnt);
-  const uint32_t all = (1u << cnt) - 1u;
-  if (kept == all) return;  // nothing to mask in any of the R rows
+  constexpr int V = 16 / sizeof(E);  // elements per vector
+  constexpr int64_t kSeg = (int64_t)kMaskThreads * kMaskVecs * V;
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * kMaskRows;
+  const int r1 = r0 + kMaskRows < R ? r0 + kMaskRows : R;
+  const int64_t e0 = (int64_t)blockIdx.x * kSeg;
+  const uint8_t* mrow = mask + (size_t)b * N;
   const Bits ninf = (Bits)Elem<E>::kNegInf;
-  for (int r = 0; r < R; ++r) {
-    Bits* p = (Bits*)(logits + ((size_t)b * R + r) * (size_t)N + n0);
-    if (cnt == kMaskPer && (((uintptr_t)p) & 15) == 0) {
-      uint4 v[kMaskPer / kVec];
-      if (kept != 0) {
+  if constexpr (VEC) {
+    uint32_t kept[kMaskVecs];
+    const uint32_t all = (1u << V) - 1u;
 #pragma unroll
-        for (int q = 0; q < kMaskPer / kVec; ++q) v[q] = ((const uint4*)p)[q];
+    for (int i = 0; i < kMaskVecs; ++i) {
+      const int64_t e = e0 + ((int64_t)i * kMaskThreads + threadIdx.x) * V;
+      kept[i] = e < N ? kept_bits<V>(mrow + e) : all;  // past the row: nothing to do
+    }
+    for (int r = r0; r < r1; ++r) {
+      uint4* p = (uint4*)(logits + ((size_t)b * R + r) * (size_t)N + e0) + threadIdx.x;
+      // The reads of the row's mixed vectors first, so the row waits for
+      // memory once, not once per vector.
+      uint4 v[kMaskVecs];
+#pragma unroll
+      for (int i = 0; i < kMaskVecs; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (kept[i] != 0 && kept[i] != all) v[i] = p[(size_t)i * kMaskThreads];
       }
 #pragma unroll
-      for (int q = 0; q < kMaskPer / kVec; ++q) {
-        Bits* e = (Bits*)&v[q];
+      for (int i = 0; i < kMaskVecs; ++i) {
+        if (kept[i] == all) continue;
+        Bits* el = (Bits*)&v[i];
 #pragma unroll
-        for (int i = 0; i < kVec; ++i)
-          if (!((kept >> (q * kVec + i)) & 1u)) e[i] = ninf;
-        ((uint4*)p)[q] = v[q];
+        for (int j = 0; j < V; ++j)
+          if (!((kept[i] >> j) & 1u)) el[j] = ninf;
+        p[(size_t)i * kMaskThreads] = v[i];
       }
-    } else {
-      for (int j = 0; j < cnt; ++j)
-        if (!((kept >> j) & 1u)) p[j] = ninf;
+    }
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      Bits* p = (Bits*)(logits + ((size_t)b * R + r) * (size_t)N);
+      for (int64_t e = e0 + threadIdx.x; e < e0 + kSeg && e < N; e += kMaskThreads)
+        if (mrow[e] == 0) p[e] = ninf;
     }
   }
 }
@@ -93,12 +115,25 @@ __global__ __launch_bounds__(kMaskThreads) void mask_logits_kernel(E* __restrict
 
 hipError_t launch_mask_logits(void* logits, int dtype, int B, int R, int64_t N, const uint8_t* mask,
                               hipStream_t stream) {
-  const dim3 grid((unsigned)((N + kMaskSlice - 1) / kMaskSlice), (unsigned)B);
-  if (dtype == FM_DTYPE_BF16)
-    hipLaunchKernelGGL(mask_logits_kernel<uint16_t>, grid, dim3(kMaskThreads), 0, stream, (uint16_t*)logits, R, N,
-                       mask);
-  else
-    hipLaunchKernelGGL(mask_logits_kernel<float>, grid, dim3(kMaskThreads), 0, stream, (float*)logits, R, N, mask);
+  const int V = dtype == FM_DTYPE_BF16 ? 8 : 4;
+  const int64_t seg = (int64_t)kMaskThreads * kMaskVecs * V;
+  const dim3 grid((unsigned)((N + seg - 1) / seg), (unsigned)((R + kMaskRows - 1) / kMaskRows), (unsigned)B);
+  const bool vec = N % V == 0 && ((uintptr_t)logits & 15) == 0 && ((uintptr_t)mask & 7) == 0;
+  if (dtype == FM_DTYPE_BF16) {
+    if (vec)
+      hipLaunchKernelGGL((mask_logits_kernel<uint16_t, true>), grid, dim3(kMaskThreads), 0, stream, (uint16_t*)logits,
+                         R, N, mask);
+    else
+      hipLaunchKernelGGL((mask_logits_kernel<uint16_t, false>), grid, dim3(kMaskThreads), 0, stream,
+                         (uint16_t*)logits, R, N, mask);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((mask_logits_kernel<float, true>), grid, dim3(kMaskThreads), 0, stream, (float*)logits, R, N,
+                         mask);
+    else
+      hipLaunchKernelGGL((mask_logits_kernel<float, false>), grid, dim3(kMaskThreads), 0, stream, (float*)logits, R,
+                         N, mask);
+  }
   return hipGetLastError();
 }
 

@@ -9,14 +9,17 @@
 // as chunk indices in list order.  Entries outside [0, N) are never chosen.
 //
 // One block of 1024 threads per row; position p of the list is handled by
-// thread p mod 1024 (coalesced list reads).  The keys (order-preserving
-// uint32 of the gathered scores) and a validity bitmap are kept in LDS when
-// the list fits, else every pass gathers them again.  An exact radix
-// selection gives the k-th largest key T and the last position kept among
-// the keys equal to T.  The chosen entries are then written in list order:
-// per round of 1024 positions each wave ballots its 64, the counts of all
-// (round, wave) pairs are scanned once, and each entry lands at its wave's
-// offset plus the chosen lanes below it.
+// thread p mod 1024 (coalesced list reads), in rounds of 1024 positions.
+// Lists of up to 32 rounds gather their keys (order-preserving uint32 of the
+// scores) once, every load in flight together, into LDS with a validity
+// bitmap; longer lists gather them again in every pass, eight rounds of
+// loads at a time.  An exact radix selection gives the k-th largest key T
+// and the last position kept among the keys equal to T.  The chosen entries
+// are then written in list order: per round each wave ballots its 64
+// positions, the counts of all (round, wave) pairs are scanned once, each
+// chosen position is written at its wave's offset plus the chosen lanes
+// below it, and a last pass replaces every written position by its chunk
+// index.
 #include "fm_radix.h"
 
 namespace fm {
@@ -47,8 +50,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return below + incl - v;
 }
 
-// LDS: keys and validity in dynamic LDS (4 cap bytes of keys, then the
-// bitmap, 128 bytes per round of 1024 positions, as the launch sizes it).
+constexpr int kSubLdsRounds = 32;  // lists of up to 32 x 1024 entries keep their keys in LDS
+constexpr int kSubBatch = 8;        // rounds of loads in flight in the gathering variant
+constexpr size_t kSubLdsBytes = (size_t)kSubLdsRounds * kSubThreads * 4 + kSubLdsRounds * kSubWaves * 8;
+
+__device__ __forceinline__ bool in_range(int32_t i, int64_t N) { return i >= 0 && (int64_t)i < N; }
+
+// LDS: the list has at most kSubLdsRounds rounds; keys and the validity
+// bitmap (bit p % 32 of word p / 32) live in dynamic LDS (kSubLdsBytes).
 template <bool LDS>
 __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __restrict__ scores, int64_t N,
                                                                  const int32_t* __restrict__ subset,
@@ -68,57 +77,74 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
   const uint32_t rounds = (n + kSubThreads - 1) / kSubThreads;
   const int32_t* srow = subset + (size_t)b * cap;
   const float* row = scores + (size_t)b * N;
-  uint32_t* s_valid = s_keys + (LDS ? (size_t)cap : 0);  // bit p % 32 of word p / 32
+  uint32_t* s_valid = s_keys + (size_t)kSubLdsRounds * kSubThreads;
 
-  // The chunk index at position p, when it is in [0, N), and its key.
-  auto gather = [&](uint32_t p, uint32_t& key) -> bool {
-    const int32_t i = srow[p];
-    if (i < 0 || (int64_t)i >= N) return false;
-    key = order_key(row[i]);
-    return true;
-  };
   uint32_t nvalid = 0;
   if constexpr (LDS) {
-    // Eight rounds of loads in flight per thread.
-    for (uint32_t j0 = 0; j0 < rounds; j0 += 8) {
-      int32_t idx[8];
+    // Every load in flight before the first use, through range-checked
+    // buffer views: reads past the list or the row return 0, no branch.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, (int)(4 * n), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)row, 0, (int)(N < 0x20000000 ? 4 * N : 0x7fffffff), 0x00020000);
+    int32_t idx[kSubLdsRounds];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t p = (j0 + u) * kSubThreads + t;
-        idx[u] = p < n ? srow[p] : -1;
-      }
-      float v[8];
+    for (int j = 0; j < kSubLdsRounds; ++j)
+      idx[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * ((uint32_t)j * kSubThreads + t), 0, 0);
+    uint32_t v[kSubLdsRounds];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (idx[u] >= 0 && (int64_t)idx[u] < N) ? row[idx[u]] : 0.f;
+    for (int j = 0; j < kSubLdsRounds; ++j) {
+      const uint32_t p = (uint32_t)j * kSubThreads + t;
+      if (!(p < n && in_range(idx[j], N))) idx[j] = -1;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, idx[j] >= 0 ? 4u * (uint32_t)idx[j] : 0x80000000u, 0, 0);
+    }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t p = (j0 + u) * kSubThreads + t;
-        const bool ok = idx[u] >= 0 && (int64_t)idx[u] < N;
+    for (int j = 0; j < kSubLdsRounds; ++j) {
+      if ((uint32_t)j < rounds) {
+        const bool ok = idx[j] >= 0;
         const uint64_t m = __ballot(ok);
-        if (p < n) s_keys[p] = order_key(v[u]);
-        const uint32_t w0 = ((j0 + u) * kSubThreads + 64 * wave) / 32;  // this wave's 64 positions
-        if ((j0 + u) < rounds && lane < 2) s_valid[w0 + lane] = (uint32_t)(m >> (32 * lane));
+        s_keys[(uint32_t)j * kSubThreads + t] = order_key(__uint_as_float(v[j]));
+        if (lane < 2) s_valid[j * 2 * kSubWaves + 2 * wave + lane] = (uint32_t)(m >> (32 * lane));
         nvalid += ok ? 1u : 0u;
       }
     }
     __syncthreads();
   } else {
-    for (uint32_t p = t; p < n; p += kSubThreads) {
-      const int32_t i = srow[p];
-      nvalid += (i >= 0 && (int64_t)i < N) ? 1u : 0u;
-    }
+    for (uint32_t p = t; p < n; p += kSubThreads) nvalid += in_range(srow[p], N) ? 1u : 0u;
   }
-  // (key, position) of every valid entry of this thread.
-  auto each = [&](auto f) {
-    for (uint32_t p = t; p < n; p += kSubThreads) {
-      if constexpr (LDS) {
-        if ((s_valid[p >> 5] >> (p & 31)) & 1u) f(make_uint2(s_keys[p], p));
-      } else {
-        uint32_t key;
-        if (gather(p, key)) f(make_uint2(key, p));
+  // fn(key, position) for each of this thread's valid entries.
+  auto each_entry = [&](auto fn) {
+    if constexpr (LDS) {
+      for (uint32_t j0 = 0; j0 < rounds; j0 += 4) {
+        uint32_t kk[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t p = (j0 + u) * kSubThreads + t;
+          ok[u] = j0 + u < rounds && ((s_valid[p >> 5] >> (p & 31)) & 1u);
+          kk[u] = s_keys[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (ok[u]) fn(kk[u], (j0 + u) * kSubThreads + t);
+      }
+    } else {
+      for (uint32_t j0 = 0; j0 < rounds; j0 += kSubBatch) {
+        int32_t bi[kSubBatch];
+        float bv[kSubBatch];
+#pragma unroll
+        for (int u = 0; u < kSubBatch; ++u) {
+          const uint32_t p = (j0 + u) * kSubThreads + t;
+          bi[u] = p < n ? srow[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSubBatch; ++u) bv[u] = in_range(bi[u], N) ? row[bi[u]] : 0.f;
+#pragma unroll
+        for (int u = 0; u < kSubBatch; ++u)
+          if (in_range(bi[u], N)) fn(order_key(bv[u]), (j0 + u) * kSubThreads + t);
       }
     }
   };
+  auto each = [&](auto f) { each_entry([&](uint32_t k, uint32_t p) { f(make_uint2(k, p)); }); };
 
   uint32_t V;
   (void)block_exclusive_scan(nvalid, s_wtot, &V);
@@ -127,25 +153,22 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
   if (k == 0) return;
   uint32_t T = 0, last = 0xffffffffu;  // k == V: every valid entry is chosen
   if (k < V) radix_select<kSubThreads>(each, k, index_bits((int64_t)n), h, s_wtot, s_out, &T, &last);
+  auto chosen = [&](uint32_t key, uint32_t p) { return key > T || (key == T && p <= last); };
 
-  auto chosen_at = [&](uint32_t p) -> bool {
-    if (p >= n) return false;
-    uint32_t key;
-    if constexpr (LDS) {
-      if (!((s_valid[p >> 5] >> (p & 31)) & 1u)) return false;
-      key = s_keys[p];
-    } else {
-      if (!gather(p, key)) return false;
-    }
-    return key > T || (key == T && p <= last);
-  };
+  // Chosen positions in list order, in groups of kSubGroupRounds rounds:
+  // out[slot] = position first, the chunk index after.
   int32_t* orow = out + (size_t)b * top_k;
   const uint64_t below_me = (1ull << lane) - 1ull;
   uint32_t base = 0;
   for (uint32_t g0 = 0; g0 < rounds; g0 += kSubGroupRounds) {
     const uint32_t gr = rounds - g0 < (uint32_t)kSubGroupRounds ? rounds - g0 : (uint32_t)kSubGroupRounds;
+    uint64_t mine = 0;  // bit j: this thread's entry of round g0 + j is chosen
+    each_entry([&](uint32_t key, uint32_t p) {
+      const uint32_t j = p / kSubThreads - g0;
+      if (j < gr && chosen(key, p)) mine |= 1ull << j;
+    });
     for (uint32_t j = 0; j < gr; ++j) {
-      const uint64_t m = __ballot(chosen_at((g0 + j) * kSubThreads + t));
+      const uint64_t m = __ballot((mine >> j) & 1ull);
       if (lane == 0) s_cnt[j * kSubWaves + wave] = (uint32_t)__popcll(m);
     }
     __syncthreads();
@@ -155,42 +178,30 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
     if ((uint32_t)t < gr * kSubWaves) s_cnt[t] = off;
     __syncthreads();
     for (uint32_t j = 0; j < gr; ++j) {
-      const uint32_t p = (g0 + j) * kSubThreads + t;
-      const bool c = chosen_at(p);
-      const uint64_t m = __ballot(c);
-      if (c) orow[base + s_cnt[j * kSubWaves + wave] + (uint32_t)__popcll(m & below_me)] = srow[p];
+      const bool cj = (mine >> j) & 1ull;
+      const uint64_t m = __ballot(cj);
+      if (cj) orow[base + s_cnt[j * kSubWaves + wave] + (uint32_t)__popcll(m & below_me)] =
+          (int32_t)((g0 + j) * kSubThreads + t);
     }
     base += tot;
-    __syncthreads();  // s_cnt is rewritten by the next group
+    __syncthreads();  // s_cnt is rewritten by the next group; the positions are visible to the block
   }
+  for (uint32_t s_ = t; s_ < k; s_ += kSubThreads) orow[s_] = srow[orow[s_]];
 }
 
 }  // namespace
 
-// Static LDS of the kernel (histograms, scan and compaction scratch, and the
-// radix selection's own) kept out of the dynamic budget.
-constexpr size_t kSubStaticLds = 24 * 1024;
-
-// Keys (4 B per entry) and the bitmap, in whole rounds of 1024 positions.
-size_t subset_lds_bytes(int32_t cap) { return 4 * (size_t)cap + 4 * 32 * (((size_t)cap + kSubThreads - 1) / kSubThreads); }
-
-hipError_t init_select_topk_subset(int device, size_t* max_dynamic_lds) {
-  int lds = 0;
-  hipError_t e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
-  if (e != hipSuccess) return e;
-  const size_t dyn = (size_t)lds > kSubStaticLds ? (size_t)lds - kSubStaticLds : 0;
-  *max_dynamic_lds = dyn;
+hipError_t init_select_topk_subset() {
   return hipFuncSetAttribute((const void*)sel_subset_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)dyn);
+                             (int)kSubLdsBytes);
 }
 
 hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, const int32_t* subset,
                                      const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out,
-                                     int32_t* n_out, size_t max_dynamic_lds, hipStream_t stream) {
-  const size_t lds = subset_lds_bytes(cap);
-  if (lds <= max_dynamic_lds)
-    hipLaunchKernelGGL(sel_subset_kernel<true>, dim3(B), dim3(kSubThreads), lds, stream, scores, N, subset, n_subset,
-                       cap, top_k, out, n_out);
+                                     int32_t* n_out, hipStream_t stream) {
+  if (cap <= kSubLdsRounds * kSubThreads)
+    hipLaunchKernelGGL(sel_subset_kernel<true>, dim3(B), dim3(kSubThreads), kSubLdsBytes, stream, scores, N, subset,
+                       n_subset, cap, top_k, out, n_out);
   else
     hipLaunchKernelGGL(sel_subset_kernel<false>, dim3(B), dim3(kSubThreads), 0, stream, scores, N, subset, n_subset,
                        cap, top_k, out, n_out);
