@@ -236,7 +236,7 @@ def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
     """fm_mask_logits: this step's top-512 keep mask applied to bf16 attention
     logits [B, 64 heads, N] in place (synthetic values).  HIP-event time per
     call on the launch stream; algorithmic bytes per call = the mask, plus per
-    (row, head) 16-chunk group: nothing when all 16 chunks are kept, one
+    (row, head) 16-byte vector of 8 chunks: nothing when all are kept, one
     write when none is, a read and a write when some are."""
     import numpy as np
     import torch
@@ -258,10 +258,11 @@ def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
     m = mask.cpu().numpy().astype(bool)
-    full = (N // 16) * 16
-    g = m[:, :full].reshape(B, -1, 16).sum(axis=2)
-    none_kept, mixed = int((g == 0).sum()), int(((g > 0) & (g < 16)).sum())
-    nbytes = B * N + heads * 2 * 16 * (none_kept + 2 * mixed)
+    V = 8  # bf16 chunks per 16-byte vector
+    full = (N // V) * V
+    g = m[:, :full].reshape(B, -1, V).sum(axis=2)
+    none_kept, mixed = int((g == 0).sum()), int(((g > 0) & (g < V)).sum())
+    nbytes = B * N + heads * 16 * (none_kept + 2 * mixed)
     del logits
     return {"us": t * 1e6, "heads": heads, "dtype": "bf16", "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9,
             "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS}
