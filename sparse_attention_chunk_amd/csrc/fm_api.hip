@@ -208,6 +208,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.score_blocks = cus;
   ctx->ws.sel_state = (uint32_t*)(p + offs[kSelState]);
   ctx->ws.sel_cand = (void*)(p + offs[kSelCand]);
+  ctx->ws.sel_cand_bytes = sizes[kSelCand];
   ctx->ws.sel_count = (uint32_t*)(p + offs[kSelCount]);
   ctx->ws.res_count = (uint32_t*)(p + offs[kResCount]);
 
@@ -309,7 +310,7 @@ fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int
     return fail(FM_EINVAL, "null pointer to fm_select_topk_subset");
   if (!aligned(scores, 4) || !aligned(subset, 4) || !aligned(n_subset, 4) || !aligned(out, 4) || !aligned(n_out, 4))
     return fail(FM_EINVAL, "scores, subset, n_subset, out, n_out must be 4-byte aligned");
-  hipError_t e = fm::launch_select_topk_subset(scores, B, N, subset, n_subset, cap, top_k, out, n_out,
+  hipError_t e = fm::launch_select_topk_subset(ctx->ws, scores, B, N, subset, n_subset, cap, top_k, out, n_out,
                                                (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fm_select_topk_subset launch");
   return FM_OK;

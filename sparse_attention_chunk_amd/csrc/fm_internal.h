@@ -84,6 +84,8 @@ struct Workspace {
   int score_blocks = 0;          // compute units of the device
   uint32_t* sel_state = nullptr; // [max_batch][4]
   void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
+                                 // (the subset top-K stages its gathered keys here too)
+  size_t sel_cand_bytes = 0;
   uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
 };
@@ -115,9 +117,9 @@ hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, i
 // Subset top-K: init raises the LDS limit of the in-LDS variant (once, at
 // context creation).
 hipError_t init_select_topk_subset();
-hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, const int32_t* subset,
-                                     const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out,
-                                     int32_t* n_out, hipStream_t stream);
+hipError_t launch_select_topk_subset(const Workspace& ws, const float* scores, int B, int64_t N,
+                                     const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
+                                     int32_t* out, int32_t* n_out, hipStream_t stream);
 
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream);

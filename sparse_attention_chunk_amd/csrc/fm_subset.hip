@@ -56,14 +56,197 @@ constexpr size_t kSubLdsBytes = (size_t)kSubLdsRounds * kSubThreads * 4 + kSubLd
 
 __device__ __forceinline__ bool in_range(int32_t i, int64_t N) { return i >= 0 && (int64_t)i < N; }
 
+// Keys of a list held in LDS, gathered beforehand by many blocks (the
+// gathers are random reads, which one block per row issues too slowly):
+// per row, kSubLdsRounds x 1024 keys then the validity bitmap (32 words per
+// round), in the top-K candidate workspace.
+constexpr size_t kSubPreRow = (size_t)kSubLdsRounds * kSubThreads + (size_t)kSubLdsRounds * 2 * kSubWaves;
+
+// grid = (rounds, B), 256 threads: round r of row b, positions r 1024 + 256 u
+// + t (u = 0..3).  Writes each position's key and the round's bitmap words.
+__global__ __launch_bounds__(256) void sub_gather_kernel(const float* __restrict__ scores, int64_t N,
+                                                         const int32_t* __restrict__ subset,
+                                                         const int32_t* __restrict__ n_subset, int32_t cap,
+                                                         uint32_t* __restrict__ pre) {
+  const int b = blockIdx.y;
+  const uint32_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t n64 = n_subset ? (int64_t)n_subset[b] : (int64_t)cap;
+  const uint32_t n = (uint32_t)(n64 < 0 ? 0 : (n64 > cap ? cap : n64));
+  if (r * kSubThreads >= n) return;
+  const int32_t* srow = subset + (size_t)b * cap;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, (int)(4 * n), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scores + (size_t)b * N), 0, (int)(N < 0x20000000 ? 4 * N : 0x7fffffff), 0x00020000);
+  uint32_t* keys = pre + (size_t)b * kSubPreRow;
+  uint32_t* bits = keys + (size_t)kSubLdsRounds * kSubThreads;
+  int32_t idx[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) idx[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (r * kSubThreads + 256 * u + t), 0, 0);
+  uint32_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t p = r * kSubThreads + 256 * u + t;
+    if (!(p < n && in_range(idx[u], N))) idx[u] = -1;
+    v[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, idx[u] >= 0 ? 4u * (uint32_t)idx[u] : 0x80000000u, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t p = r * kSubThreads + 256 * u + t;
+    keys[p] = order_key(__uint_as_float(v[u]));
+    const uint64_t m = __ballot(idx[u] >= 0);
+    if (lane < 2) bits[(p - lane) / 32 + lane] = (uint32_t)(m >> (32 * lane));  // words of this wave's 64 positions
+  }
+}
+
+constexpr uint32_t kSubSample = 4096;      // sampled keys for the cut-off
+constexpr uint32_t kSubCandMax = 16384;    // candidates compacted into the first half of the key area
+
+// The selection of a long list held in LDS, narrowed by a sample (as the row
+// top-K does): the m-th largest of 4096 evenly spaced valid keys gives a
+// cut-off L with m chosen so that about k plus four standard deviations of
+// the list's keys are expected at or above L.  One pass over the list keeps
+// the keys >= L in registers, counts them per (round, wave), and compacts
+// them, in list order, into the first half of the key area (keys) and the
+// second half (positions).  The exact radix selection then runs over these
+// candidates only, and their chosen ones are written in list order.  Returns
+// false, with LDS untouched, when the candidates are fewer than k or too
+// many; the caller then selects over the whole list.
+__device__ bool sampled_select(uint32_t* s_keys, const uint32_t* s_valid, uint32_t n, uint32_t rounds, uint32_t V,
+                               uint32_t k, const int32_t* srow, int32_t* orow, uint32_t* h, uint32_t* s_wtot,
+                               uint32_t* s_out, uint32_t* s_cnt) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  auto valid_at = [&](uint32_t p) { return (s_valid[p >> 5] >> (p & 31)) & 1u; };
+
+  // 1. Cut-off from the sample (sample i at position i n / 4096).
+  constexpr int kPer = kSubSample / kSubThreads;
+  uint32_t sk[kPer];
+  uint32_t sv = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const uint32_t i = (uint32_t)t + kSubThreads * u;
+    const uint32_t p = (uint32_t)(((uint64_t)i * n) / kSubSample);
+    sk[u] = s_keys[p];
+    sv |= valid_at(p) << u;
+  }
+  uint32_t S;
+  (void)block_exclusive_scan((uint32_t)__popc(sv), s_wtot, &S);
+  if (S == 0) return false;
+  const double expect = (double)k * (double)S / (double)V;
+  const double mm = ceil(expect + 4.0 * sqrt(expect) + 16.0);
+  const uint32_t m = mm >= (double)S ? S : (uint32_t)mm;
+  uint32_t L, unused;
+  radix_select<kSubThreads, false>(
+      [&](auto f) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          if ((sv >> u) & 1u) f(make_uint2(sk[u], (uint32_t)t + kSubThreads * u));
+      },
+      m, 0, h, s_wtot, s_out, &L, &unused);
+
+  // 2. Candidates (keys >= L) of this thread, in registers; counts per
+  // (round, wave), then their offsets in list order.
+  uint32_t ck[kSubLdsRounds];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kSubLdsRounds; ++j) {
+    const uint32_t p = (uint32_t)j * kSubThreads + t;
+    ck[j] = s_keys[p];
+    const bool c = (uint32_t)j < rounds && p < n && valid_at(p) && ck[j] >= L;
+    mine |= (uint32_t)c << j;
+  }
+  // Lane j of each wave keeps the wave's count (later its offset) of round j.
+  uint32_t lane_cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kSubLdsRounds; ++j) {
+    if ((uint32_t)j < rounds) {
+      const uint32_t c = (uint32_t)__popcll(__ballot((mine >> j) & 1u));
+      lane_cnt = lane == j ? c : lane_cnt;
+    }
+  }
+  if ((uint32_t)lane < rounds) s_cnt[lane * kSubWaves + wave] = lane_cnt;
+  __syncthreads();
+  const uint32_t nc = rounds * kSubWaves;  // at most 512 (round, wave) pairs
+  const uint32_t cnt = (uint32_t)t < nc ? s_cnt[t] : 0u;
+  uint32_t C;
+  const uint32_t off = block_exclusive_scan(cnt, s_wtot, &C);
+  if (C < k || C > kSubCandMax) return false;  // block-uniform; LDS keys untouched
+  if ((uint32_t)t < nc) s_cnt[t] = off;
+  __syncthreads();
+  const uint32_t lane_off = (uint32_t)lane < rounds ? s_cnt[lane * kSubWaves + wave] : 0u;
+  uint32_t* c_key = s_keys;
+  uint32_t* c_pos = s_keys + kSubCandMax;
+#pragma unroll
+  for (int j = 0; j < kSubLdsRounds; ++j) {
+    if ((uint32_t)j < rounds) {
+      const bool c = (mine >> j) & 1u;
+      const uint64_t bm = __ballot(c);
+      const uint32_t base = __builtin_amdgcn_readlane(lane_off, j);
+      if (c) {
+        const uint32_t slot = base + (uint32_t)__popcll(bm & below_me);
+        c_key[slot] = ck[j];
+        c_pos[slot] = (uint32_t)j * kSubThreads + t;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. Exact selection over the candidates (ties by list position).
+  auto cand_each = [&](auto f) {
+    for (uint32_t sl = t; sl < C; sl += kSubThreads) f(make_uint2(c_key[sl], c_pos[sl]));
+  };
+  uint32_t T, last;
+  radix_select<kSubThreads>(cand_each, k, index_bits((int64_t)n), h, s_wtot, s_out, &T, &last);
+
+  // 4. The chosen candidates in slot (= list) order: positions first, then
+  // chunk indices.
+  const uint32_t crounds = (C + kSubThreads - 1) / kSubThreads;  // at most 16
+  uint32_t cm = 0, lane_cnt2 = 0;
+  for (uint32_t u = 0; u < crounds; ++u) {
+    const uint32_t sl = u * kSubThreads + t;
+    bool c = false;
+    if (sl < C) {
+      const uint32_t key = c_key[sl], pos = c_pos[sl];
+      c = key > T || (key == T && pos <= last);
+    }
+    cm |= (uint32_t)c << u;
+    const uint32_t cu = (uint32_t)__popcll(__ballot(c));
+    lane_cnt2 = (uint32_t)lane == u ? cu : lane_cnt2;
+  }
+  if ((uint32_t)lane < crounds) s_cnt[lane * kSubWaves + wave] = lane_cnt2;
+  __syncthreads();
+  const uint32_t nc2 = crounds * kSubWaves;
+  const uint32_t cnt2 = (uint32_t)t < nc2 ? s_cnt[t] : 0u;
+  uint32_t tot;
+  const uint32_t off2 = block_exclusive_scan(cnt2, s_wtot, &tot);
+  if ((uint32_t)t < nc2) s_cnt[t] = off2;
+  __syncthreads();
+  const uint32_t lane_off2 = (uint32_t)lane < crounds ? s_cnt[lane * kSubWaves + wave] : 0u;
+  for (uint32_t u = 0; u < crounds; ++u) {
+    const bool c = (cm >> u) & 1u;
+    const uint64_t bm = __ballot(c);
+    const uint32_t base = __builtin_amdgcn_readlane(lane_off2, u);
+    if (c) orow[base + (uint32_t)__popcll(bm & below_me)] = (int32_t)c_pos[u * kSubThreads + t];
+  }
+  __syncthreads();  // the positions are visible to the block
+  for (uint32_t s_ = t; s_ < k; s_ += kSubThreads) orow[s_] = srow[orow[s_]];
+  return true;
+}
+
 // LDS: the list has at most kSubLdsRounds rounds; keys and the validity
 // bitmap (bit p % 32 of word p / 32) live in dynamic LDS (kSubLdsBytes).
-template <bool LDS>
+// PRE (with LDS): the keys and bitmap were gathered by sub_gather_kernel
+// into pre; they are copied to LDS with coalesced reads.
+template <bool LDS, bool PRE = false>
 __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __restrict__ scores, int64_t N,
                                                                  const int32_t* __restrict__ subset,
                                                                  const int32_t* __restrict__ n_subset, int32_t cap,
                                                                  int32_t top_k, int32_t* __restrict__ out,
-                                                                 int32_t* __restrict__ n_out) {
+                                                                 int32_t* __restrict__ n_out,
+                                                                 const uint32_t* __restrict__ pre) {
   extern __shared__ uint32_t s_keys[];
   __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
   __shared__ uint32_t s_wtot[kSubWaves];
@@ -80,7 +263,21 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
   uint32_t* s_valid = s_keys + (size_t)kSubLdsRounds * kSubThreads;
 
   uint32_t nvalid = 0;
-  if constexpr (LDS) {
+  if constexpr (LDS && PRE) {
+    const uint32_t* keys = pre + (size_t)b * kSubPreRow;
+    const uint32_t* bits = keys + (size_t)kSubLdsRounds * kSubThreads;
+    uint32_t v[kSubLdsRounds];
+#pragma unroll
+    for (int j = 0; j < kSubLdsRounds; ++j)
+      if ((uint32_t)j < rounds) v[j] = keys[(uint32_t)j * kSubThreads + t];
+    const uint32_t word = (uint32_t)t < rounds * 2 * kSubWaves ? bits[t] : 0u;
+#pragma unroll
+    for (int j = 0; j < kSubLdsRounds; ++j)
+      if ((uint32_t)j < rounds) s_keys[(uint32_t)j * kSubThreads + t] = v[j];
+    if ((uint32_t)t < rounds * 2 * kSubWaves) s_valid[t] = word;
+    nvalid = (uint32_t)__popc(word);
+    __syncthreads();
+  } else if constexpr (LDS) {
     // Every load in flight before the first use, through range-checked
     // buffer views: reads past the list or the row return 0, no branch.
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, (int)(4 * n), 0x00020000);
@@ -151,14 +348,19 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
   const uint32_t k = (uint32_t)top_k < V ? (uint32_t)top_k : V;
   if (t == 0) n_out[b] = (int32_t)k;
   if (k == 0) return;
+  int32_t* orow = out + (size_t)b * top_k;
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  if constexpr (LDS) {
+    if (k < V && n > 2 * kSubSample && sampled_select(s_keys, s_valid, n, rounds, V, k, srow, orow, h, s_wtot,
+                                                      s_out, s_cnt))
+      return;
+  }
   uint32_t T = 0, last = 0xffffffffu;  // k == V: every valid entry is chosen
   if (k < V) radix_select<kSubThreads>(each, k, index_bits((int64_t)n), h, s_wtot, s_out, &T, &last);
   auto chosen = [&](uint32_t key, uint32_t p) { return key > T || (key == T && p <= last); };
 
   // Chosen positions in list order, in groups of kSubGroupRounds rounds:
   // out[slot] = position first, the chunk index after.
-  int32_t* orow = out + (size_t)b * top_k;
-  const uint64_t below_me = (1ull << lane) - 1ull;
   uint32_t base = 0;
   for (uint32_t g0 = 0; g0 < rounds; g0 += kSubGroupRounds) {
     const uint32_t gr = rounds - g0 < (uint32_t)kSubGroupRounds ? rounds - g0 : (uint32_t)kSubGroupRounds;
@@ -192,19 +394,31 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
 }  // namespace
 
 hipError_t init_select_topk_subset() {
-  return hipFuncSetAttribute((const void*)sel_subset_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute((const void*)sel_subset_kernel<true, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSubLdsBytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)sel_subset_kernel<true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)kSubLdsBytes);
 }
 
-hipError_t launch_select_topk_subset(const float* scores, int B, int64_t N, const int32_t* subset,
-                                     const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out,
-                                     int32_t* n_out, hipStream_t stream) {
-  if (cap <= kSubLdsRounds * kSubThreads)
-    hipLaunchKernelGGL(sel_subset_kernel<true>, dim3(B), dim3(kSubThreads), kSubLdsBytes, stream, scores, N, subset,
-                       n_subset, cap, top_k, out, n_out);
-  else
-    hipLaunchKernelGGL(sel_subset_kernel<false>, dim3(B), dim3(kSubThreads), 0, stream, scores, N, subset, n_subset,
-                       cap, top_k, out, n_out);
+hipError_t launch_select_topk_subset(const Workspace& ws, const float* scores, int B, int64_t N,
+                                     const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
+                                     int32_t* out, int32_t* n_out, hipStream_t stream) {
+  if (cap <= kSubLdsRounds * kSubThreads) {
+    uint32_t* pre = (uint32_t*)ws.sel_cand;
+    if (B > 0 && cap > 0 && (size_t)B * kSubPreRow * 4 <= ws.sel_cand_bytes) {
+      const dim3 grid((unsigned)((cap + kSubThreads - 1) / kSubThreads), (unsigned)B);
+      hipLaunchKernelGGL(sub_gather_kernel, grid, dim3(256), 0, stream, scores, N, subset, n_subset, cap, pre);
+      hipLaunchKernelGGL((sel_subset_kernel<true, true>), dim3(B), dim3(kSubThreads), kSubLdsBytes, stream, scores, N,
+                         subset, n_subset, cap, top_k, out, n_out, (const uint32_t*)pre);
+    } else {
+      hipLaunchKernelGGL((sel_subset_kernel<true, false>), dim3(B), dim3(kSubThreads), kSubLdsBytes, stream, scores,
+                         N, subset, n_subset, cap, top_k, out, n_out, (const uint32_t*)nullptr);
+    }
+  } else {
+    hipLaunchKernelGGL((sel_subset_kernel<false, false>), dim3(B), dim3(kSubThreads), 0, stream, scores, N, subset,
+                       n_subset, cap, top_k, out, n_out, (const uint32_t*)nullptr);
+  }
   return hipGetLastError();
 }
 

@@ -78,6 +78,39 @@ def test_random_subsets_exact(retr, B, N, cap, order, bad):
     report(f"subset top-k B={B} N={N} cap={cap} {order}", rows=B)
 
 
+@pytest.mark.parametrize("levels,k", [(4, 512), (64, 512), (100000, 7000), (3, 20000)])
+def test_sampled_cutoff_paths(retr, levels, k):
+    """Long lists held in LDS take the sampled cut-off; heavy ties at the
+    cut-off (few distinct scores) overflow it and fall back to the whole
+    list.  Both must give the exact result."""
+    rng = np.random.default_rng(levels + k)
+    B, N, cap = 3, 262144, 32768
+    scores = (rng.integers(0, levels, (B, N)) / levels).astype(np.float32)
+    subset = np.stack([np.sort(rng.choice(N, cap, replace=False)) for _ in range(B)]).astype(np.int32)
+    n_sub = np.array([cap, 30001, 9000], np.int32)
+    check(retr, scores, subset, n_sub, k)
+
+
+def test_small_context_gathers_in_the_selecting_block():
+    """A context whose workspace cannot stage the gathered keys (small
+    max_n) gathers them in the selecting block instead; lists longer than N
+    (padded with out-of-range entries) still take the sampled cut-off."""
+    import sparse_attention_chunk_amd as fm
+    r = fm.FlashMemoryRetriever(fm.weights_to_device(synth.make_weights()), max_batch=4, max_n=8192)
+    try:
+        rng = np.random.default_rng(21)
+        B, N, cap = 3, 8000, 20000
+        scores = (rng.integers(0, 5000, (B, N)) / 5000.0).astype(np.float32)
+        subset = np.full((B, cap), -1, np.int32)
+        for b in range(B):
+            vals = np.concatenate([rng.permutation(N), rng.integers(N, 3 * N, cap - N)])
+            subset[b] = rng.permutation(vals)[:cap] if b else vals
+        for k in (1, 512, 6000):
+            check(r, scores, subset, np.array([cap, 15000, 9000], np.int32), k)
+    finally:
+        r.close()
+
+
 def test_without_counts_uses_cap(retr):
     scores, subset, n_sub = make_case(3, 2, 9000, 1200)
     subset[:, :] = np.stack([np.sort(np.random.default_rng(b).choice(9000, 1200, replace=False))
