@@ -218,17 +218,22 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// grid = (outputs / 64, layers * K / 512, row groups), block = 256, dynamic
-// LDS kProjLds.
+// grid = (outputs / (64 T), layers * K / 512, row groups), block = 256,
+// dynamic LDS kProjLds.  Each wave takes T consecutive 16-row tiles over the
+// block's K slice, one after the other: the weight ring runs on across the
+// tiles, so a wave streams T x 4 chunks.  T > 1 fits a large launch into one
+// round of resident blocks (two per compute unit).
+template <int T>
 __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs p) {
   constexpr int BT = kProjRowsPerWave / 16;
+  constexpr int kChunks = T * kSliceChunks;
   extern __shared__ __attribute__((aligned(16))) unsigned char proj_lds[];
   _Float16* xs_hi = (_Float16*)proj_lds;
   _Float16* xs_lo = xs_hi + kProjRowsPerWave * kXsStride;
   float* xs_inv = (float*)(xs_lo + kProjRowsPerWave * kXsStride);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int o_base = (blockIdx.x * 4 + wave) * 16;
+  const int o_first = (blockIdx.x * 4 + wave) * 16 * T;
   const int splits = p.K / kSliceK;
   const int layer = blockIdx.y / splits;
   const int split = blockIdx.y % splits;
@@ -236,62 +241,76 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs p) {
   const int i = lane & 15;
   const int g = lane >> 4;
 
-  ProjLane pl;
+  ProjLane pl[T];
   {
     // Static indices and readfirstlane keep the descriptors in scalar
     // registers (a vector-register descriptor costs a loop per load).
     const _Float16* wl = layer == 0 ? p.w[0] : (layer == 1 ? p.w[1] : p.w[2]);
     const size_t tile_halves = (size_t)16 * p.K * 2;
-    const uint64_t a = (uint64_t)(uintptr_t)(wl + (size_t)(o_base >> 4) * tile_halves);  // never read past the rows
-    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
-                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-    const int bytes = __builtin_amdgcn_readfirstlane(o_base < p.rows ? (int)(tile_halves * 2) : 0);
-    pl.w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, 0, bytes, kBufferWord3);
-    pl.x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + layer * p.x_layer_stride), 0, p.B * p.K * 4, kBufferWord3);
-    pl.K = p.K;
-    pl.b_base = blockIdx.z * kProjRowsPerWave;
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const int o_base = o_first + 16 * tt;
+      const uint64_t a = (uint64_t)(uintptr_t)(wl + (size_t)(o_base >> 4) * tile_halves);  // never read past the rows
+      const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+      const int bytes = __builtin_amdgcn_readfirstlane(o_base < p.rows ? (int)(tile_halves * 2) : 0);
+      pl[tt].w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, 0, bytes, kBufferWord3);
+      pl[tt].x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + layer * p.x_layer_stride), 0, p.B * p.K * 4,
+                                                   kBufferWord3);
+      pl[tt].K = p.K;
+      pl[tt].b_base = blockIdx.z * kProjRowsPerWave;
+    }
   }
 
+  // Chunk q of the wave's stream: tile q / 4, K chunk q % 4 of the slice.
   WChunk wbuf[kWRing];
 #pragma unroll
-  for (int c = 0; c < kWRing - 1; ++c) proj_load_w(pl, k_begin + c * kKChunk, wbuf[c]);
+  for (int q = 0; q < kWRing - 1; ++q)
+    proj_load_w(pl[q / kSliceChunks], k_begin + (q % kSliceChunks) * kKChunk, wbuf[q]);
   {
     f32x4 xr[kSliceChunks][kStage];
 #pragma unroll
-    for (int c = 0; c < kSliceChunks; ++c) proj_load_x(pl, k_begin + c * kKChunk, xr[c]);
+    for (int c = 0; c < kSliceChunks; ++c) proj_load_x(pl[0], k_begin + c * kKChunk, xr[c]);
 #pragma unroll
     for (int c = 0; c < kSliceChunks; ++c) proj_store_x(xr[c], c, xs_hi, xs_lo, xs_inv);
   }
   lds_barrier();
 
-  f32x4 tot[BT];
 #pragma unroll
-  for (int bt = 0; bt < BT; ++bt) tot[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < T; ++tt) {
+    f32x4 tot[BT];
 #pragma unroll
-  for (int c = 0; c < kSliceChunks; ++c) {
-    if (c + kWRing - 1 < kSliceChunks)
-      proj_load_w(pl, k_begin + (c + kWRing - 1) * kKChunk, wbuf[(c + kWRing - 1) % kWRing]);
-    proj_chunk<BT>(wbuf[c % kWRing], c, xs_hi, xs_lo, xs_inv, i, g, tot);
-    __builtin_amdgcn_sched_barrier(0);  // keep each chunk's loads with it (registers)
-  }
+    for (int bt = 0; bt < BT; ++bt) tot[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) {
+      const int q = tt * kSliceChunks + c;
+      if (q + kWRing - 1 < kChunks) {
+        const int qn = q + kWRing - 1;
+        proj_load_w(pl[qn / kSliceChunks], k_begin + (qn % kSliceChunks) * kKChunk, wbuf[qn % kWRing]);
+      }
+      proj_chunk<BT>(wbuf[q % kWRing], c, xs_hi, xs_lo, xs_inv, i, g, tot);
+      __builtin_amdgcn_sched_barrier(0);  // keep each chunk's loads with it (registers)
+    }
 
-  // C rows are outputs, C columns batch rows: lane l holds o = o_base +
-  // 4(l/16) + r, r = 0..3, for batch row 16 bt + l%16.  Undo the weight
-  // rows' scales and store the four consecutive outputs.
-  const int o = o_base + 4 * g;
-  if (o < p.rows) {
-    const float* inv = layer == 0 ? p.winv[0] : (layer == 1 ? p.winv[1] : p.winv[2]);
-    const f32x4 sw = *(const f32x4*)(inv + o);
+    // C rows are outputs, C columns batch rows: lane l holds o = o_base +
+    // 4(l/16) + r, r = 0..3, for batch row 16 bt + l%16.  Undo the weight
+    // rows' scales and store the four consecutive outputs.
+    const int o = o_first + 16 * tt + 4 * g;
+    if (o < p.rows) {
+      const float* inv = layer == 0 ? p.winv[0] : (layer == 1 ? p.winv[1] : p.winv[2]);
+      const f32x4 sw = *(const f32x4*)(inv + o);
 #pragma unroll
-    for (int bt = 0; bt < BT; ++bt) {
-      const int b = pl.b_base + 16 * bt + i;
-      if (b < p.B) *(f32x4*)(p.out + (((size_t)split * kLayers + layer) * p.B + b) * p.rows + o) = tot[bt] * sw;
+      for (int bt = 0; bt < BT; ++bt) {
+        const int b = pl[0].b_base + 16 * bt + i;
+        if (b < p.B) *(f32x4*)(p.out + (((size_t)split * kLayers + layer) * p.B + b) * p.rows + o) = tot[bt] * sw;
+      }
     }
   }
 }
 
+template <int T>
 void launch_proj(const ProjArgs& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL(proj_kernel, grid, dim3(256), kProjLds, stream, p);
+  hipLaunchKernelGGL(proj_kernel<T>, grid, dim3(256), kProjLds, stream, p);
 }
 
 __device__ inline float wave_sum(float v) {
@@ -447,7 +466,7 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     p.B = B;
     const int col_tiles = (kProj1Out + 15) / 16;
     dim3 grid((col_tiles + 3) / 4, kLayers * s1, row_groups);
-    launch_proj(p, grid, stream);
+    launch_proj<1>(p, grid, stream);
   }
   // RMSNorm + weight-branch finish + RoPE angles.
   {
@@ -471,9 +490,11 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     p.rows = kHeads * kHeadDim;
     p.K = kQLora;
     p.B = B;
+    // Two tiles per wave: 384 blocks for one row group, one round of two
+    // resident blocks per compute unit (one tile per wave would need 1.5).
     const int col_tiles = kHeads * kHeadDim / 16;
-    dim3 grid((col_tiles + 3) / 4, kLayers * s2, row_groups);
-    launch_proj(p, grid, stream);
+    dim3 grid((col_tiles + 7) / 8, kLayers * s2, row_groups);
+    launch_proj<2>(p, grid, stream);
   }
   // Split-K sum, RoPE (YaRN) + normalized Hadamard.
   hipLaunchKernelGGL(rope_hadamard_kernel, dim3(kLayers * B * kHeads / 4), dim3(256), 0, stream, ws.q_lin, s2,
@@ -484,7 +505,9 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
 hipError_t launch_pack_weights(const fm_weights& wts, const Workspace& ws, hipStream_t stream) {
   // The projection kernel stages a 512-wide slice of 32 activation rows
   // (about 66 KB of LDS, above the default dynamic limit).
-  hipError_t a = hipFuncSetAttribute((const void*)proj_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
+  hipError_t a = hipFuncSetAttribute((const void*)proj_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
+  if (a == hipSuccess)
+    a = hipFuncSetAttribute((const void*)proj_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
   if (a != hipSuccess) return a;
   for (int l = 0; l < kLayers; ++l) {
     _Float16* w1 = ws.w1 + (size_t)l * kProj1Out * kHidden * 2;
