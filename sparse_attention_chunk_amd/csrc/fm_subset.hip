@@ -8,18 +8,21 @@
 // list position (the lower chunk index when the list is ascending), written
 // as chunk indices in list order.  Entries outside [0, N) are never chosen.
 //
-// One block of 1024 threads per row; position p of the list is handled by
-// thread p mod 1024 (coalesced list reads), in rounds of 1024 positions.
-// Lists of up to 32 rounds gather their keys (order-preserving uint32 of the
-// scores) once, every load in flight together, into LDS with a validity
-// bitmap; longer lists gather them again in every pass, eight rounds of
-// loads at a time.  An exact radix selection gives the k-th largest key T
-// and the last position kept among the keys equal to T.  The chosen entries
-// are then written in list order: per round each wave ballots its 64
-// positions, the counts of all (round, wave) pairs are scanned once, each
-// chosen position is written at its wave's offset plus the chosen lanes
-// below it, and a last pass replaces every written position by its chunk
-// index.
+// One block of 1024 threads per row selects; position p of the list is
+// handled by thread p mod 1024 (coalesced list reads), in rounds of 1024
+// positions.  Lists of up to 32 rounds keep their keys (order-preserving
+// uint32 of the scores) and a validity bitmap in LDS: gathered beforehand by
+// one block per round (sub_gather_kernel) when the workspace can stage them,
+// else by the selecting block with every load in flight together.  Longer
+// lists gather their keys again in every pass, eight rounds of loads at a
+// time.  Lists in LDS longer than 8192 entries narrow the selection with a
+// sampled cut-off (sampled_select); otherwise an exact radix selection over
+// the whole list gives the k-th largest key T and the last position kept
+// among the keys equal to T.  The chosen entries are then written in list
+// order: per round each wave ballots its 64 positions, the counts of all
+// (round, wave) pairs are scanned once, each chosen position is written at
+// its wave's offset plus the chosen lanes below it, and a last pass replaces
+// every written position by its chunk index.
 #include "fm_radix.h"
 
 namespace fm {
