@@ -39,8 +39,8 @@ enum : uint32_t { kSelect = 0, kKeepAll = 1, kKeepNone = 2 };
 constexpr int kSampleRuns = 64;
 constexpr int kSampleRun = 64;
 constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 4096
-constexpr int kSampleThreads = 256;
-constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 16
+constexpr int kSampleThreads = 1024;
+constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 4
 
 // 1. Cut-off per row from a sample.  grid = B, block = kSampleThreads.
 __global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float* scores, int64_t N,
