@@ -181,3 +181,47 @@ def test_fp8_argument_errors(retr):
     assert L.fm_score_fp8(retr.ctx, q.data_ptr(), w.data_ptr(), ck.data_ptr(), 65, 16, None, 0, s.data_ptr(), None,
                           None) == _lib.FM_EINVAL
     assert L.fm_score_fp8(retr.ctx, None, None, None, 0, 0, None, 0, None, None, None) == _lib.FM_OK
+
+
+# --------------------------------------------------------------------------- properties of the fp8 path
+
+def _records(n, seed, rows=1):
+    rng = np.random.default_rng(seed)
+    return np.stack([synth.encode_records(rng.standard_normal((n, 128)).astype(np.float32)) for _ in range(rows)])
+
+
+@pytest.fixture(scope="module")
+def qw4(weights_np):
+    wl = synth.WORKLOADS[3]
+    return oracle.prepare_query(weights_np, synth.make_hidden(wl)[:4], synth.make_positions(wl)[:4],
+                                oracle.OracleConfig())
+
+
+def _run8(retr, q, w, ck):
+    s, p = score_fp8(retr, dev(q.astype(np.float32)), dev(w.astype(np.float32)), dev(ck))
+    return host(s), host(p)
+
+
+def test_fp8_bit_identical_and_row_independent(retr, qw4):
+    q, w = qw4
+    ck = _records(5000, 11, rows=3)
+    a, pa = _run8(retr, q[:, :3], w[:, :3], ck)
+    b, pb = _run8(retr, q[:, :3], w[:, :3], ck)
+    assert np.array_equal(a, b) and np.array_equal(pa, pb)
+    c, _ = _run8(retr, q[:, 1:2], w[:, 1:2], ck[1:2])
+    assert np.array_equal(a[1], c[0])
+
+
+def test_fp8_zero_records_and_negative_scales(retr, qw4):
+    q, w = qw4
+    s, p = _run8(retr, q[:, :1], w[:, :1], np.zeros((1, 100, 132), np.uint8))
+    assert np.all(s == 0.5) and np.all(p == 0.5)
+    ck = _records(1000, 12)
+    sc = ck[0, :, 128:].copy().view("<f4")[:, 0]
+    sc[::3] *= -1.0
+    ck[0, :, 128:] = sc.astype("<f4").view(np.uint8).reshape(-1, 4)
+    s, p = _run8(retr, q[:, :1], w[:, :1], ck)
+    per_ref, ens_ref = oracle_scores(ck, q[:, :1], w[:, :1], [1000], "max")
+    e = max(max_score_err(s, ens_ref), max_score_err(p, per_ref))
+    report("fp8 negative scales", max_abs=e)
+    assert e <= SCORE_TOL
