@@ -39,7 +39,8 @@ def bits(t):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("B,R,N", [(2, 3, 1), (2, 4, 17), (3, 8, 4096), (2, 5, 70001), (1, 2, 262144)])
+@pytest.mark.parametrize("B,R,N", [(2, 3, 1), (2, 4, 17), (3, 8, 4096), (2, 5, 70001), (1, 2, 262144),
+                                   (5, 6, 8200), (5, 9, 65536)])
 def test_random_masks_bit_exact(retr, dtype, B, R, N):
     rng = np.random.default_rng(B * 100 + R * 10 + N)
     logits = torch.from_numpy(rng.normal(size=(B, R, N)).astype(np.float32)).to(dtype)
