@@ -223,14 +223,18 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
   store_tile<MEAN, PER_LAYER>(cx, t, tile);
 }
 
-// Instruction order of one phase: every MFMA followed by three vector-ALU
-// instructions (the reduction of the previous tile), then the phase's
-// requests and stores; nothing crosses a phase boundary.
+// Instruction order of one phase: every MFMA followed by up to four
+// vector-ALU instructions (the reduction of the previous tile, about 84 per
+// tile, so none is left after the last MFMA), then the phase's requests and
+// stores; nothing crosses a phase boundary.  Measured per tile in shader
+// clocks: three per MFMA 1017 (the sigmoid chain then runs after the last
+// MFMA), four 906, five 940, six 1000; requests placed earlier in the
+// phase cost more.
 __device__ __forceinline__ void interleave_phase8() {
 #pragma unroll
   for (int k = 0; k < kLayers * 4 * 2 + 1; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
   }
   __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);    // VMEM read: codes, scale
   __builtin_amdgcn_sched_group_barrier(0x040, 4, 0);    // VMEM write
