@@ -137,18 +137,17 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   if (cus < 1 || cus > kMaxScoreBlocks) return fail(FM_EUNSUPPORTED, "device reports %d compute units", cus);
 
   // One allocation, each buffer 256-byte aligned.  The split-K partial
-  // buffers hold splits(B) * B rows, largest at B = max_batch or at the
+  // buffer holds splits(B) * B rows, largest at B = max_batch or at the
   // largest B of the most-split row-group count.
   const size_t mb = (size_t)max_batch;
-  size_t p1_rows = 0, p2_rows = 0;
+  size_t p1_rows = 0;
   for (int g = 1; g <= proj_row_groups(max_batch); ++g) {
     const int b = g * kProjRowsPerWave < max_batch ? g * kProjRowsPerWave : max_batch;
     p1_rows = std::max(p1_rows, (size_t)proj1_splits(b) * b);
-    p2_rows = std::max(p2_rows, (size_t)proj2_splits(b) * b);
   }
   const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
   enum {
-    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kQLin, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
+    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
     kSelState, kSelCand, kSelCount, kResCount, kNumBuffers
   };
   size_t sizes[kNumBuffers];
@@ -159,7 +158,6 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kGain] = sizeof(float) * kLayers * kQLora;
   sizes[kPart1] = sizeof(float) * kLayers * p1_rows * kProj1Out;
   sizes[kAHat] = sizeof(float) * kLayers * mb * kQLora;
-  sizes[kQLin] = sizeof(float) * kLayers * p2_rows * kHeads * kHeadDim;
   sizes[kFreq] = sizeof(double) * (kRopeDim / 2);
   sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
   sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
@@ -197,7 +195,6 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.q_norm = (float*)(p + offs[kGain]);
   ctx->ws.proj1_part = (float*)(p + offs[kPart1]);
   ctx->ws.a_hat = (float*)(p + offs[kAHat]);
-  ctx->ws.q_lin = (float*)(p + offs[kQLin]);
   ctx->ws.rope_freq = (double*)(p + offs[kFreq]);
   ctx->ws.rope_cs = (float*)(p + offs[kCosSin]);
   ctx->ws.qpack = (void*)(p + offs[kQPack]);

@@ -32,9 +32,8 @@ constexpr int kSliceK = 512;
 constexpr int kSliceChunks = kSliceK / 128;
 
 inline int proj_row_groups(int B) { return (B + kProjRowsPerWave - 1) / kProjRowsPerWave; }
-// K slices of the first projection (K = 4096) and of wq_b (K = 1024).
+// K slices of the first projection (K = 4096).
 inline int proj1_splits(int) { return kHidden / kSliceK; }
-inline int proj2_splits(int) { return kQLora / kSliceK; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,
@@ -73,7 +72,6 @@ struct Workspace {
   float* q_norm = nullptr;       // [3][kQLora] RMSNorm gains
   float* proj1_part = nullptr;   // [proj1_splits(B)][3][B][kProj1Out]
   float* a_hat = nullptr;        // [3][max_batch][kQLora]
-  float* q_lin = nullptr;        // [proj2_splits(B)][3][B][kHeads * kHeadDim]
   double* rope_freq = nullptr;   // [kRopeDim / 2]
   float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16

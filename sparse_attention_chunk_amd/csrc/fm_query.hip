@@ -131,9 +131,12 @@ __device__ __forceinline__ void proj_load_w(const ProjLane& pl, int kc, WChunk& 
   }
 }
 
-// Load j of wave v covers batch rows 8 j + 2 v (lanes 0..31) and
-// 8 j + 2 v + 1 (lanes 32..63), one float4 per lane.
-__device__ __forceinline__ int stage_row(int j) { return 8 * j + 2 * (int)(threadIdx.x >> 6) + ((threadIdx.x >> 5) & 1); }
+// Load j of wave v (of a group of four staging one slice) covers batch
+// rows 8 j + 2 v (lanes 0..31) and 8 j + 2 v + 1 (lanes 32..63), one float4
+// per lane.
+__device__ __forceinline__ int stage_row(int j) {
+  return 8 * j + 2 * (int)((threadIdx.x >> 6) & 3) + ((threadIdx.x >> 5) & 1);
+}
 
 // Activation rows b_base .. b_base + 32 (zeros past B) of the slice's
 // chunk c, to registers.  The per-lane offset holds the row (so rows past B
@@ -221,8 +224,8 @@ __device__ __forceinline__ void lds_barrier() {
 // grid = (outputs / (64 T), layers * K / 512, row groups), block = 256,
 // dynamic LDS kProjLds.  Each wave takes T consecutive 16-row tiles over the
 // block's K slice, one after the other: the weight ring runs on across the
-// tiles, so a wave streams T x 4 chunks.  T > 1 fits a large launch into one
-// round of resident blocks (two per compute unit).
+// tiles, so a wave streams T x 4 chunks.  The first projection (408 blocks,
+// within one round of two resident blocks per compute unit) uses T = 1.
 template <int T>
 __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs p) {
   constexpr int BT = kProjRowsPerWave / 16;
@@ -394,29 +397,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* part, GainPtr
   }
 }
 
-// One wave per (layer, row, head), 4 heads per block.  Lane l holds dims 2l
-// and 2l+1 of the head (the wq_b K-slice partials added in slice order).
-// RoPE: lanes 32..63 hold the rotated dims 64..127; pair j = l - 32 is
-// turned counter-clockwise by pos * freq[j] (cosine and sine from the
-// RMSNorm kernel), the rotation in fp32.  Then the 128-point Walsh-Hadamard
-// butterfly in Sylvester order, scaled by 128^-0.5.
-__global__ __launch_bounds__(256) void rope_hadamard_kernel(const float* q_lin, int splits, const float* rope_cs, int B,
-                                                            float* q_out) {
-  const int lane = threadIdx.x & 63;
-  const int gh = blockIdx.x * 4 + (threadIdx.x >> 6);  // (layer * B + b) * 64 + h
-  const int h = gh % kHeads;
-  const int lb = gh / kHeads;
-  const int b = lb % B;
-  const size_t off = (size_t)lb * kHeads * kHeadDim + (size_t)h * kHeadDim + 2 * lane;
-  const size_t split_stride = (size_t)kLayers * B * kHeads * kHeadDim;
-  float x = 0.f, y = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float2 v = *(const float2*)(q_lin + s * split_stride + off);
-    x += v.x;
-    y += v.y;
-  }
+// RoPE and the normalized Hadamard transform of one head's 128 dims, held
+// by a wave as dims 2l and 2l+1 in lane l (x, y).  RoPE: lanes 32..63 hold
+// the rotated dims 64..127; pair j = l - 32 is turned counter-clockwise by
+// pos * freq[j] (cosine and sine from the RMSNorm kernel), the rotation in
+// fp32.  Then the 128-point Walsh-Hadamard butterfly in Sylvester order,
+// scaled by 128^-0.5.
+__device__ __forceinline__ float2 rope_hadamard(float x, float y, const float* cs_row, int lane) {
   if (lane >= 32) {
-    const float2 c = *(const float2*)(rope_cs + ((size_t)b * (kRopeDim / 2) + (lane - 32)) * 2);
+    const float2 c = *(const float2*)(cs_row + 2 * (lane - 32));
     const float rx = x * c.x - y * c.y;
     const float ry = x * c.y + y * c.x;
     x = rx;
@@ -437,7 +426,131 @@ __global__ __launch_bounds__(256) void rope_hadamard_kernel(const float* q_lin, 
     }
   }
   const float inv_sqrt = 0.08838834764831845f;  // 128^-0.5
-  *(float2*)(q_out + off) = make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
+  return make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
+}
+
+// q = Hadamard(RoPE(wq_b a_hat)) in one pass.  One block of 8 waves per
+// (head, layer, group of 32 batch rows) computes the head's 128 outputs of
+// wq_b over the whole K = Q_LORA_RANK: wave w takes K slice w / 4 and the
+// 32 outputs 32 (w % 4) .. + 31 (two 16-row tiles, streamed one after the
+// other through one register ring); both slices' activations are staged
+// side by side in LDS.
+// The two slices' sums meet in LDS (slice 0 + slice 1), and each wave then
+// rotates, transforms and stores four batch rows.  The head's whole weight
+// block (512 KB) is streamed by one compute unit, so no partial sums leave
+// the block and no second launch is needed.
+constexpr int kHeadThreads = 512;
+constexpr int kHeadProjLds = 2 * kProjLds;
+constexpr int kHeadRing = 3;  // weight chunks in registers per wave (kHeadRing - 1 in flight)
+static_assert(kQLora == 2 * kSliceK, "two K slices per head block");
+static_assert(2 * kProjRowsPerWave * kHeadDim * 4 <= kHeadProjLds, "slice sums fit in the staging area");
+
+struct HeadProjArgs {
+  const _Float16* w[kLayers];  // packed wq_b of each layer
+  const float* winv[kLayers];  // [kHeads * kHeadDim]: 2^-e of each row
+  const float* a_hat;          // [3][B][kQLora]
+  const float* rope_cs;        // [B][kRopeDim / 2][2]
+  float* q_out;                // [3][B][kHeads][kHeadDim]
+  int B;
+};
+
+__global__ __launch_bounds__(kHeadThreads, 1) void head_proj_kernel(HeadProjArgs p) {
+  constexpr int BT = kProjRowsPerWave / 16;
+  constexpr int T = 2;
+  constexpr int kChunks = T * kSliceChunks;
+  extern __shared__ __attribute__((aligned(16))) unsigned char head_lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave >> 2;  // K slice
+  const int head = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int b_base = blockIdx.z * kProjRowsPerWave;
+  _Float16* xs_hi = (_Float16*)(head_lds + half * kProjLds);
+  _Float16* xs_lo = xs_hi + kProjRowsPerWave * kXsStride;
+  float* xs_inv = (float*)(xs_lo + kProjRowsPerWave * kXsStride);
+  const int k_begin = half * kSliceK;
+  const int d_first = (wave & 3) * 16 * T;  // first of the wave's outputs within the head
+  const int o_first = head * kHeadDim + d_first;
+  const int i = lane & 15;
+  const int g = lane >> 4;
+
+  ProjLane pl[T];
+  {
+    const _Float16* wl = layer == 0 ? p.w[0] : (layer == 1 ? p.w[1] : p.w[2]);
+    const size_t tile_halves = (size_t)16 * kQLora * 2;
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const uint64_t a = (uint64_t)(uintptr_t)(wl + (size_t)((o_first >> 4) + tt) * tile_halves);
+      const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+      pl[tt].w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, 0, (int)(tile_halves * 2), kBufferWord3);
+      pl[tt].x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_hat + (size_t)layer * p.B * kQLora), 0,
+                                                   p.B * kQLora * 4, kBufferWord3);
+      pl[tt].K = kQLora;
+      pl[tt].b_base = b_base;
+    }
+  }
+
+  WChunk wbuf[kHeadRing];
+#pragma unroll
+  for (int q = 0; q < kHeadRing - 1; ++q)
+    proj_load_w(pl[q / kSliceChunks], k_begin + (q % kSliceChunks) * kKChunk, wbuf[q]);
+  {
+    f32x4 xr[kSliceChunks][kStage];
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) proj_load_x(pl[0], k_begin + c * kKChunk, xr[c]);
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) proj_store_x(xr[c], c, xs_hi, xs_lo, xs_inv);
+  }
+  lds_barrier();
+
+  f32x4 res[T][BT];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    f32x4 tot[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) tot[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kSliceChunks; ++c) {
+      const int q = tt * kSliceChunks + c;
+      if (q + kHeadRing - 1 < kChunks) {
+        const int qn = q + kHeadRing - 1;
+        proj_load_w(pl[qn / kSliceChunks], k_begin + (qn % kSliceChunks) * kKChunk, wbuf[qn % kHeadRing]);
+      }
+      proj_chunk<BT>(wbuf[q % kHeadRing], c, xs_hi, xs_lo, xs_inv, i, g, tot);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Lane l holds outputs o = o_first + 16 tt + 4(l/16) + r for batch row
+    // 16 bt + l%16; undo the weight rows' scales.
+    const float* inv = layer == 0 ? p.winv[0] : (layer == 1 ? p.winv[1] : p.winv[2]);
+    const f32x4 sw = *(const f32x4*)(inv + o_first + 16 * tt + 4 * g);
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) res[tt][bt] = tot[bt] * sw;
+  }
+
+  // Slice sums to LDS (over the staging area, once every wave is done with
+  // it): sums[half][batch row][dim].
+  lds_barrier();
+  float* sums = (float*)head_lds;
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt)
+      *(f32x4*)(sums + ((size_t)half * kProjRowsPerWave + 16 * bt + i) * kHeadDim + d_first + 16 * tt + 4 * g) =
+          res[tt][bt];
+  lds_barrier();
+
+  // Wave w finishes batch rows w, w + 8, w + 16, w + 24 of the group.
+#pragma unroll
+  for (int j = 0; j < kProjRowsPerWave / 8; ++j) {
+    const int r = wave + 8 * j;
+    const int b = b_base + r;
+    if (b >= p.B) break;
+    const float2 s0 = *(const float2*)(sums + (size_t)r * kHeadDim + 2 * lane);
+    const float2 s1 = *(const float2*)(sums + ((size_t)kProjRowsPerWave + r) * kHeadDim + 2 * lane);
+    const float2 v = rope_hadamard(s0.x + s1.x, s0.y + s1.y, p.rope_cs + (size_t)b * kRopeDim, lane);
+    *(float2*)(p.q_out + (((size_t)layer * p.B + b) * kHeads + head) * kHeadDim + 2 * lane) = v;
+  }
 }
 
 }  // namespace
@@ -449,7 +562,6 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
   (void)wts;  // packed into the workspace by fm_create
   const int row_groups = proj_row_groups(B);
   const int s1 = kHidden / kSliceK;
-  const int s2 = kQLora / kSliceK;
 
   // wq_a | weights_proj (packed together), split over K.
   {
@@ -477,28 +589,20 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     hipLaunchKernelGGL(kern, dim3(kLayers * B), dim3(256), 0, stream, ws.proj1_part, gp, B, cfg.rms_eps, w_scale,
                        positions, ws.rope_freq, ws.rope_cs, ws.a_hat, w_out);
   }
-  // wq_b, split over K.
+  // wq_b, RoPE (YaRN) and the normalized Hadamard transform, per head.
   {
-    ProjArgs p{};
+    HeadProjArgs p{};
     for (int l = 0; l < kLayers; ++l) {
       p.w[l] = ws.w2 + (size_t)l * kHeads * kHeadDim * kQLora * 2;
       p.winv[l] = ws.w2_inv + (size_t)l * kHeads * kHeadDim;
     }
-    p.x = ws.a_hat;
-    p.x_layer_stride = (long)B * kQLora;
-    p.out = ws.q_lin;
-    p.rows = kHeads * kHeadDim;
-    p.K = kQLora;
+    p.a_hat = ws.a_hat;
+    p.rope_cs = ws.rope_cs;
+    p.q_out = q_out;
     p.B = B;
-    // Two tiles per wave: 384 blocks for one row group, one round of two
-    // resident blocks per compute unit (one tile per wave would need 1.5).
-    const int col_tiles = kHeads * kHeadDim / 16;
-    dim3 grid((col_tiles + 7) / 8, kLayers * s2, row_groups);
-    launch_proj<2>(p, grid, stream);
+    hipLaunchKernelGGL(head_proj_kernel, dim3(kHeads, kLayers, row_groups), dim3(kHeadThreads), kHeadProjLds, stream,
+                       p);
   }
-  // Split-K sum, RoPE (YaRN) + normalized Hadamard.
-  hipLaunchKernelGGL(rope_hadamard_kernel, dim3(kLayers * B * kHeads / 4), dim3(256), 0, stream, ws.q_lin, s2,
-                     ws.rope_cs, B, q_out);
   return hipGetLastError();
 }
 
@@ -507,7 +611,7 @@ hipError_t launch_pack_weights(const fm_weights& wts, const Workspace& ws, hipSt
   // (about 66 KB of LDS, above the default dynamic limit).
   hipError_t a = hipFuncSetAttribute((const void*)proj_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
   if (a == hipSuccess)
-    a = hipFuncSetAttribute((const void*)proj_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kProjLds);
+    a = hipFuncSetAttribute((const void*)head_proj_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kHeadProjLds);
   if (a != hipSuccess) return a;
   for (int l = 0; l < kLayers; ++l) {
     _Float16* w1 = ws.w1 + (size_t)l * kProj1Out * kHidden * 2;
