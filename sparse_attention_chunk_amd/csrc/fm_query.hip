@@ -150,6 +150,24 @@ __device__ __forceinline__ void proj_load_x(const ProjLane& pl, int k0, f32x4 (&
   }
 }
 
+// Largest value over each group of 32 lanes (lanes 0..31 and 32..63), every
+// lane of the group receiving it: DPP moves within rows of 16 lanes (quad
+// swaps, then the half-row and row mirrors pair each lane with one of the
+// other half), then a swap of neighbouring rows.  All in the vector ALU, no
+// LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float max32(float m) {
+  m = fmaxf(m, dpp_move<0xb1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_move<0x4e>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_move<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_move<0x140>(m));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Chunk c of each staged row: scaled by its power of two (from its largest
 // entry, a reduction over the 32 lanes holding it), split into f16 hi/lo,
 // stored to LDS columns 128 c .. with the row's 2^-e.
@@ -159,9 +177,7 @@ __device__ __forceinline__ void proj_store_x(const f32x4 (&xr)[kStage], int c, _
 #pragma unroll
   for (int j = 0; j < kStage; ++j) {
     const f32x4 v = xr[j];
-    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float m = max32(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     const int e = split_exponent(m);
     const float sc = ldexpf(1.f, e);
     f16x4 h, l;
@@ -316,10 +332,19 @@ void launch_proj(const ProjArgs& p, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL(proj_kernel<T>, grid, dim3(256), kProjLds, stream, p);
 }
 
+// Sum over the 64 lanes, every lane receiving it: the max32 pattern with
+// adds, then a swap of the wave's halves.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_move<0xb1>(v);
+  v += dpp_move<0x4e>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct GainPtrs {

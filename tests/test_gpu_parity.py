@@ -74,16 +74,17 @@ def test_prepare_query_parity(retr, weights_np, cid, rows):
     assert dq <= Q_TOL and dw <= W_TOL
 
 
-def test_prepare_query_parity_yarn(retr_yarn, weights_np):
+@pytest.mark.parametrize("rows", [list(range(12)), list(range(40))])
+def test_prepare_query_parity_yarn(retr_yarn, weights_np, rows):
+    """YaRN positions; 40 rows span two groups of 32 batch rows."""
     wl = synth.WORKLOADS[4]
-    rows = list(range(12))
     hidden = synth.make_hidden(wl)[rows]
     pos = synth.make_positions(wl)[rows]
     q_ref, w_ref = oracle.prepare_query(weights_np, hidden, pos, oracle_config(wl))
     q, w = retr_yarn.prepare_query(dev(hidden), dev(pos))
     dq = np.abs(host(q) - q_ref).max()
     dw = np.abs(host(w) - w_ref).max()
-    report("prepare_query cfg4 yarn", max_abs_q=dq, max_abs_w=dw)
+    report(f"prepare_query cfg4 yarn B={len(rows)}", max_abs_q=dq, max_abs_w=dw)
     assert dq <= Q_TOL and dw <= W_TOL
 
 
