@@ -94,7 +94,6 @@ def cpu_baseline(budget_s: float):
     pos = synth.make_positions(wl)
     cfg = oracle.OracleConfig()
     rows = 0
-    t0 = time.perf_counter()
     elapsed = 0.0
     while rows < wl.batch:
         comp = synth.make_comp_k(wl, rows=[rows])[0]   # generation is outside the timed part
@@ -104,7 +103,6 @@ def cpu_baseline(budget_s: float):
         rows += 1
         if elapsed >= budget_s:
             break
-    _ = t0
     return {"value": rows * wl.n_chunks / elapsed, "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} of {wl.batch} rows x {wl.n_chunks} chunks (query prep, 3-layer score, max "
                       f"ensemble, top-{TOP_K}), fp64 numpy, {elapsed:.1f} s",
