@@ -110,18 +110,18 @@ constexpr uint32_t kSubCandMax = 16384;    // candidates compacted into the firs
 // top-K does): the m-th largest of 4096 evenly spaced valid keys gives a
 // cut-off L with m chosen so that about k plus four standard deviations of
 // the list's keys are expected at or above L.  One pass over the list keeps
-// the keys >= L in registers, counts them per (round, wave), and compacts
-// them, in list order, into the first half of the key area (keys) and the
-// second half (positions).  The exact radix selection then runs over these
-// candidates only, and their chosen ones are written in list order.  Returns
-// false, with LDS untouched, when the candidates are fewer than k or too
-// many; the caller then selects over the whole list.
-__device__ bool sampled_select(uint32_t* s_keys, const uint32_t* s_valid, uint32_t n, uint32_t rounds, uint32_t V,
-                               uint32_t k, const int32_t* srow, int32_t* orow, uint32_t* h, uint32_t* s_wtot,
-                               uint32_t* s_out, uint32_t* s_cnt) {
+// the keys >= L in registers and writes them, at each thread's offset from a
+// block scan of the counts, into the first half of the key area (keys) and
+// the second half (positions): unordered, since the exact radix selection
+// that then runs over these candidates does not depend on their order.  The
+// chosen ones set their bits in a bitmap of the list (over the validity
+// bitmap, no longer needed), and a scan of its words writes them in list
+// order.  Returns false, with LDS untouched, when the candidates are fewer
+// than k or too many; the caller then selects over the whole list.
+__device__ __forceinline__ bool sampled_select(uint32_t* s_keys, uint32_t* s_valid, uint32_t n, uint32_t rounds,
+                                               uint32_t V, uint32_t k, const int32_t* srow, int32_t* orow,
+                                               uint32_t* h, uint32_t* s_wtot, uint32_t* s_out) {
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const uint64_t below_me = (1ull << lane) - 1ull;
   auto valid_at = [&](uint32_t p) { return (s_valid[p >> 5] >> (p & 31)) & 1u; };
 
   // 1. Cut-off from the sample (sample i at position i n / 4096).
@@ -150,92 +150,56 @@ __device__ bool sampled_select(uint32_t* s_keys, const uint32_t* s_valid, uint32
       },
       m, 0, h, s_wtot, s_out, &L, &unused);
 
-  // 2. Candidates (keys >= L) of this thread, in registers; counts per
-  // (round, wave), then their offsets in list order.
+  // 2. Candidates (keys >= L) of this thread, in registers (the key area is
+  // overwritten below); the scan's barriers order every read before the
+  // first write.  Every round's key and bitmap word is read (past the list
+  // they are stale and masked off by p < n), so nothing here branches.
   uint32_t ck[kSubLdsRounds];
   uint32_t mine = 0;
 #pragma unroll
   for (int j = 0; j < kSubLdsRounds; ++j) {
     const uint32_t p = (uint32_t)j * kSubThreads + t;
     ck[j] = s_keys[p];
-    const bool c = (uint32_t)j < rounds && p < n && valid_at(p) && ck[j] >= L;
-    mine |= (uint32_t)c << j;
+    const uint32_t c = (uint32_t)(p < n) & valid_at(p) & (uint32_t)(ck[j] >= L);  // no short circuit
+    mine |= c << j;
   }
-  // Lane j of each wave keeps the wave's count (later its offset) of round j.
-  uint32_t lane_cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kSubLdsRounds; ++j) {
-    if ((uint32_t)j < rounds) {
-      const uint32_t c = (uint32_t)__popcll(__ballot((mine >> j) & 1u));
-      lane_cnt = lane == j ? c : lane_cnt;
-    }
-  }
-  if ((uint32_t)lane < rounds) s_cnt[lane * kSubWaves + wave] = lane_cnt;
-  __syncthreads();
-  const uint32_t nc = rounds * kSubWaves;  // at most 512 (round, wave) pairs
-  const uint32_t cnt = (uint32_t)t < nc ? s_cnt[t] : 0u;
   uint32_t C;
-  const uint32_t off = block_exclusive_scan(cnt, s_wtot, &C);
-  if (C < k || C > kSubCandMax) return false;  // block-uniform; LDS keys untouched
-  if ((uint32_t)t < nc) s_cnt[t] = off;
-  __syncthreads();
-  const uint32_t lane_off = (uint32_t)lane < rounds ? s_cnt[lane * kSubWaves + wave] : 0u;
+  uint32_t slot = block_exclusive_scan((uint32_t)__popc(mine), s_wtot, &C);
+  if (C < k || C > kSubCandMax) return false;  // block-uniform; LDS untouched
   uint32_t* c_key = s_keys;
   uint32_t* c_pos = s_keys + kSubCandMax;
 #pragma unroll
   for (int j = 0; j < kSubLdsRounds; ++j) {
-    if ((uint32_t)j < rounds) {
-      const bool c = (mine >> j) & 1u;
-      const uint64_t bm = __ballot(c);
-      const uint32_t base = __builtin_amdgcn_readlane(lane_off, j);
-      if (c) {
-        const uint32_t slot = base + (uint32_t)__popcll(bm & below_me);
-        c_key[slot] = ck[j];
-        c_pos[slot] = (uint32_t)j * kSubThreads + t;
-      }
+    if ((mine >> j) & 1u) {
+      c_key[slot] = ck[j];
+      c_pos[slot] = (uint32_t)j * kSubThreads + t;
+      ++slot;
     }
   }
   __syncthreads();
-
   // 3. Exact selection over the candidates (ties by list position).
   auto cand_each = [&](auto f) {
     for (uint32_t sl = t; sl < C; sl += kSubThreads) f(make_uint2(c_key[sl], c_pos[sl]));
   };
   uint32_t T, last;
   radix_select<kSubThreads>(cand_each, k, index_bits((int64_t)n), h, s_wtot, s_out, &T, &last);
-
-  // 4. The chosen candidates in slot (= list) order: positions first, then
-  // chunk indices.
-  const uint32_t crounds = (C + kSubThreads - 1) / kSubThreads;  // at most 16
-  uint32_t cm = 0, lane_cnt2 = 0;
-  for (uint32_t u = 0; u < crounds; ++u) {
-    const uint32_t sl = u * kSubThreads + t;
-    bool c = false;
-    if (sl < C) {
-      const uint32_t key = c_key[sl], pos = c_pos[sl];
-      c = key > T || (key == T && pos <= last);
-    }
-    cm |= (uint32_t)c << u;
-    const uint32_t cu = (uint32_t)__popcll(__ballot(c));
-    lane_cnt2 = (uint32_t)lane == u ? cu : lane_cnt2;
-  }
-  if ((uint32_t)lane < crounds) s_cnt[lane * kSubWaves + wave] = lane_cnt2;
+  // 4. The chosen ones in list order: bit p % 32 of word p / 32 of the list
+  // bitmap; thread t owns word t (positions 32 t .. 32 t + 31).
+  const uint32_t words = rounds * (kSubThreads / 32);  // at most kSubThreads
+  if ((uint32_t)t < words) s_valid[t] = 0u;
   __syncthreads();
-  const uint32_t nc2 = crounds * kSubWaves;
-  const uint32_t cnt2 = (uint32_t)t < nc2 ? s_cnt[t] : 0u;
+  cand_each([&](uint2 e) {
+    if (e.x > T || (e.x == T && e.y <= last)) atomicOr(&s_valid[e.y >> 5], 1u << (e.y & 31));
+  });
+  __syncthreads();
+  uint32_t bits = (uint32_t)t < words ? s_valid[t] : 0u;
   uint32_t tot;
-  const uint32_t off2 = block_exclusive_scan(cnt2, s_wtot, &tot);
-  if ((uint32_t)t < nc2) s_cnt[t] = off2;
-  __syncthreads();
-  const uint32_t lane_off2 = (uint32_t)lane < crounds ? s_cnt[lane * kSubWaves + wave] : 0u;
-  for (uint32_t u = 0; u < crounds; ++u) {
-    const bool c = (cm >> u) & 1u;
-    const uint64_t bm = __ballot(c);
-    const uint32_t base = __builtin_amdgcn_readlane(lane_off2, u);
-    if (c) orow[base + (uint32_t)__popcll(bm & below_me)] = (int32_t)c_pos[u * kSubThreads + t];
+  uint32_t out_slot = block_exclusive_scan((uint32_t)__popc(bits), s_wtot, &tot);
+  while (bits) {
+    const uint32_t p = 32u * (uint32_t)t + (uint32_t)__builtin_ctz(bits);
+    bits &= bits - 1u;
+    orow[out_slot++] = srow[p];
   }
-  __syncthreads();  // the positions are visible to the block
-  for (uint32_t s_ = t; s_ < k; s_ += kSubThreads) orow[s_] = srow[orow[s_]];
   return true;
 }
 
@@ -355,7 +319,7 @@ __global__ __launch_bounds__(kSubThreads) void sel_subset_kernel(const float* __
   const uint64_t below_me = (1ull << lane) - 1ull;
   if constexpr (LDS) {
     if (k < V && n > 2 * kSubSample && sampled_select(s_keys, s_valid, n, rounds, V, k, srow, orow, h, s_wtot,
-                                                      s_out, s_cnt))
+                                                      s_out))
       return;
   }
   uint32_t T = 0, last = 0xffffffffu;  // k == V: every valid entry is chosen
