@@ -16,13 +16,15 @@
 // else by the selecting block with every load in flight together.  Longer
 // lists gather their keys again in every pass, eight rounds of loads at a
 // time.  Lists in LDS longer than 8192 entries narrow the selection with a
-// sampled cut-off (sampled_select); otherwise an exact radix selection over
-// the whole list gives the k-th largest key T and the last position kept
-// among the keys equal to T.  The chosen entries are then written in list
-// order: per round each wave ballots its 64 positions, the counts of all
-// (round, wave) pairs are scanned once, each chosen position is written at
-// its wave's offset plus the chosen lanes below it, and a last pass replaces
-// every written position by its chunk index.
+// sampled cut-off (sampled_select: candidates above it, an exact radix
+// selection among them, and the chosen ones written in list order through a
+// bitmap of the list); otherwise an exact radix selection over the whole
+// list gives the k-th largest key T and the last position kept among the
+// keys equal to T, and the chosen entries are written in list order: per
+// round each wave ballots its 64 positions, the counts of all (round, wave)
+// pairs are scanned once, each chosen position is written at its wave's
+// offset plus the chosen lanes below it, and a last pass replaces every
+// written position by its chunk index.
 #include "fm_radix.h"
 
 namespace fm {
