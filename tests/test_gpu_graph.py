@@ -1,9 +1,10 @@
 """The hot path under HIP graph capture: fm_prepare_query + fm_score +
-fm_select_topk (and the decode-step calls fm_select_topk_subset and
-fm_mask_logits) captured once and replayed several times, with eager work
-and synchronisations between the replays; every replay must equal the eager
-result bit for bit.  The calls allocate nothing and never synchronise, so
-they can be captured."""
+fm_select_topk, and the calls around it (fm_score_fp8, fm_resident_delta
+against the previous cycle's mask, and the decode-step calls
+fm_select_topk_subset and fm_mask_logits), captured once and replayed
+several times, with eager work and synchronisations between the replays;
+every replay must equal the eager result bit for bit.  The calls allocate
+nothing and never synchronise, so they can be captured."""
 
 import pytest
 import torch
@@ -42,20 +43,38 @@ def test_graph_replays_match_eager(retr):
     logits = torch.empty((B, 8, N), dtype=torch.bfloat16, device="cuda")
     logits_src = torch.randn((B, 8, N), generator=torch.Generator(device="cuda").manual_seed(4), device="cuda",
                              dtype=torch.bfloat16)
+    scores8 = torch.empty((B, N), device="cuda")
+    prev = (torch.rand((B, N), generator=torch.Generator(device="cuda").manual_seed(5), device="cuda") < 0.01)
+    prev = prev.to(torch.uint8)
+    rcap = 2048
+    res = torch.empty((B, rcap), dtype=torch.int32, device="cuda")
+    ent = torch.empty((B, rcap), dtype=torch.int32, device="cuda")
+    lea = torch.empty((B, rcap), dtype=torch.int32, device="cuda")
+    n_res, n_ent, n_lea = (torch.empty((B,), dtype=torch.int32, device="cuda") for _ in range(3))
 
     def body(stream):
         sh = stream.cuda_stream
         _lib.fm_prepare_query(retr.ctx, hidden, pos, B, q, w, sh)
         _lib.fm_score(retr.ctx, q, w, comp, B, N, None, _lib.FM_ENSEMBLE_MAX, scores, None, sh)
         _lib.fm_select_topk(retr.ctx, scores, B, N, None, K, mask, sh)
+        _lib.fm_score_fp8(retr.ctx, q, w, comp, B, N, None, _lib.FM_ENSEMBLE_MAX, scores8, None, sh)
+        _lib.fm_resident_delta(retr.ctx, prev, mask, B, N, rcap, res, n_res, ent, n_ent, lea, n_lea, sh)
         _lib.fm_select_topk_subset(retr.ctx, step, B, N, sub, None, cap, K, out, n_out, sh)
         logits.copy_(logits_src)
         _lib.fm_mask_logits(retr.ctx, logits, _lib.FM_DTYPE_BF16, B, 8, N, mask, sh)
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.clone() for t in (q, w, scores, mask, out, n_out, logits)]
+        return [t.clone() for t in (q, w, scores, mask, out, n_out, logits, scores8, res, n_res, ent, n_ent, lea,
+                                    n_lea)]
 
+    def clear():
+        # The lists are written only up to their counts: their tails stay as cleared.
+        for t in (q, w, scores, out, n_out, logits, scores8, res, n_res, ent, n_ent, lea, n_lea):
+            t.zero_()
+        mask.fill_(False)
+
+    clear()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -67,9 +86,7 @@ def test_graph_replays_match_eager(retr):
     with torch.cuda.graph(g):
         body(torch.cuda.current_stream())
     for rep in range(4):
-        for t in (q, w, scores, out, n_out, logits):
-            t.zero_()
-        mask.fill_(False)
+        clear()
         torch.cuda.synchronize()
         g.replay()
         got = snapshot()
