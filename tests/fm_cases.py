@@ -18,15 +18,14 @@ BAND = 2e-3        # mask disagreement allowed only this close to the K-th score
 Q_TOL = 1e-4       # prepared q, absolute (diagnostic)
 W_TOL = 1e-6       # prepared w, absolute (diagnostic)
 
-REPORT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
-                      "parity_report.jsonl")
+REPORT = os.environ.get("FM_PARITY_REPORT")  # JSON-lines file for the measured margins, if set
 
 
 def report(case: str, **vals):
-    """Append measured margins to gpurun_out/parity_report.jsonl when that folder exists."""
+    """Print the measured margins of a case and append them to the file named
+    by FM_PARITY_REPORT when it is set."""
     print(case, vals, flush=True)
-    d = os.path.dirname(REPORT)
-    if os.path.isdir(d):
+    if REPORT:
         with open(REPORT, "a") as f:
             f.write(json.dumps({"case": case, **{k: float(v) for k, v in vals.items()}}) + "\n")
 
