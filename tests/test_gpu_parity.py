@@ -125,6 +125,29 @@ def _whole_pass(r, wl, rows, weights_np, mode, top_k, threshold, use_valid=False
     return e_ens, e_per, excused
 
 
+def test_max_batch_whole_pass(retr, weights_np):
+    """B = max_batch (64 rows: two groups of 32 in the projections, every wave
+    of the score grid on a share of 64 rows): prepared queries and every
+    chunk's score against the oracle, each row's top-512 exactly that of its
+    own scores and within the band of the oracle's."""
+    rng = np.random.default_rng(64)
+    B, N = 64, 8192
+    hidden = rng.standard_normal((B, 4096)).astype(np.float32)
+    pos = rng.integers(0, 1 << 20, B).astype(np.int64)
+    comp_k = np.stack([synth.encode_records(rng.standard_normal((N, 128)).astype(np.float32)) for _ in range(B)])
+    q_ref, w_ref = oracle.prepare_query(weights_np, hidden, pos, oracle.OracleConfig())
+    q, w = retr.prepare_query(dev(hidden), dev(pos))
+    dq, dw = np.abs(host(q) - q_ref).max(), np.abs(host(w) - w_ref).max()
+    scores = retr.score(q, w, dev(comp_k), None, "max")
+    mask = retr.keep_topk(scores, 512)
+    s, m = host(scores), host(mask)
+    per_ref, ens_ref = oracle_scores(comp_k, q_ref, w_ref, [N] * B, "max")
+    e = max_score_err(s, ens_ref)
+    exc = check_topk(m, s, ens_ref, [N] * B, 512)
+    report(f"max batch B={B} N={N}", max_abs_q=dq, max_abs_w=dw, max_abs_ens=e, band_excused=exc)
+    assert dq <= Q_TOL and dw <= W_TOL and e <= SCORE_TOL
+
+
 def test_cfg1_whole_pass_top512(retr, weights_np):
     e_ens, e_per, exc = _whole_pass(retr, synth.WORKLOADS[1], [0], weights_np, "max", 512, None)
     report("cfg1 b1 n4096 max top512", max_abs_ens=e_ens, max_abs_per_layer=e_per, band_excused=exc)
