@@ -159,6 +159,48 @@ def resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stre
             "leaving_per_row": float(n[2].mean()), "oracle_us": t_cpu * 1e6}
 
 
+def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
+    """The same workload's other ensemble and selection modes (mean ensemble
+    with top-512, max ensemble with the 0.5 threshold), score + select per
+    call pair from HIP events on the launch stream (median): launched in
+    turn, so all see the same thermal state."""
+    import numpy as np
+    import torch
+
+    def mean_topk():
+        L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MEAN, scores, None, sh)
+        L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
+
+    def max_threshold():
+        L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
+        L.fm_select_threshold(r.ctx, scores, B, N, None, 0.5, mask, sh)
+
+    def max_topk():
+        L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
+        L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
+
+    fns = (("max_top512", max_topk), ("mean_top512", mean_topk), ("max_threshold_0.5", max_threshold))
+    for _, fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    n = max(1, steps // 5)
+    for _ in range(n):
+        for name, fn in fns:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+            ev.append((name, e))
+    torch.cuda.synchronize()
+    out = {}
+    for name, _ in fns:
+        t = float(np.median([e[0].elapsed_time(e[1]) for nm, e in ev if nm == name])) * 1e-3
+        out[name] = {"score_select_us": t * 1e6, "chunks_per_s": B * N / t}
+    out["calls_each"] = n
+    return out
+
+
 def score_fp8_leg(L, r, q, w, comp_k, scores, B, N, sh, stream, steps):
     """fm_score_fp8 on the same prepared queries, launched alternately with
     fm_score (f16) so both see the same thermal state; HIP-event times per
@@ -380,6 +422,7 @@ def main(argv=None):
     score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
     subset = subset_topk_leg(fm, L, r, scores, B, N, sh, stream, args.steps)
     masking = mask_logits_leg(L, r, mask, B, N, sh, stream, args.steps)
+    variants = variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, args.steps)
 
     timed = [e for e in events if e is not None]
     prep = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
@@ -434,6 +477,7 @@ def main(argv=None):
         "score_select_chunks_per_s": chunks / (t_score + float(sel.mean())),
         "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
                       "mask_logits": masking},
+        "workload_variants": variants,
         "host_cpu": cpu_model,
         "software": {"rocm": _rocm_version(), "torch": torch.__version__},
     }
