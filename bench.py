@@ -13,7 +13,9 @@ seeded inputs already resident in HBM.  Prints one JSON line.
 fm_score call on the stream the kernels run on.  `traffic` is read from the
 committed rocprofv3 counter summary when that summary was taken on the
 current score-kernel source, else null.  `cpu_baseline` times the fp64
-oracle on a bounded sample of the same workload on this host.
+oracle on a bounded sample of the same workload on this host, and under
+`next_rows` on the inputs the resident-delta and subset top-K legs ran on.
+The next-row and variant legs run before the W warmup and K timed steps.
 """
 
 from __future__ import annotations
@@ -80,9 +82,11 @@ def read_traffic(chunks_per_launch: int):
         return None
 
 
-def cpu_baseline(budget_s: float):
+def cpu_baseline(budget_s: float, leg_inputs: dict):
     """The oracle, as it stands, on whole rows of the workload until the time
-    budget is spent (at least one row); chunks/s over the rows done."""
+    budget is spent (at least one row); chunks/s over the rows done.  Also
+    times the oracle's resident delta and subset top-K on the host copies of
+    the inputs the next-row legs ran on (all B rows each)."""
     import numpy as np
 
     import oracle
@@ -107,21 +111,33 @@ def cpu_baseline(budget_s: float):
         rows += 1
         if elapsed >= budget_s:
             break
+    next_rows = {}
+    if "resident_delta" in leg_inputs:
+        cur, prev = leg_inputs["resident_delta"]
+        t1 = time.perf_counter()
+        for b in range(cur.shape[0]):
+            oracle.resident_delta(cur[b], prev[b])
+        next_rows["resident_delta_us"] = (time.perf_counter() - t1) * 1e6
+    if "subset_topk" in leg_inputs:
+        step, sub = leg_inputs["subset_topk"]
+        t1 = time.perf_counter()
+        for b in range(step.shape[0]):
+            oracle.select_topk_subset(step[b], sub[b], TOP_K)
+        next_rows["subset_topk_us"] = (time.perf_counter() - t1) * 1e6
     return {"value": rows * wl.n_chunks / elapsed, "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} of {wl.batch} rows x {wl.n_chunks} chunks (query prep, 3-layer score, max "
                       f"ensemble, top-{TOP_K}), fp64 numpy, {elapsed:.1f} s",
-            "_cpu_model": _cpu_model()}
+            "next_rows": next_rows, "_cpu_model": _cpu_model()}
 
 
-def resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, steps):
+def resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, steps, leg_inputs):
     """fm_resident_delta on this step's top-K mask against the previous
-    cycle's: HIP-event time per call on the launch stream, algorithmic HBM
-    bytes (both masks read, the three index lists and counts written), and
-    the oracle on the same masks."""
+    cycle's: HIP-event time per call on the launch stream and algorithmic HBM
+    bytes (both masks read, the three index lists and counts written).  Host
+    copies of the two masks go into leg_inputs for the CPU baseline."""
     import numpy as np
     import torch
 
-    import oracle
     qp = torch.empty_like(q)
     wp = torch.empty_like(w)
     sp = torch.empty((B, N), device="cuda")
@@ -149,14 +165,10 @@ def resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stre
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
     n = [c.cpu().numpy().astype(np.int64) for c in counts]
     nbytes = 2 * B * N + 4 * int(n[0].sum() + n[1].sum() + n[2].sum()) + 3 * 4 * B
-    pm, cm = prev.cpu().numpy(), mask.cpu().numpy()
-    t0 = time.perf_counter()
-    for b in range(B):
-        oracle.resident_delta(cm[b], pm[b])
-    t_cpu = time.perf_counter() - t0
+    leg_inputs["resident_delta"] = (mask.cpu().numpy(), prev.cpu().numpy())
     return {"us": t * 1e6, "hbm_gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
             "bytes": nbytes, "resident_per_row": float(n[0].mean()), "entering_per_row": float(n[1].mean()),
-            "leaving_per_row": float(n[2].mean()), "oracle_us": t_cpu * 1e6}
+            "leaving_per_row": float(n[2].mean())}
 
 
 def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
@@ -241,18 +253,17 @@ def score_fp8_leg(L, r, q, w, comp_k, scores, B, N, sh, stream, steps):
             "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t8 / 1e9 / PEAK_HBM_GBS}
 
 
-def subset_topk_leg(fm, L, r, scores, B, N, sh, stream, steps, resident_k=32768):
+def subset_topk_leg(L, r, scores, B, N, sh, stream, steps, leg_inputs, resident_k=32768):
     """fm_select_topk_subset: a decode step's top-512 within each row's
     resident set.  The resident set is this pass's top-32768 chunks per row
     (12.5% of N, the share of the compressed cache the model card keeps on
     the GPU); the step's scores are seeded uniform stand-ins (the pages do
     not define the step's score function).  HIP-event time per call on the
     launch stream; bytes = the list and the gathered scores (4 B each per
-    entry) plus the chosen indices; the oracle timed on the same inputs."""
-    import numpy as np
+    entry) plus the chosen indices.  Host copies of the step's scores and the
+    lists go into leg_inputs for the CPU baseline."""
     import torch
 
-    import oracle
     keep = torch.empty((B, N), dtype=torch.bool, device="cuda")
     L.fm_select_topk(r.ctx, scores, B, N, None, resident_k, keep, sh)
     sub = torch.empty((B, resident_k), dtype=torch.int32, device="cuda")
@@ -277,13 +288,9 @@ def subset_topk_leg(fm, L, r, scores, B, N, sh, stream, steps, resident_k=32768)
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
     nbytes = B * (8 * resident_k + 4 * TOP_K + 8)
-    st, sb = step.cpu().numpy(), sub.cpu().numpy()
-    t0 = time.perf_counter()
-    for b in range(B):
-        oracle.select_topk_subset(st[b], sb[b], TOP_K)
-    t_cpu = time.perf_counter() - t0
+    leg_inputs["subset_topk"] = (step.cpu().numpy(), sub.cpu().numpy())
     return {"us": t * 1e6, "resident_per_row": resident_k, "top_k": TOP_K, "entries_per_s": B * resident_k / t,
-            "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9, "oracle_us": t_cpu * 1e6}
+            "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9}
 
 
 def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
@@ -399,6 +406,24 @@ def main(argv=None):
         if ev is not None:
             ev[3].record(stream)
 
+    # The next rows of the path and the workload's other modes, each timed on
+    # its own with HIP events, run before the warmup: the chip takes a few
+    # tens of steps of load after idle to reach its steady clock, so the
+    # timed steps start at that clock whatever W is (run right before the
+    # timed steps instead, the legs' own load left them about 1.5% slower).
+    # Their inputs are this pass's outputs: one step (not timed) makes them.
+    # The resident delta compares this cycle's mask with the previous
+    # cycle's (the same pass for the decode token 64 steps earlier:
+    # positions - 256 at 4 tokens per chunk).  The variants leg overwrites
+    # scores and mask, so it runs last.
+    step()
+    leg_inputs = {}
+    resident = resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps, leg_inputs)
+    score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
+    subset = subset_topk_leg(L, r, scores, B, N, sh, stream, args.steps, leg_inputs)
+    masking = mask_logits_leg(L, r, mask, B, N, sh, stream, args.steps)
+    variants = variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, args.steps)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -415,15 +440,6 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Next row of the path: the resident set and recall delta of this cycle's
-    # mask against the previous cycle's (the same pass for the decode token
-    # 64 steps earlier: positions - 256 at 4 tokens per chunk).
-    resident = resident_delta_leg(fm, L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps)
-    score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
-    subset = subset_topk_leg(fm, L, r, scores, B, N, sh, stream, args.steps)
-    masking = mask_logits_leg(L, r, mask, B, N, sh, stream, args.steps)
-    variants = variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, args.steps)
-
     timed = [e for e in events if e is not None]
     prep = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
     score = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
@@ -433,7 +449,7 @@ def main(argv=None):
     t_score = float(score.mean())
     achieved = FLOP_PER_CHUNK * chunks / t_score / 1e12
     traffic = read_traffic(chunks)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, leg_inputs)
     cpu_model = cpu.pop("_cpu_model") if cpu else None
     r.close()
 

@@ -1,10 +1,13 @@
 """bench.py's contract on the host: one GPU only (a clear exit for more),
 the committed HBM-traffic summary belongs to the score kernel as it is,
-and the CPU baseline leg reports the oracle's rate with its core count."""
+and the CPU baseline leg, the only one that touches the oracle, reports its
+rate with its core count."""
 
 import os
 import subprocess
 import sys
+
+import numpy as np
 
 import bench
 
@@ -29,7 +32,28 @@ def test_traffic_summary_matches_the_score_source():
 
 
 def test_cpu_baseline_reports_the_oracle():
-    b = bench.cpu_baseline(0.0)  # one row, the least the leg times
+    """One row, the least the leg times, plus the oracle's resident delta and
+    subset top-K on small host inputs standing in for the legs' copies."""
+    rng = np.random.default_rng(0)
+    legs = {"resident_delta": (rng.random((2, 600)) < 0.1, rng.random((2, 600)) < 0.1),
+            "subset_topk": (rng.random((2, 600)).astype(np.float32),
+                            rng.permutation(600)[:300].astype(np.int32)[None].repeat(2, 0))}
+    b = bench.cpu_baseline(0.0, legs)
     assert b["kind"] == "oracle" and b["unit"] == "chunks/s"
     assert b["value"] > 0 and b["cores"] >= 1
     assert b["sample"].startswith("1 of 30 rows")
+    assert b["next_rows"]["resident_delta_us"] > 0 and b["next_rows"]["subset_topk_us"] > 0
+    assert bench.cpu_baseline(0.0, {})["next_rows"] == {}
+
+
+def test_only_the_cpu_baseline_leg_reaches_the_oracle():
+    """The GPU legs of bench.py never import or call the oracle."""
+    import ast
+    import inspect
+    tree = ast.parse(inspect.getsource(bench))
+    for fn in tree.body:
+        if isinstance(fn, ast.FunctionDef) and fn.name != "cpu_baseline":
+            names = {n.id for n in ast.walk(fn) if isinstance(n, ast.Name)}
+            mods = {a.name for n in ast.walk(fn) if isinstance(n, (ast.Import, ast.ImportFrom))
+                    for a in n.names} | {n.module for n in ast.walk(fn) if isinstance(n, ast.ImportFrom)}
+            assert "oracle" not in names and "oracle" not in mods, fn.name
