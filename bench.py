@@ -82,6 +82,55 @@ def read_traffic(chunks_per_launch: int):
         return None
 
 
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence.  A default
+    event's record also writes back and invalidates the caches at system
+    scope, which lengthens every interval it bounds by 1-2 us; this one only
+    takes the timestamp.  Read it after a device synchronisation.  The HIP
+    functions are looked up through libfm's handle, so they are those of the
+    runtime libfm and torch share."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+
+        if TimingEvent._hip is None:
+            from sparse_attention_chunk_amd import _lib
+            hip = _lib.LIB
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.ev, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end`, as torch.cuda.Event reports."""
+        ms = self._ct.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if TimingEvent._hip is not None and self.ev:
+                TimingEvent._hip.hipEventDestroy(self.ev)
+        except Exception:  # interpreter shutdown
+            pass
+
+
 def cpu_baseline(budget_s: float, leg_inputs: dict):
     """The oracle, as it stands, on whole rows of the workload until the time
     budget is spent (at least one row); chunks/s over the rows done.  Also
@@ -156,7 +205,7 @@ def resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, 
     for _ in range(3):
         call()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
         call()
@@ -199,7 +248,7 @@ def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
     n = max(1, steps // 5)
     for _ in range(n):
         for name, fn in fns:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e = [TimingEvent() for _ in range(2)]
             e[0].record(stream)
             fn()
             e[1].record(stream)
@@ -231,7 +280,7 @@ def score_fp8_leg(L, r, q, w, comp_k, scores, B, N, sh, stream, steps):
     ev = []
     for _ in range(steps):
         for name, fn in fns:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e = [TimingEvent() for _ in range(2)]
             e[0].record(stream)
             fn(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
             e[1].record(stream)
@@ -280,7 +329,7 @@ def subset_topk_leg(L, r, scores, B, N, sh, stream, steps, leg_inputs, resident_
     for _ in range(3):
         call()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
         call()
@@ -311,7 +360,7 @@ def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
     for _ in range(2):
         call()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
         call()
@@ -428,10 +477,10 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    # Per-phase HIP events on every EVENT_STRIDE-th timed step: each event
-    # record costs the stream about 2 us, so recording four on every step
-    # would slow the loop being timed by 2%.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if i % EVENT_STRIDE == 0 else None
+    # Per-phase HIP events on every EVENT_STRIDE-th timed step: each record
+    # still costs the stream about 1 us, so recording four on every step would
+    # slow the loop being timed by about 1%.
+    events = [[TimingEvent() for _ in range(4)] if i % EVENT_STRIDE == 0 else None
               for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 import bench
 
@@ -57,3 +58,27 @@ def test_only_the_cpu_baseline_leg_reaches_the_oracle():
             mods = {a.name for n in ast.walk(fn) if isinstance(n, (ast.Import, ast.ImportFrom))
                     for a in n.names} | {n.module for n in ast.walk(fn) if isinstance(n, ast.ImportFrom)}
             assert "oracle" not in names and "oracle" not in mods, fn.name
+
+
+@pytest.mark.gpu
+def test_timing_event_brackets_the_same_work_as_torch_events():
+    """bench.TimingEvent (no system-scope fence) times 20 fills of 256 MB
+    within a few percent of torch's default events around the same work."""
+    import torch
+    x = torch.empty(1 << 26, device="cuda")
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        x.fill_(1.0)
+    torch.cuda.synchronize()
+    a, b = bench.TimingEvent(), bench.TimingEvent()
+    ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ta.record(s)
+    a.record(s)
+    for _ in range(20):
+        x.fill_(2.0)
+    b.record(s)
+    tb.record(s)
+    torch.cuda.synchronize()
+    t_hip, t_torch = a.elapsed_time(b), ta.elapsed_time(tb)
+    assert 0.8 * t_torch < t_hip <= 1.05 * t_torch + 0.01, (t_hip, t_torch)
+    assert float(x[-1]) == 2.0
