@@ -6,28 +6,36 @@
 //
 // logits [B][R][N] (R logit rows per request row: heads, query positions)
 // are changed in place: -inf where mask[b][n] == 0, untouched elsewhere.
-// Stores are the cost, and they stream fastest as long contiguous runs per
-// block: a block takes one segment of kMaskVecs x 256 16-byte vectors of a
-// request row's chunks and kMaskRows of its logit rows; instruction i of
-// thread t handles vector i * 256 + t, so every store instruction of a block
-// covers 4 KB.  The mask bits of the segment are read once per block, and
-// they are the same for all of the block's logit rows.  Per vector: all
-// kept -> nothing; none kept -> a store of -inf, no read; mixed -> load,
-// select, store.  The loads of a thread's first mixed vector are issued for
-// every row of the block before the -inf stores, so their latency hides
-// behind the stores; the writes of a line's vectors then land close
-// together in time and merge in the L2 cache.  Reads mixed into the write
-// stream are the expensive part: with 0.2% of the chunks kept, 12% of the
-// 128-byte lines hold a kept element.  Rows whose length is not a whole
-// number of vectors use element stores.
+// Stores are the cost.  A block takes one segment of kMaskVecs x 256
+// 16-byte vectors of a request row's chunks and kMaskRows of its logit rows;
+// instruction i of thread t handles vector i * 256 + t, so every store
+// instruction of a block covers 4 KB.  The mask bits of the segment are read
+// once per block, and they are the same for all of the block's logit rows.
+// Per vector: all kept -> nothing; none kept -> a store of -inf, no read;
+// mixed -> load, select, store.  The loads of a thread's first mixed vector
+// are issued for every row of the block before the -inf stores, so their
+// latency hides behind the stores.  With 0.2% of the chunks kept, 12% of the
+// 128-byte lines hold a kept element, and those lines are read as well as
+// written.  Every store is non-temporal: with ordinary stores the reads of
+// the mixed lines slowed the whole write stream (B=30, 64 bf16 logit rows,
+// N=262144: 272 us with a top-512 mask against 192 us with nothing kept);
+// non-temporal, with one vector per thread and four rows per block, 159 us
+// and 166 us (a plain fill of the same bytes: 146 us).  Rows whose length is
+// not a whole number of vectors use element stores.
 #include "fm_internal.h"
 
 namespace fm {
 namespace {
 
 constexpr int kMaskThreads = 256;
-constexpr int kMaskVecs = 8;   // 16-byte vectors per thread per logit row
+constexpr int kMaskVecs = 1;   // 16-byte vectors per thread per logit row
 constexpr int kMaskRows = 4;   // logit rows per block
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
+}
 
 template <typename E>
 struct Elem;
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_logits_kernel(E* __restrict
     for (int r = r0; r < r1; ++r) {
 #pragma unroll
       for (int i = 0; i < kMaskVecs; ++i)
-        if ((none >> i) & 1u) *at(r, i) = fill;
+        if ((none >> i) & 1u) store_nt(at(r, i), fill);
     }
     for (bool first = true; mixed; first = false) {
       const int i = __builtin_ctz(mixed);
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_logits_kernel(E* __restrict
 #pragma unroll
         for (int j = 0; j < V; ++j)
           if (!((k >> j) & 1u)) el[j] = ninf;
-        *at(r0 + rr, i) = v[rr];
+        store_nt(at(r0 + rr, i), v[rr]);
       }
     }
   } else {
