@@ -148,8 +148,9 @@ fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* c
                    const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream);
 
 /* fm_score on the fp8 matrix cores: the native-FP8 indexer form that the
- * model card's "It is / isn't" section names for production.  Same
- * arguments, outputs and error behaviour as fm_score.  The stored e4m3
+ * FlashMemory DS-V4 Retriever README's "Is / is not" section names for
+ * production.  Same arguments, outputs and error behaviour as fm_score.
+ * The stored e4m3
  * codes enter the fp8 MFMA directly; each head's query is scaled by a power
  * of two and split into two e4m3 parts (hi + lo, about 8 significant bits;
  * relative error at most 2^-8 per element), so the scores are less precise

@@ -11,7 +11,7 @@
 // product x . w is formed on the f16 MFMA from two-part operands: at
 // context creation every weight row is scaled by a power of two (its
 // largest entry lands in [2^14, 2^15)) and split into f16 hi + lo parts (4
-// bytes per weight, like fp32); each 256-wide chunk of an activation row is
+// bytes per weight, like fp32); each 128-wide chunk of an activation row is
 // scaled and split the same way while it is staged.  Then
 //   x w = xh wh + xh wl + xl wh  (+ xl wl, about 2^-22 relative, dropped)
 // on three MFMAs, accumulated in fp32, and the scales are undone exactly.

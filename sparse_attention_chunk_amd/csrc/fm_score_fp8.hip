@@ -1,8 +1,8 @@
 // Per-layer chunk score and ensemble on the fp8 matrix cores: the same
 // definition as fm_score.hip (FlashMemory DS-V4 Retriever README,
 // "compressed_k format", "Architecture" score line, "Joint checkpoint +
-// ensemble"), in the native-FP8 indexer form the FlashMemory-DeepSeek-V4
-// model card names for production ("It is / isn't").
+// ensemble"), in the native-FP8 indexer form that the same README's "Is /
+// is not" section names for production.
 //
 // The e4m3 codes of the records enter the 16x16x128 fp8 MFMA as stored (no
 // decode); the queries are split into two e4m3 parts:

@@ -1,10 +1,10 @@
 """The retriever interface of the FlashMemory DS-V4 README ("Usage") over libfm.
 
-    model = FlashMemoryRetriever(weights)                  # device fp32 weights
-    per_layer = model(hidden, comp_k, positions)           # {"l10","l12","l20"}: [B, N]
-    scores = model.ensemble(hidden, comp_k, positions, mode="max")     # [B, N]
-    keep = model.select_topk(hidden, comp_k, positions, top_k=512)     # bool [B, N]
-    keep = model.select_topk(hidden, comp_k, positions, threshold=0.5)
+FlashMemoryRetriever wraps one libfm context built from device fp32 weights.
+Calling it on (hidden, comp_k, positions) returns the three layers' scores
+keyed by layer name; ensemble() combines them by max or mean; select_topk()
+turns the ensemble into a boolean keep mask, either the top_k best chunks or
+those above a threshold (exactly one of the two).
 
 Also the three stages on their own (prepare_query, score, keep_topk /
 keep_threshold).  Torch only allocates outputs and supplies the stream; the

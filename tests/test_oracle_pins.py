@@ -394,6 +394,139 @@ def test_run_row_modes_exclusive():
     assert list(r["mask"]) == [1, 1, 0]          # all scores 0.5: ties to the lowest indices
 
 
+# --------------------------------------------------------------------------- assemblers: prepare_query, run_row
+
+def _assembler_cfg():
+    # README "Architecture" on tiny sizes: 2 hidden dims, rank 2, 2 heads of
+    # 4 dims, RoPE over all 4 dims (pairs (0, 1) and (2, 3)), eps 0 so that
+    # the RMS divisions come out exact.  theta_j = base^(-2j/4): theta_0 = 1
+    # and, with base = 4 / pi^2, theta_1 = pi / 2, so position 1 turns pair
+    # (2, 3) by a quarter turn and position 2 by a half turn.  The weights
+    # keep pair (0, 1) at zero, where any angle leaves it unchanged.
+    return OracleConfig(hidden=2, q_lora_rank=2, n_heads=2, head_dim=4, rope_dim=4, rms_eps=0.0,
+                        rope_base=4.0 / math.pi ** 2, n_layers=2)
+
+
+def _assembler_weights():
+    z = [0.0, 0.0]
+    l0 = {"wq_a": np.eye(2), "q_norm": np.array([1.0, 1.0]),
+          # head 0 dims 2, 3 <- (a0, a1); head 1 dims 2, 3 <- (a1, a0)
+          "wq_b": np.array([z, z, [1.0, 0.0], [0.0, 1.0], z, z, [0.0, 1.0], [1.0, 0.0]]),
+          "w_proj": np.eye(2)}
+    l1 = {"wq_a": 2.0 * np.eye(2), "q_norm": np.array([2.0, 1.0]),
+          # head 0 dims 2, 3 <- (a0 + a1, a0 - a1); head 1 dim 3 <- a0
+          "wq_b": np.array([z, z, [1.0, 1.0], [1.0, -1.0], z, z, z, [1.0, 0.0]]),
+          "w_proj": np.array([[0.0, 1.0], [1.0, 0.0]])}
+    return [l0, l1]
+
+
+def test_prepare_query_hand_worked_layers_rows_positions():
+    """Two layers x two rows at distinct positions, worked by hand.
+
+    Row 0: h = (1, 7) at position 1; row 1: h = (-7, 1) at position 2.
+    Per head the (2, 3) pair (x, y) is turned counter-clockwise ((-y, x) at a
+    quarter turn, (-x, -y) at a half turn), then the normalized 4-point
+    Hadamard maps (0, 0, x', y') to (x'+y', x'-y', -x'-y', -x'+y') / 2.
+    w = W_p h * (4 * 2)^-1/2.
+
+    layer 0, row 0: a = (1, 7), mean a^2 = 25, a_hat = (0.2, 1.4)
+      head 0: (0.2, 1.4) -> (-1.4, 0.2) -> (-0.6, -0.8, 0.6, 0.8)
+      head 1: (1.4, 0.2) -> (-0.2, 1.4) -> (0.6, -0.8, -0.6, 0.8)
+    layer 0, row 1: a = (-7, 1), a_hat = (-1.4, 0.2)
+      head 0: (-1.4, 0.2) -> (1.4, -0.2) -> (0.6, 0.8, -0.6, -0.8)
+      head 1: (0.2, -1.4) -> (-0.2, 1.4) -> (0.6, -0.8, -0.6, 0.8)
+    layer 1, row 0: a = (2, 14), mean a^2 = 100, a_hat = (0.2, 1.4) * (2, 1) = (0.4, 1.4)
+      head 0: (1.8, -1.0) -> (1.0, 1.8) -> (1.4, -0.4, -1.4, 0.4)
+      head 1: (0.0, 0.4) -> (-0.4, 0.0) -> (-0.2, -0.2, 0.2, 0.2)
+    layer 1, row 1: a = (-14, 2), a_hat = (-2.8, 0.2)
+      head 0: (-2.6, -3.0) -> (2.6, 3.0) -> (2.8, -0.2, -2.8, 0.2)
+      head 1: (0.0, -2.8) -> (0.0, 2.8) -> (1.4, -1.4, -1.4, 1.4)
+    w: layer 0 rows (1, 7) and (-7, 1); layer 1 (swapped W_p) rows (7, 1) and (1, -7), each / sqrt(8).
+    """
+    cfg = _assembler_cfg()
+    hidden = np.array([[1.0, 7.0], [-7.0, 1.0]])
+    positions = np.array([1, 2], dtype=np.int64)
+    q, w = oracle.prepare_query(_assembler_weights(), hidden, positions, cfg)
+    want_q = np.array([
+        [[[-0.6, -0.8, 0.6, 0.8], [0.6, -0.8, -0.6, 0.8]],
+         [[0.6, 0.8, -0.6, -0.8], [0.6, -0.8, -0.6, 0.8]]],
+        [[[1.4, -0.4, -1.4, 0.4], [-0.2, -0.2, 0.2, 0.2]],
+         [[2.8, -0.2, -2.8, 0.2], [1.4, -1.4, -1.4, 1.4]]],
+    ])
+    want_w = np.array([[[1.0, 7.0], [-7.0, 1.0]], [[7.0, 1.0], [1.0, -7.0]]]) / math.sqrt(8.0)
+    assert q.shape == (2, 2, 2, 4) and w.shape == (2, 2, 2)
+    np.testing.assert_allclose(q, want_q, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(w, want_w, rtol=0, atol=1e-15)
+    # the positions belong to their rows: swapped, row 0 head 0 turns by a half turn
+    q_sw, _ = oracle.prepare_query(_assembler_weights(), hidden, positions[::-1].copy(), cfg)
+    np.testing.assert_allclose(q_sw[0, 0, 0], [-0.8, 0.6, 0.8, -0.6], rtol=0, atol=1e-12)
+
+
+def _run_row_case():
+    """Two one-head layers whose prepared queries are unit vectors.
+
+    h = (1, 1), wq_a = I, eps 0: a_hat = (1, 1).  Layer 0's wq_b rows are all
+    (1/4, 1/4), so q_lin = (1, 1, 1, 1) / 2 and, at position 0 (no turn), the
+    normalized Hadamard gives q = (1, 0, 0, 0); layer 1's rows carry signs
+    (+, -, +, -), giving q = (0, 1, 0, 0).  W_p = (ln 3, ln 3) and the scale
+    (4 * 1)^-1/2 give w = ln 3 in both layers.  Keys (scale 0.5, codes 2 k):
+      chunk 0: k = (2, 0, 0, 0)   layer logits (2 ln 3, 0)  -> scores (0.9, 0.5)
+      chunk 1: k = (1, 1, 0, 0)   (ln 3, ln 3)              -> (0.75, 0.75)
+      chunk 2: k = (-1, -1, 0, 0) (0, 0)                    -> (0.5, 0.5)
+      chunk 3: k = (0, 2, 0, 0)   (0, 2 ln 3)               -> (0.5, 0.9)
+      chunk 4: k = (1, 0, 0, 0)   (ln 3, 0)                 -> (0.75, 0.5)
+    since sigmoid(ln 3) = 3/4 and sigmoid(2 ln 3) = 9/10.
+    """
+    cfg = OracleConfig(hidden=2, q_lora_rank=2, n_heads=1, head_dim=4, rope_dim=4, rms_eps=0.0, n_layers=2)
+    ln3 = math.log(3.0)
+    quarter = np.full((4, 2), 0.25)
+    signs = np.array([[1.0], [-1.0], [1.0], [-1.0]])
+    layers = [{"wq_a": np.eye(2), "q_norm": np.ones(2), "wq_b": quarter, "w_proj": np.array([[ln3, ln3]])},
+              {"wq_a": np.eye(2), "q_norm": np.ones(2), "wq_b": quarter * signs, "w_proj": np.array([[ln3, ln3]])}]
+    codes = {0.0: 0x00, 2.0: 0x40, 4.0: 0x48, -2.0: 0xC0}  # e4m3fn: 2 = 0.1000.000, 4 = 0.1001.000
+    keys = [(2, 0), (1, 1), (-1, -1), (0, 2), (1, 0)]
+    rec = np.zeros((5, 8), np.uint8)
+    for n, (k0, k1) in enumerate(keys):
+        rec[n, 0] = codes[2.0 * k0]
+        rec[n, 1] = codes[2.0 * k1]
+        rec[n, 4:8] = np.frombuffer(np.array([0.5], "<f4").tobytes(), np.uint8)
+    return cfg, layers, np.ones(2), rec
+
+
+def test_run_row_hand_worked_max_and_mean():
+    cfg, layers, h, rec = _run_row_case()
+    per_layer = np.array([[0.9, 0.75, 0.5, 0.5, 0.75], [0.5, 0.75, 0.5, 0.9, 0.5]])
+    r = oracle.run_row(layers, h, 0, rec, cfg, mode="max", top_k=1)
+    np.testing.assert_allclose(r["q"], [[[1, 0, 0, 0]], [[0, 1, 0, 0]]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["w"], [[math.log(3.0)]] * 2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["per_layer"], per_layer, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["scores"], [0.9, 0.75, 0.5, 0.9, 0.75], rtol=0, atol=1e-15)
+    assert list(r["mask"]) == [1, 0, 0, 0, 0]                     # 0.9 ties: chunk 0 before chunk 3
+    r = oracle.run_row(layers, h, 0, rec, cfg, mode="mean", top_k=1)
+    np.testing.assert_allclose(r["scores"], [0.7, 0.75, 0.5, 0.7, 0.625], rtol=0, atol=1e-15)
+    assert list(r["mask"]) == [0, 1, 0, 0, 0]                     # the mean ranks chunk 1 first
+    r = oracle.run_row(layers, h, 0, rec, cfg, mode="max", top_k=3)
+    assert list(r["mask"]) == [1, 1, 0, 1, 0]                     # 0.75 ties: chunk 1 before chunk 4
+    r = oracle.run_row(layers, h, 0, rec, cfg, mode="max", threshold=0.72)
+    assert list(r["mask"]) == [1, 1, 0, 1, 1]
+    r = oracle.run_row(layers, h, 0, rec, cfg, mode="mean", threshold=0.72)
+    assert list(r["mask"]) == [0, 1, 0, 0, 0]
+
+
+def test_run_row_hand_worked_valid_n():
+    cfg, layers, h, rec = _run_row_case()
+    r = oracle.run_row(layers, h, 0, rec, cfg, valid_n=3, mode="max", threshold=0.72)
+    np.testing.assert_allclose(r["scores"][:3], [0.9, 0.75, 0.5], rtol=0, atol=1e-15)
+    assert np.all(np.isneginf(r["scores"][3:])) and np.all(np.isneginf(r["per_layer"][:, 3:]))
+    assert list(r["mask"]) == [1, 1, 0, 0, 0]                     # chunks 3 and 4 lie past valid_n
+    r = oracle.run_row(layers, h, 0, rec, cfg, valid_n=3, mode="mean", top_k=2)
+    assert list(r["mask"]) == [1, 1, 0, 0, 0]
+    r = oracle.run_row(layers, h, 0, rec, cfg, valid_n=3, mode="max", top_k=5)
+    assert list(r["mask"]) == [1, 1, 1, 0, 0]                     # K above valid_n keeps every valid chunk
+    r = oracle.run_row(layers, h, 0, rec, cfg, valid_n=0, mode="max", top_k=2)
+    assert r["mask"].sum() == 0 and np.all(np.isneginf(r["scores"]))
+
+
 # --------------------------------------------------------------------------- resident set and recall delta
 
 def _delta_by_sets(mask, prev):
