@@ -15,7 +15,14 @@ committed rocprofv3 counter summary when that summary was taken on the
 current score-kernel source, else null.  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on this host, and under
 `next_rows` on the inputs the resident-delta and subset top-K legs ran on.
-The next-row and variant legs run before the W warmup and K timed steps.
+The next-row and variant legs run before the W warmup steps.  After the
+warmup, untimed steps continue until at least --settle-seconds of
+back-to-back load have run (the chip raises its clock over the first
+fraction of a second of load after idle), then the K timed steps run.
+`configs` times the other four seeded workloads (B=1 N=4096; B=8 N=65536
+planted; B=32 N=131072 mean/threshold; B=60 N=131072 ragged YaRN top-1024)
+the same way, each with its own oracle baseline; the headline `value` is
+the B=30 N=262144 workload.
 """
 
 from __future__ import annotations
@@ -39,7 +46,11 @@ SCORE_BYTES_PER_CHUNK = 132 + 4        # record read + ensemble score written
 PEAK_F16_TFLOPS = 2500.0               # MI355X dense f16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0               # MI355X dense fp8 MFMA
-SCORE_SRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc", "fm_score.hip")
+CSRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc")
+# Everything the score kernel's code and launch shape come from: a change to
+# any of them voids the committed counter summary.
+SCORE_SRCS = [os.path.join(CSRC, f) for f in ("fm_score.hip", "fm_score_common.h", "fm_internal.h", "fm_api.hip")]
+QUERY_WEIGHT_BYTES = 3 * (1024 * 4096 + 1024 + 8192 * 1024 + 64 * 4096) * 4   # fp32 weights of the query branch
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_b30_n262144_pmc.txt")
 
 
@@ -51,6 +62,9 @@ def parse_args(argv=None):
     # under this load: five warmup steps time the ramp (about 415 us per step
     # instead of 370 us).
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="untimed back-to-back steps after the warmup until this much load has run")
+    ap.add_argument("--no-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -59,17 +73,21 @@ def parse_args(argv=None):
 
 
 def source_digest() -> str:
-    with open(SCORE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the score kernel's sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in SCORE_SRCS:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
-def read_traffic(chunks_per_launch: int):
+def read_traffic(chunks_per_launch: int, summary: str = PMC_SUMMARY):
     """HBM bytes per score launch from the committed counter summary, or None
     if it is missing or was taken on another version of the score kernel."""
-    if not os.path.exists(PMC_SUMMARY):
+    if not os.path.exists(summary):
         return None
     vals = {}
-    with open(PMC_SUMMARY) as f:
+    with open(summary) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -131,11 +149,141 @@ class TimingEvent:
             pass
 
 
-def cpu_baseline(budget_s: float, leg_inputs: dict):
+class ClockSampler:
+    """Samples the GPU's firmware metrics (amdsmi gpu_metrics: GFX clocks,
+    memory clock, socket power) from a background thread while running.
+    The firmware reports clocks averaged over its own short window, which
+    is closer to the shader clock kernels run at than the target clock the
+    SMI's clock query shows.  Fails soft: summary() is None when amdsmi or
+    the metrics table is unavailable."""
+
+    KEYS = ("average_gfxclk_frequency", "current_gfxclk", "current_gfxclks", "current_uclk",
+            "average_uclk_frequency", "average_socket_power", "current_socket_power")
+
+    def __init__(self, period_s: float = 0.01):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self.error = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:  # no amdsmi, no metrics table, no permission
+            self.error = f"{type(e).__name__}: {e}"
+            self._handle = None
+
+    def _read(self) -> dict:
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        out = {}
+        for k in self.KEYS:
+            v = m.get(k)
+            if isinstance(v, (list, tuple)):
+                v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 65535]
+                if v:
+                    out[k] = sum(v) / len(v)
+            elif isinstance(v, (int, float)) and 0 < v < 65535:
+                out[k] = float(v)
+        return out
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+        self.samples = []
+        self._stop.clear()
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+            self._thread = None
+        return self
+
+    def summary(self):
+        if self._handle is None or not self.samples:
+            return None if self.error is None else {"error": self.error}
+        out = {"samples": len(self.samples), "source": "amdsmi gpu_metrics"}
+        for k in self.KEYS:
+            vals = [smp[k] for smp in self.samples if k in smp]
+            if vals:
+                out[k] = {"mean": sum(vals) / len(vals), "min": min(vals), "max": max(vals)}
+        return out
+
+
+def settle(step, stream, min_s: float, block: int = 50):
+    """Untimed back-to-back steps until at least min_s seconds of load have
+    run, in blocks of `block` steps (one synchronisation per block).
+    Returns the number of steps, the seconds and the per-step time of the
+    first and last block (the clock ramp)."""
+    import torch
+
+    steps = 0
+    per_block = []
+    t0 = time.perf_counter()
+    while True:
+        t1 = time.perf_counter()
+        for _ in range(block):
+            step()
+        torch.cuda.synchronize()
+        per_block.append((time.perf_counter() - t1) / block)
+        steps += block
+        if time.perf_counter() - t0 >= min_s:
+            break
+    return {"steps": steps, "seconds": time.perf_counter() - t0, "first_block_us_per_step": per_block[0] * 1e6,
+            "last_block_us_per_step": per_block[-1] * 1e6}
+
+
+def _parity(ref: dict, gpu_scores, gpu_mask, valid_n: int, top_k, threshold, band: float = 2e-3) -> dict:
+    """One row's GPU outputs against the oracle's: the largest score error
+    over the valid chunks, and the mask entries that differ, split into
+    those whose oracle score lies within `band` of the K-th score (or of the
+    threshold) and the others (the acceptance rule allows only the first)."""
+    import numpy as np
+
+    s_ref = ref["scores"][:valid_n]
+    err = float(np.max(np.abs(gpu_scores[:valid_n].astype(np.float64) - s_ref))) if valid_n else 0.0
+    cut = threshold if top_k is None else (np.sort(s_ref)[::-1][min(top_k, valid_n) - 1] if valid_n else 0.0)
+    diff = np.asarray(gpu_mask, np.uint8) != ref["mask"]
+    near = np.zeros_like(diff)
+    near[:valid_n] = np.abs(s_ref - cut) <= band
+    return {"max_abs_score_err": err, "mask_diff_in_band": int((diff & near).sum()),
+            "mask_diff_outside_band": int((diff & ~near).sum())}
+
+
+def _merge_parity(acc: dict | None, p: dict) -> dict:
+    if acc is None:
+        return dict(p, rows=1)
+    return {"max_abs_score_err": max(acc["max_abs_score_err"], p["max_abs_score_err"]),
+            "mask_diff_in_band": acc["mask_diff_in_band"] + p["mask_diff_in_band"],
+            "mask_diff_outside_band": acc["mask_diff_outside_band"] + p["mask_diff_outside_band"],
+            "rows": acc["rows"] + 1}
+
+
+def cpu_baseline(budget_s: float, leg_inputs: dict, config_inputs: dict | None = None,
+                 config_budget_s: float = 3.0):
     """The oracle, as it stands, on whole rows of the workload until the time
     budget is spent (at least one row); chunks/s over the rows done.  Also
     times the oracle's resident delta and subset top-K on the host copies of
-    the inputs the next-row legs ran on (all B rows each)."""
+    the inputs the next-row legs ran on (all B rows each), and, under
+    `configs`, whole rows of each other workload on the host copies of the
+    inputs its GPU leg ran on (valid chunks only, config_budget_s each)."""
     import numpy as np
 
     import oracle
@@ -152,11 +300,15 @@ def cpu_baseline(budget_s: float, leg_inputs: dict):
     cfg = oracle.OracleConfig()
     rows = 0
     elapsed = 0.0
+    parity = None
     while rows < wl.batch:
         comp = synth.make_comp_k(wl, rows=[rows])[0]   # generation is outside the timed part
         t1 = time.perf_counter()
-        oracle.run_row(weights, hidden[rows], int(pos[rows]), comp, cfg, mode="max", top_k=TOP_K)
+        ref = oracle.run_row(weights, hidden[rows], int(pos[rows]), comp, cfg, mode="max", top_k=TOP_K)
         elapsed += time.perf_counter() - t1
+        if "headline" in leg_inputs:
+            g_scores, g_mask = leg_inputs["headline"]
+            parity = _merge_parity(parity, _parity(ref, g_scores[rows], g_mask[rows], wl.n_chunks, TOP_K, None))
         rows += 1
         if elapsed >= budget_s:
             break
@@ -173,10 +325,32 @@ def cpu_baseline(budget_s: float, leg_inputs: dict):
         for b in range(step.shape[0]):
             oracle.select_topk_subset(step[b], sub[b], TOP_K)
         next_rows["subset_topk_us"] = (time.perf_counter() - t1) * 1e6
+    configs = {}
+    for cid, inp in (config_inputs or {}).items():
+        cwl = synth.WORKLOADS[cid]
+        ccfg = oracle.OracleConfig(yarn_factor=cwl.yarn_factor, yarn_orig_ctx=cwl.yarn_orig_ctx,
+                                   yarn_beta_fast=cwl.yarn_beta_fast, yarn_beta_slow=cwl.yarn_beta_slow)
+        done = chunks = 0
+        spent = 0.0
+        cpar = None
+        while done < cwl.batch:
+            vn = int(inp["valid_n"][done])
+            t1 = time.perf_counter()
+            ref = oracle.run_row(weights, inp["hidden"][done], int(inp["positions"][done]), inp["comp_k"][done],
+                                 ccfg, valid_n=vn, mode=cwl.mode, top_k=cwl.top_k, threshold=cwl.threshold)
+            spent += time.perf_counter() - t1
+            cpar = _merge_parity(cpar, _parity(ref, inp["scores"][done], inp["mask"][done], vn, cwl.top_k,
+                                               cwl.threshold))
+            done += 1
+            chunks += vn
+            if spent >= config_budget_s:
+                break
+        configs[cwl.name] = {"value": chunks / spent, "unit": "chunks/s", "rows": done, "valid_chunks": chunks,
+                             "seconds": spent, "parity": cpar}
     return {"value": rows * wl.n_chunks / elapsed, "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} of {wl.batch} rows x {wl.n_chunks} chunks (query prep, 3-layer score, max "
                       f"ensemble, top-{TOP_K}), fp64 numpy, {elapsed:.1f} s",
-            "next_rows": next_rows, "_cpu_model": _cpu_model()}
+            "parity": parity, "next_rows": next_rows, "configs": configs, "_cpu_model": _cpu_model()}
 
 
 def resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, steps, leg_inputs):
@@ -378,6 +552,124 @@ def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
             "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS}
 
 
+def config_leg(cid: int, weights_dev, steps: int, settle_s: float, config_inputs: dict, flush_bytes: int = 1 << 29):
+    """One of the other seeded workloads on its own context: the whole pass
+    (fm_prepare_query, fm_score with the workload's ensemble, its top-K or
+    threshold selection, valid_n for ragged rows) timed like the headline
+    (settle, then `steps` back-to-back steps between two HIP events), plus
+    per-phase events on a second run of `steps` steps (medians).  Workloads
+    whose inputs fit the 256 MB Infinity Cache (B=1 N=4096, B=8 N=65536) are
+    also timed flushed: a 512 MB device fill before each step evicts it, and
+    events bracket the step alone.  Rates count valid chunks only.  The
+    planted workload plants along the queries fm_prepare_query returns for
+    its rows (the tests plant along the oracle's; the two agree to about
+    1e-6).  Host copies of the inputs go into config_inputs[cid] for the CPU
+    baseline."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_attention_chunk_amd as fm
+
+    wl = synth.WORKLOADS[cid]
+    B, N = wl.batch, wl.n_chunks
+    L = fm._lib
+    yarn = None
+    if wl.yarn_factor != 1.0:
+        yarn = {"factor": wl.yarn_factor, "orig_ctx": wl.yarn_orig_ctx, "beta_fast": wl.yarn_beta_fast,
+                "beta_slow": wl.yarn_beta_slow}
+    r = fm.FlashMemoryRetriever(weights_dev, max_batch=B, max_n=N, yarn=yarn)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hidden_np, pos_np, vn_np = synth.make_hidden(wl), synth.make_positions(wl), synth.make_valid_n(wl)
+    hidden = torch.from_numpy(hidden_np).cuda()
+    pos = torch.from_numpy(pos_np).cuda()
+    q = torch.empty((3, B, 64, 128), device="cuda")
+    w = torch.empty((3, B, 64), device="cuda")
+    dirs = None
+    if wl.plant_fraction > 0:
+        L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, sh)
+        qh = q.cpu().numpy()
+        dirs = {b: qh[:, b] for b in range(B)}
+    comp_np = synth.make_comp_k(wl, plant_dirs=dirs)
+    comp_k = torch.from_numpy(comp_np).cuda()
+    valid_n = torch.from_numpy(vn_np).cuda() if wl.ragged else None
+    scores = torch.empty((B, N), device="cuda")
+    mask = torch.empty((B, N), dtype=torch.bool, device="cuda")
+    mode = L.FM_ENSEMBLE_MEAN if wl.mode == "mean" else L.FM_ENSEMBLE_MAX
+    valid = int(vn_np.astype(np.int64).sum())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        L.fm_score(r.ctx, q, w, comp_k, B, N, valid_n, mode, scores, None, sh)
+        if ev is not None:
+            ev[2].record(stream)
+        if wl.top_k is not None:
+            L.fm_select_topk(r.ctx, scores, B, N, valid_n, wl.top_k, mask, sh)
+        else:
+            L.fm_select_threshold(r.ctx, scores, B, N, valid_n, wl.threshold, mask, sh)
+        if ev is not None:
+            ev[3].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    st = settle(step, stream, settle_s)
+    ends = [TimingEvent(), TimingEvent()]
+    ends[0].record(stream)
+    for _ in range(steps):
+        step()
+    ends[1].record(stream)
+    torch.cuda.synchronize()
+    t_step = ends[0].elapsed_time(ends[1]) * 1e-3 / steps
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ph = np.array([[e[i].elapsed_time(e[i + 1]) * 1e-3 for i in range(3)] for e in evs])
+    t_prep, t_score, t_sel = (float(np.median(ph[:, i])) for i in range(3))
+    out = {
+        "workload": wl.name, "batch": B, "n_chunks": N, "valid_chunks": valid,
+        "ensemble": wl.mode, "select": f"top-{wl.top_k}" if wl.top_k is not None else f"threshold {wl.threshold}",
+        "step_us": t_step * 1e6, "step_chunks_per_s": valid / t_step,
+        "chunks_per_s": valid / (t_score + t_sel),
+        "breakdown_us": {"prepare_query": t_prep * 1e6, "score": t_score * 1e6, "select": t_sel * 1e6},
+        "score_tflops": FLOP_PER_CHUNK * valid / t_score / 1e12,
+        "score_mfma_frac": FLOP_PER_CHUNK * valid / t_score / 1e12 / PEAK_F16_TFLOPS,
+        "score_hbm_gbs": SCORE_BYTES_PER_CHUNK * valid / t_score / 1e9,
+        "score_hbm_frac": SCORE_BYTES_PER_CHUNK * valid / t_score / 1e9 / PEAK_HBM_GBS,
+        "select_hbm_gbs": 5 * valid / t_sel / 1e9,
+        "prepare_hbm_gbs": QUERY_WEIGHT_BYTES / t_prep / 1e9,
+        "settle": st,
+    }
+    if comp_np.nbytes + QUERY_WEIGHT_BYTES < (256 << 20):
+        junk = torch.empty(flush_bytes // 4, device="cuda")
+        fl = []
+        for i in range(steps):
+            junk.fill_(float(i))
+            e = [TimingEvent(), TimingEvent()]
+            e[0].record(stream)
+            step()
+            e[1].record(stream)
+            fl.append(e)
+        torch.cuda.synchronize()
+        t_fl = float(np.median([e[0].elapsed_time(e[1]) for e in fl])) * 1e-3
+        out["flushed"] = {"step_us": t_fl * 1e6, "step_chunks_per_s": valid / t_fl,
+                          "note": "512 MB device fill before each step evicts the Infinity Cache; events "
+                                  "bracket the step alone (median)"}
+        del junk
+    step()
+    config_inputs[cid] = {"hidden": hidden_np, "positions": pos_np, "valid_n": vn_np, "comp_k": comp_np,
+                          "scores": scores.cpu().numpy(), "mask": mask.cpu().numpy()}
+    r.close()
+    del comp_k
+    torch.cuda.empty_cache()
+    return out
+
+
 def _rocm_version() -> str:
     try:
         with open("/opt/rocm/.info/version") as f:
@@ -476,6 +768,13 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Back-to-back load right before the timed steps, whatever W is: after the
+    # legs' host work the chip idles briefly and lowers its clock again.  The
+    # firmware's clock and power figures are sampled over this phase (not
+    # over the timed steps, which the sampling thread would perturb).
+    clocks = ClockSampler().start()
+    settled = settle(step, stream, args.settle_seconds)
+    clocks.stop()
 
     # Per-phase HIP events on every EVENT_STRIDE-th timed step: each record
     # still costs the stream about 1 us, so recording four on every step would
@@ -498,9 +797,19 @@ def main(argv=None):
     t_score = float(score.mean())
     achieved = FLOP_PER_CHUNK * chunks / t_score / 1e12
     traffic = read_traffic(chunks)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, leg_inputs)
-    cpu_model = cpu.pop("_cpu_model") if cpu else None
+    leg_inputs["headline"] = (scores.cpu().numpy(), mask.cpu().numpy())
     r.close()
+    del comp_k
+    torch.cuda.empty_cache()
+    configs = {}
+    config_inputs = {}
+    if not args.no_configs:
+        for cid in (1, 2, 3, 4):
+            print(f"# workload {cid}: {synth.WORKLOADS[cid].name}", file=sys.stderr, flush=True)
+            configs[synth.WORKLOADS[cid].name] = config_leg(cid, weights, args.steps, 0.5, config_inputs)
+    print("# cpu baseline", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, leg_inputs, config_inputs)
+    cpu_model = cpu.pop("_cpu_model") if cpu else None
 
     out = {
         "metric": METRIC,
@@ -543,6 +852,9 @@ def main(argv=None):
         "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
                       "mask_logits": masking},
         "workload_variants": variants,
+        "settle": dict(settled, note="untimed back-to-back steps after the warmup, before the timed steps"),
+        "clocks": clocks.summary(),
+        "configs": configs,
         "host_cpu": cpu_model,
         "software": {"rocm": _rocm_version(), "torch": torch.__version__},
     }

@@ -22,14 +22,27 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_traffic_summary_matches_the_score_source():
-    """profiles/ holds FETCH/WRITE counters taken on this fm_score.hip: the
-    bench reads its bytes per launch (about 1.014x the algorithmic 136 B per
-    chunk at B=30, N=262144)."""
-    t = bench.read_traffic(30 * 262144)
-    assert t is not None, "counter summary missing or taken on another version of fm_score.hip"
+def test_traffic_summary_tied_to_the_score_source(tmp_path):
+    """The bench reads HBM bytes per launch from a counter summary only when
+    the summary's digest is that of the score kernel's sources as they are;
+    a stale summary gives null.  When the committed summary is current, its
+    bytes are about the algorithmic 136 B per chunk at B=30, N=262144."""
     algorithmic = 30 * 262144 * bench.SCORE_BYTES_PER_CHUNK
-    assert 0.99 * algorithmic < t < 1.10 * algorithmic
+    good = tmp_path / "good.txt"
+    good.write_text(f"# x\nscore_source_sha256: {bench.source_digest()}\nhbm_bytes_per_launch: 1084266125\n")
+    assert bench.read_traffic(30 * 262144, str(good)) == 1084266125.0
+    stale = tmp_path / "stale.txt"
+    stale.write_text("score_source_sha256: " + "0" * 64 + "\nhbm_bytes_per_launch: 1084266125\n")
+    assert bench.read_traffic(30 * 262144, str(stale)) is None
+    assert bench.read_traffic(30 * 262144, str(tmp_path / "missing.txt")) is None
+    t = bench.read_traffic(30 * 262144)
+    if t is not None:
+        assert 0.99 * algorithmic < t < 1.10 * algorithmic
+
+
+def test_source_digest_covers_the_shared_score_headers():
+    names = [os.path.basename(p) for p in bench.SCORE_SRCS]
+    assert {"fm_score.hip", "fm_score_common.h", "fm_internal.h"} <= set(names)
 
 
 def test_cpu_baseline_reports_the_oracle():
@@ -41,14 +54,43 @@ def test_cpu_baseline_reports_the_oracle():
                             rng.permutation(600)[:300].astype(np.int32)[None].repeat(2, 0))}
     b = bench.cpu_baseline(0.0, legs)
     assert b["kind"] == "oracle" and b["unit"] == "chunks/s"
+    assert b["parity"] is None and b["configs"] == {}
     assert b["value"] > 0 and b["cores"] >= 1
     assert b["sample"].startswith("1 of 30 rows")
     assert b["next_rows"]["resident_delta_us"] > 0 and b["next_rows"]["subset_topk_us"] > 0
     assert bench.cpu_baseline(0.0, {})["next_rows"] == {}
 
 
+def test_cpu_baseline_times_and_checks_the_other_workloads():
+    """Per workload, the leg times the oracle on whole rows of the inputs the
+    GPU leg ran on and compares the GPU's outputs with the oracle's: here
+    the oracle's own outputs stand in for the GPU's, so every difference is
+    zero; a flipped mask entry far from the cut-off counts as outside the
+    band."""
+    import oracle
+    import synth
+    wl = synth.WORKLOADS[1]
+    weights = synth.make_weights()
+    inp = {"hidden": synth.make_hidden(wl), "positions": synth.make_positions(wl),
+           "valid_n": synth.make_valid_n(wl), "comp_k": synth.make_comp_k(wl)}
+    ref = oracle.run_row(weights, inp["hidden"][0], int(inp["positions"][0]), inp["comp_k"][0],
+                         oracle.OracleConfig(), mode="max", top_k=512)
+    inp["scores"] = ref["scores"][None].astype(np.float32)
+    inp["mask"] = ref["mask"][None].copy()
+    b = bench.cpu_baseline(0.0, {}, {1: inp}, config_budget_s=0.0)
+    c = b["configs"][wl.name]
+    assert c["rows"] == 1 and c["valid_chunks"] == 4096 and c["value"] > 0
+    assert c["parity"]["rows"] == 1 and c["parity"]["max_abs_score_err"] < 1e-7
+    assert c["parity"]["mask_diff_outside_band"] == 0
+    low = int(np.argmin(ref["scores"]))
+    inp["mask"][0, low] ^= 1
+    c = bench.cpu_baseline(0.0, {}, {1: inp}, config_budget_s=0.0)["configs"][wl.name]
+    assert c["parity"]["mask_diff_outside_band"] == 1
+
+
 def test_only_the_cpu_baseline_leg_reaches_the_oracle():
-    """The GPU legs of bench.py never import or call the oracle."""
+    """The GPU legs of bench.py never import or call the oracle (the parity
+    helpers take the oracle's outputs from the CPU-baseline leg)."""
     import ast
     import inspect
     tree = ast.parse(inspect.getsource(bench))
