@@ -37,9 +37,11 @@ inline int proj1_splits(int) { return kHidden / kSliceK; }
 
 // Score kernel: per request row the packed fp16 queries are 48 MFMA
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,
-// then 4 fragments (one per k-step) of the per-layer weighted query sums.
+// then one fp8 fragment (64 lanes x 32 bytes) of the per-layer weighted
+// query sums in three e4m3 parts and their three power-of-two scales; a
+// row takes kQFrags 1 KB units.
 constexpr int kQHeadFrags = kLayers * 4 * 4;
-constexpr int kQFrags = kQHeadFrags + 4;
+constexpr int kQFrags = kQHeadFrags + 3;
 // fp8 score path: per request row 24 fragments of 64 lanes x 32 e4m3 bytes
 // (3 layers x 4 head tiles x {hi, lo} parts), then one fragment of the
 // per-layer weighted query sums in three parts; per (row, layer) the halved

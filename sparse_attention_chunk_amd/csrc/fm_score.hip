@@ -7,7 +7,7 @@
 //
 // Per request row this is a [N x 128] x [128 x 192] contraction (3 layers x
 // 64 heads), 49152 flop per 132-byte chunk, on the 16x16x32 f16 MFMA
-// (plus 4096 flop per chunk for the linear term below).
+// (plus one 16x16x128 fp8 MFMA per 16 chunks for the linear term below).
 //
 // Exact-algebra choices that keep it within the fp64 result:
 //   - the e4m3 codes are converted exactly to f16 (every finite e4m3 value
@@ -18,10 +18,12 @@
 //     y_h = s x_h:
 //       sum_h w_h relu(y_h) = s/2 * sum_h w_h x_h + |s|/2 * sum_h w_h |x_h|.
 //     The first sum is linear in the codes: it is (sum_h w_h q_h) . code,
-//     four more MFMAs per tile on spare A rows holding the weighted query
-//     sum of each layer split into two f16 parts (hi + lo, about 22
-//     significant bits).  The second is one fused multiply-add per head with
-//     an absolute-value operand, and a scale of either sign costs nothing;
+//     one more MFMA per tile, on the fp8 matrix core with the stored e4m3
+//     codes as they are (no decode) and the weighted query sum of each layer
+//     scaled by a power of two and split into three e4m3 parts (about 15
+//     bits below the largest element).  The second is one fused multiply-add
+//     per head with an absolute-value operand, and a scale of either sign
+//     costs nothing;
 //   - max ensemble: max_l sigmoid(t_l) = sigmoid(max_l t_l), one sigmoid.
 #include <algorithm>
 
@@ -34,6 +36,7 @@ using namespace score;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // MFMA 16x16x32 f16 operand layout: lane l supplies A[l%16][8(l/16) + e] and
 // B[8(l/16) + e][l%16], e = 0..7, and receives C[4(l/16) + r][l%16].
@@ -41,23 +44,46 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // chunks).  For k-step t (t = 0..3) lane l's eight k slots are the dims
 // 32(l/16) + 8t + e, so each lane reads one contiguous 32-byte run of its
 // chunk's codes.  Fragment f = (layer * 4 + head_tile) * 4 + t for the
-// heads; fragment 48 + t holds the linear-term rows for k-step t: row l
-// (l < 3) is the high f16 part of v_l = 1/2 sum_h w_{l,h} q_{l,h} (with q
-// already rounded to f16, the sum in fp32), row 4 + l the low part
-// v_l - hi, other rows zero.  The MFMA output of that tile then holds, in
-// lane group 0, the high part of layer r's term in element r, and in lane
-// group 1 the low part.
+// heads.
+//
+// The linear term uses the 16x16x128 fp8 MFMA, whose lane l supplies
+// A[l%16][32(l/16) + e] and B[32(l/16) + e][l%16], e = 0..31: B is lane
+// l's 32 stored code bytes as they are.  Row 4k + l (k = 0..2, l = layer)
+// of its A holds part k of u_l = 2^b_l v_l, v_l = 1/2 sum_h w_{l,h} q_{l,h}
+// (q already rounded to f16, the sum in fp32), with 2^b_l putting the
+// largest |u_l| in [128, 256): part 0 = e4m3(u), part 1 = e4m3(u - part 0),
+// part 2 = e4m3 of what remains.  Other rows are zero.  The MFMA output
+// then holds, in lane group k, part k of layer r's term in element r; the
+// parts share the scale 2^-b_l, so the cross-group sum adds them.
+//
+// Packed row: 48 head fragments (64 lanes x 16 bytes), the linear fragment
+// (64 lanes x 32 bytes) at byte kQLinOffset, and the three 2^-b_l at byte
+// kQScaleOffset.
+constexpr int kQLinOffset = kQHeadFrags * 64 * 16;
+constexpr int kQScaleOffset = kQLinOffset + 64 * 32;
+static_assert(kQScaleOffset + 16 <= kQFrags * 64 * 16, "packed query row too small");
+
+// 2^a with m 2^a in [128, 256) (m > 0); 0 for m = 0.
+__device__ __forceinline__ int part_exponent(float m) {
+  if (!(m > 0.f)) return 0;
+  int ex;
+  (void)frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+  return 8 - ex;
+}
+
 // One block per (row, layer), 256 threads.  Thread t packs the head
 // fragments o = t + 256 j (j = 0..3; fragment o / 64, lane o % 64) from two
 // float4 loads each, all issued first, and keeps the f16 queries in LDS;
-// then v_d = 1/2 sum_h w_h q_hd is summed in two head halves (fp32), split
-// into hi + lo f16 parts and scattered to the linear-term rows of this
-// layer.  The layer-0 block also writes the zero rows.
+// then v_d = 1/2 sum_h w_h q_hd is summed in two head halves (fp32), scaled
+// by this layer's 2^b and split into three e4m3 parts scattered to this
+// layer's rows of the linear fragment.  The layer-0 block also writes the
+// zero rows.
 __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q, const float* __restrict__ w, int B,
                                                      f16x8* __restrict__ qpack) {
   __shared__ __attribute__((aligned(16))) _Float16 qs[kHeads][kHeadDim + 8];
   __shared__ float red[2][kHeadDim];
-  __shared__ __attribute__((aligned(16))) _Float16 lin[4][4][2][8];  // [t][g][hi, lo][e]
+  __shared__ float vmax[2];
+  __shared__ __attribute__((aligned(16))) uint32_t lin8[3][kHeadDim / 4];  // [part][dims / 4]
   const int b = blockIdx.x / kLayers;
   const int layer = blockIdx.x % kLayers;
   const int t = threadIdx.x;
@@ -94,24 +120,50 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q
     red[half][d] = acc;
   }
   __syncthreads();
+  float u = 0.f;
   if (t < kHeadDim) {
-    const float vd = 0.5f * (red[0][t] + red[1][t]);
-    const _Float16 hi = (_Float16)vd;
-    const _Float16 lo = (_Float16)(vd - (float)hi);
-    const int g = t >> 5, ks = (t >> 3) & 3, e = t & 7;  // dim t = 32 g + 8 ks + e
-    lin[ks][g][0][e] = hi;
-    lin[ks][g][1][e] = lo;
+    u = 0.5f * (red[0][t] + red[1][t]);
+    float mu = fabsf(u);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mu = fmaxf(mu, __shfl_xor(mu, off));
+    if ((t & 63) == 0) vmax[t >> 6] = mu;
   }
   __syncthreads();
-  if (t < 32) {
-    const int ks = t >> 3, g = (t >> 1) & 3, part = t & 1;
-    const int row = part ? 4 + layer : layer;
-    out[(kQHeadFrags + ks) * 64 + row + 16 * g] = *(const f16x8*)&lin[ks][g][part][0];
+  uint8_t* row = (uint8_t*)out;
+  if (t < kHeadDim) {
+    const int bl = part_exponent(fmaxf(vmax[0], vmax[1]));
+    float r = ldexpf(u, bl);
+    uint32_t p[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      p[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.f, 0, false) & 0xffu;
+      r -= __builtin_amdgcn_cvt_f32_fp8((int)p[k], 0);  // exact: p[k] is r rounded to 4 significant bits
+    }
+    // Gather the bytes of four consecutive dims into one word (lanes t..t+3).
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      uint32_t word = p[k] << (8 * (t & 3));
+      word |= __shfl_xor(word, 1);
+      word |= __shfl_xor(word, 2);
+      if ((t & 3) == 0) lin8[k][t >> 2] = word;
+    }
+    if (t == 0) ((float*)(row + kQScaleOffset))[layer] = ldexpf(1.0f, -bl);
   }
-  if (layer == 0 && t < 4 * 4 * 10) {  // rows 3, 7, 8 .. 15 of every (k-step, lane group)
-    const int ks = t / 40, g = (t / 10) & 3, z = t % 10;
-    const int row = z == 0 ? 3 : (z == 1 ? 7 : 6 + z);
-    out[(kQHeadFrags + ks) * 64 + row + 16 * g] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  __syncthreads();
+  uint4* lin_out = (uint4*)(row + kQLinOffset);
+  if (t < 12) {  // part k = t / 4 of this layer, dims 32 j .. + 31 with j = t % 4
+    const int k = t >> 2, j = t & 3;
+    const int lane = 4 * k + layer + 16 * j;
+    const uint4* src = (const uint4*)&lin8[k][8 * j];
+    lin_out[2 * lane] = src[0];
+    lin_out[2 * lane + 1] = src[1];
+  }
+  if (layer == 0 && t >= 16 && t < 16 + 28) {  // rows 3, 7, 11 .. 15 of every lane group
+    const int z = (t - 16) >> 2, j = (t - 16) & 3;
+    const int rw = z < 3 ? 4 * z + 3 : 9 + z;
+    const int lane = rw + 16 * j;
+    lin_out[2 * lane] = make_uint4(0, 0, 0, 0);
+    lin_out[2 * lane + 1] = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -131,14 +183,23 @@ __device__ __forceinline__ void decode_tile(const RawTile& t, f16x8 (&kf)[4]) {
   kf[3] = decode8(t.hi[2], t.hi[3]);
 }
 
-__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const f16x8 (&ql)[4], const f16x8 (&kf)[4],
-                                          f32x4 (&acc)[kLayers][4], f32x4& lin) {
+__device__ __forceinline__ i32x8 tile_codes(const RawTile& t) {
+  return i32x8{(int)t.lo[0], (int)t.lo[1], (int)t.lo[2], (int)t.lo[3],
+               (int)t.hi[0], (int)t.hi[1], (int)t.hi[2], (int)t.hi[3]};
+}
+
+// The 49 MFMAs of one tile: the linear term first (fp8, from the stored
+// codes), then the 48 head MFMAs in k-step order, so no MFMA waits on the
+// one before it.
+__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const i32x8& qlin, const RawTile& raw,
+                                          const f16x8 (&kf)[4], f32x4 (&acc)[kLayers][4], f32x4& lin) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // Format code 0 (e4m3) for both operands; no block scales.
+  lin = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qlin, tile_codes(raw), zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][0], kf[0], zero, 0, 0, 0);
-  lin = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[0], kf[0], zero, 0, 0, 0);
 #pragma unroll
   for (int t = 1; t < 4; ++t) {
 #pragma unroll
@@ -146,14 +207,15 @@ __device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], cons
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[l][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[l][mt][t], kf[t], acc[l][mt], 0, 0, 0);
-    lin = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[t], kf[t], lin, 0, 0, 0);
   }
 }
 
-// Head reduction, sigmoid, ensemble and store of one tile.  wh = w / 2.
+// Head reduction, sigmoid, ensemble and store of one tile.  wh = w / 2,
+// ub[l] = 2^-b_l.
 template <bool MEAN, bool PER_LAYER>
 __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
-                                            const f32x4 (&wh)[kLayers][4], float s, int tile) {
+                                            const f32x4 (&wh)[kLayers][4], const float (&ub)[kLayers], float s,
+                                            int tile) {
   float t[kLayers];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -162,21 +224,24 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) p = fmaf(fabsf(acc[l][mt][r]), wh[l][mt][r], p);
-    // |s| p + s lin: lane group 0 adds the high part of the linear term,
-    // group 1 the low part, groups 2 and 3 hold zeros there.
-    t[l] = sum4groups(fmaf(s, lin[l], fabsf(s) * p));  // the layer's logit
+    // (s 2^-b lin + |s| p) / |s| = sign(s) 2^-b lin + p: lane groups 0..2
+    // add the three parts of the linear term, group 3 holds zero there.
+    t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  store_tile<MEAN, PER_LAYER>(cx, t, tile);
+  store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
 }
 
-// Instruction order of one phase for the scheduler: every MFMA followed by
-// two vector-ALU instructions (a wave issues in order, so the vector work
-// of the reduction and decode must sit between the MFMAs to overlap them),
-// then the phase's requests (after the decode has consumed the ring slot
-// they refill) and its stores.
+// Instruction order of one phase for the scheduler: the fp8 MFMA (32
+// cycles) followed by four vector-ALU instructions, every f16 MFMA (16
+// cycles) by two (a wave issues in order, so the vector work of the
+// reduction and decode must sit between the MFMAs to overlap them), then
+// the phase's requests (after the decode has consumed the ring slot they
+// refill) and its stores.
 __device__ __forceinline__ void interleave_phase() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA (fp8 linear term)
+  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // VALU
 #pragma unroll
-  for (int k = 0; k < kLayers * 4 * 4 + 4; ++k) {
+  for (int k = 0; k < kLayers * 4 * 4; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
   }
@@ -191,7 +256,7 @@ __device__ __forceinline__ void interleave_phase() {
 // chunk below the row's valid_n.
 //
 // Software pipeline, one wave per SIMD: in the phase of tile i the wave
-// issues the 52 MFMAs of tile i, interleaved with the reduction of tile i-1
+// issues the 49 MFMAs of tile i, interleaved with the reduction of tile i-1
 // and the decode of tile i+1; the records of tile i+6 are requested in the
 // same phase (6 tiles in flight).  Tiles past the run's chunks read as zeros
 // and their stores are dropped by the buffer range checks.
@@ -202,22 +267,26 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
                                           float* __restrict__ per_layer) {
   const Ctx cx = make_ctx<PER_LAYER>(comp_k, B, N, b, start, count, lane, scores, per_layer);
 
-  // Query fragments, linear-term fragments and w: every load is issued
+  // Query fragments, the linear-term fragment and its scales, and w: every load is issued
   // before the first use, so the wave pays one memory latency here, not one
   // per fragment.
   f16x8 qf[kLayers][4][4];
-  f16x8 ql[4];
+  i32x8 qlin;
   f32x4 wv[kLayers][4];  // w / 2 of the heads this lane's accumulators hold: 16 mt + 4 g + r
+  float ub[kLayers];     // 2^-b_l of the linear term
   {
-    const f16x8* qp = qpack + (size_t)b * kQFrags * 64 + lane;
+    const f16x8* qrow = qpack + (size_t)b * kQFrags * 64;
+    const f16x8* qp = qrow + lane;
 #pragma unroll
     for (int l = 0; l < kLayers; ++l)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
+    qlin = *((const i32x8*)((const uint8_t*)qrow + kQLinOffset) + lane);
+    const float* usc = (const float*)((const uint8_t*)qrow + kQScaleOffset);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ql[t] = qp[(kQHeadFrags + t) * 64];
+    for (int l = 0; l < kLayers; ++l) ub[l] = usc[l];
 #pragma unroll
     for (int l = 0; l < kLayers; ++l)
 #pragma unroll
@@ -242,8 +311,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(qf[l][mt][t]));
-#pragma unroll
-  for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(ql[t]));
+  asm volatile("" : "+a"(qlin));
   // Consume w here, so its wait is paid before the loop; a wait inside the
   // loop would also drain the records in flight.
 #pragma unroll
@@ -253,6 +321,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
       wv[l][mt] = 0.5f * wv[l][mt];
       asm volatile("" : "+v"(wv[l][mt]));
     }
+#pragma unroll
+  for (int l = 0; l < kLayers; ++l) asm volatile("" : "+v"(ub[l]));
 
   const int tiles = (int)((count + kTile - 1) / kTile);
 
@@ -266,9 +336,9 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   // into the slot of tile i-2, finished in the previous phase.
 #define FM_PHASE(P, I)                                                                                \
   {                                                                                                   \
-    mfma_tile(qf, ql, kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                                       \
-    finish_tile<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ring[((P) + 7) & 7].s,  \
-                                 (I) - 1);                                                            \
+    mfma_tile(qf, qlin, ring[(P) & 7], kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                     \
+    finish_tile<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,                  \
+                                 ring[((P) + 7) & 7].s, (I) - 1);                                     \
     decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
     interleave_phase();                                                                               \
@@ -276,7 +346,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 
   // Tile 0 (nothing to finish yet).
   decode_tile(ring[0], kf[0]);
-  mfma_tile(qf, ql, kf[0], acc[0], lin[0]);
+  mfma_tile(qf, qlin, ring[0], kf[0], acc[0], lin[0]);
   decode_tile(ring[1], kf[1]);
   load_tile(cx, kAhead, ring[kAhead]);
 
@@ -295,7 +365,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
     FM_PHASE(0, i + 7)
     i += 8;
   } while (i < tiles);
-  finish_tile<MEAN, PER_LAYER>(cx, acc[0], lin[0], wv, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
+  finish_tile<MEAN, PER_LAYER>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
 #undef FM_PHASE
 }
 

@@ -30,18 +30,56 @@ constexpr int kAhead = 6;                        // tile i + 6 is requested in t
 // check, with no branch.
 constexpr uint32_t kDropOffset = 0x40000000u;
 
-// Sum over the four lane groups {l, l^16, l^32, l^48} (every lane gets it).
-__device__ __forceinline__ float sum4groups(float v) {
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return v;
+// Cross-lane moves.  permlane32_swap(x, y) swaps lanes 32..63 of x with
+// lanes 0..31 of y; permlane16_swap(x, y) swaps the odd 16-lane rows of x
+// with the even rows of y.  Both return the new (x, y).
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
 }
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Sum and max over the four 16-lane rows {l, l^16, l^32, l^48} (every lane
+// gets it).
+__device__ __forceinline__ float sum4rows(float v) {
+  float w = v;
+  swap32(v, w);
+  v += w;
+  w = v;
+  swap16(v, w);
+  return v + w;
+}
+__device__ __forceinline__ float max4rows(float v) {
+  float w = v;
+  swap32(v, w);
+  v = fmaxf(v, w);
+  w = v;
+  swap16(v, w);
+  return fmaxf(v, w);
+}
+
+// The three layers' logits of every chunk from the lanes' partial sums:
+// u[l] is lane group g's part of layer l for the lane's chunk (l % 16).
+// Layers 0 and 1 share the first swap (lanes 0..31 then hold layer 0's sums
+// over the row pairs {r, r + 2}, lanes 32..63 layer 1's), layer 2 takes the
+// other operand; the second swap completes the sums.  Returns, per 16-lane
+// row, one layer's total: row 0 layer 0, row 1 layer 2, row 2 layer 1, and
+// row 3 layer 2 again (dup_zero false) or 0 (dup_zero true).
+__device__ __forceinline__ float layer_totals(const float (&u)[kLayers], bool dup_zero) {
+  float a = u[0], b = u[1], c = u[2], d = dup_zero ? 0.f : u[2];
+  swap32(a, b);
+  swap32(c, d);
+  float ab = a + b, cd = c + d;
+  swap16(ab, cd);
+  return ab + cd;
+}
+// 16-lane row of each layer's total in layer_totals' result.
+constexpr int kLayerRow[kLayers] = {0, 2, 1};
 
 __device__ __forceinline__ float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
@@ -52,14 +90,21 @@ struct RawTile {
   float s;       // the chunk's scale
 };
 
+// One pipeline run's buffers: base addresses and byte counts of this
+// run's records and outputs (wave-uniform), and the lane's offsets within a
+// tile.  Each tile's buffer descriptors start at the tile (scalar
+// arithmetic) and end at the run's end, so the per-lane offsets stay fixed
+// and the range checks make reads past the run return 0 and drop writes
+// past it.
 struct Ctx {
-  __amdgpu_buffer_rsrc_t rec;            // records of this wave's chunks; reads past them return 0
-  __amdgpu_buffer_rsrc_t out;            // scores of this wave's chunks; writes past them are dropped
-  __amdgpu_buffer_rsrc_t pl[kLayers];    // per-layer scores of this wave's chunks (when requested)
+  const uint8_t* rec;                    // records of this run's chunks
+  float* out;                            // their scores
+  float* pl[kLayers];                    // their per-layer scores (when requested)
+  int32_t rec_bytes, out_bytes;          // 132 and 4 bytes per chunk of the run
   uint32_t lane_rec_off;                 // 132 c + 32 g
   uint32_t lane_scale_off;               // 132 c + 128
   uint32_t lane_out_off;                 // 4 c in lane group 0, out of range elsewhere
-  uint32_t lane_pl_off[kLayers];         // 4 c in lane group l, out of range elsewhere
+  uint32_t lane_pl_off[kLayers];         // 4 c in the lane row holding layer l's total, out of range elsewhere
   int c, g;
 };
 
@@ -73,49 +118,56 @@ __device__ __forceinline__ Ctx make_ctx(const uint8_t* comp_k, int B, int64_t N,
   cx.lane_rec_off = (uint32_t)(cx.c * kRecord + 32 * cx.g);
   cx.lane_scale_off = (uint32_t)(cx.c * kRecord + kHeadDim);
   cx.lane_out_off = cx.g == 0 ? (uint32_t)(cx.c * 4) : kDropOffset;
-  cx.rec = __builtin_amdgcn_make_buffer_rsrc((void*)(comp_k + ((size_t)b * N + start) * kRecord), 0,
-                                             (int)(count * kRecord), kBufferWord3);
-  cx.out = __builtin_amdgcn_make_buffer_rsrc((void*)(scores + (size_t)b * N + start), 0, (int)(count * 4),
-                                             kBufferWord3);
+  cx.rec = comp_k + ((size_t)b * N + start) * kRecord;
+  cx.out = scores + (size_t)b * N + start;
+  cx.rec_bytes = (int32_t)(count * kRecord);
+  cx.out_bytes = (int32_t)(count * 4);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
-    cx.lane_pl_off[l] = cx.g == l ? (uint32_t)(cx.c * 4) : kDropOffset;
-    cx.pl[l] = __builtin_amdgcn_make_buffer_rsrc(
-        PER_LAYER ? (void*)(per_layer + ((size_t)l * B + b) * N + start) : (void*)scores, 0,
-        PER_LAYER ? (int)(count * 4) : 0, kBufferWord3);
+    cx.lane_pl_off[l] = cx.g == kLayerRow[l] ? (uint32_t)(cx.c * 4) : kDropOffset;
+    cx.pl[l] = PER_LAYER ? per_layer + ((size_t)l * B + b) * N + start : scores;
   }
   return cx;
 }
 
-// Offsets go in the per-lane voffset (the range check covers voffset).
-__device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
-  const uint32_t so = (uint32_t)tile * kTileBytes;
-  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so, 0, 0));
-  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.rec, cx.lane_rec_off + so + 16, 0, 0));
-  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cx.rec, cx.lane_scale_off + so, 0, 0));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int32_t bytes, int32_t from) {
+  const int32_t left = bytes - from;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + from), 0, left > 0 ? left : 0,
+                                           kBufferWord3);
 }
 
-// Sigmoid, ensemble and store of one tile from the layers' logits t[l]
-// (every lane holds its chunk's logits).
+__device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(cx.rec, cx.rec_bytes, tile * kTileBytes);
+  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off, 0, 0));
+  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off + 16, 0, 0));
+  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, cx.lane_scale_off, 0, 0));
+}
+
+// Ensemble and store of one tile.  u[l] is this lane's part of layer l's
+// logit divided by |s| (as = |s|, the chunk's scale magnitude): the logit is
+// |s| times the sum of u[l] over the four lane groups, and since |s| >= 0,
+// max_l sigmoid(|s| T_l) = sigmoid(|s| max_l T_l) takes one sigmoid.  For
+// the mean and per-layer outputs each lane row computes the sigmoid of the
+// layer total it holds.
 template <bool MEAN, bool PER_LAYER>
-__device__ __forceinline__ void store_tile(const Ctx& cx, const float (&t)[kLayers], int tile) {
+__device__ __forceinline__ void store_tile(const Ctx& cx, const float (&u)[kLayers], float as, int tile) {
+  const int32_t to = tile * (kTile * 4);
   float e;
-  float sl[kLayers];
   if (MEAN || PER_LAYER) {
+    // Row 3 holds 0 for the mean (its sigmoid, 1/2, is taken back out of
+    // the sum) and layer 2 again for the max.
+    const float sl = sigmoid(as * layer_totals(u, MEAN));
+    e = MEAN ? (sum4rows(sl) - 0.5f) * (1.0f / 3.0f) : max4rows(sl);
+    if (PER_LAYER) {
 #pragma unroll
-    for (int l = 0; l < kLayers; ++l) sl[l] = sigmoid(t[l]);
-    e = MEAN ? (sl[0] + sl[1] + sl[2]) * (1.0f / 3.0f) : fmaxf(fmaxf(sl[0], sl[1]), sl[2]);
+      for (int l = 0; l < kLayers; ++l)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl), tile_rsrc(cx.pl[l], PER_LAYER ? cx.out_bytes : 0, to),
+                                              cx.lane_pl_off[l], 0, 0);
+    }
   } else {
-    // max_l sigmoid(t_l) = sigmoid(max_l t_l): one sigmoid.
-    e = sigmoid(fmaxf(fmaxf(t[0], t[1]), t[2]));
+    e = sigmoid(as * max4rows(layer_totals(u, false)));
   }
-  const uint32_t to = (uint32_t)tile * (kTile * 4);
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), cx.out, cx.lane_out_off + to, 0, 0);
-  if (PER_LAYER) {
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl[l]), cx.pl[l], cx.lane_pl_off[l] + to, 0, 0);
-  }
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), tile_rsrc(cx.out, cx.out_bytes, to), cx.lane_out_off, 0, 0);
 }
 
 // The persistent grid's work split: the valid tiles of all rows, in

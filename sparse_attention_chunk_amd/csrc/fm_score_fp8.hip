@@ -216,11 +216,11 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) p = fmaf(fabsf(acc[l][mt][r]), wv[l][mt][r], p);
-    // |s| p + s 2^-b lin: lane groups 0..2 add the three parts of the
-    // linear term, group 3 holds zero there.
-    t[l] = sum4groups(fmaf(s * ub[l], lin[l], fabsf(s) * p));
+    // (s 2^-b lin + |s| p) / |s| = sign(s) 2^-b lin + p: lane groups 0..2
+    // add the three parts of the linear term, group 3 holds zero there.
+    t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  store_tile<MEAN, PER_LAYER>(cx, t, tile);
+  store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
 }
 
 // Instruction order of one phase: every MFMA followed by up to four
