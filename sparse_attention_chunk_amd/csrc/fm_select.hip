@@ -36,6 +36,7 @@ __device__ inline int64_t row_valid(const int32_t* valid_n, int b, int64_t N) {
 // state[b] = {cut-off L, unused, mode, unused}
 enum : uint32_t { kSelect = 0, kKeepAll = 1, kKeepNone = 2 };
 
+constexpr int kTile16 = 16;  // chunks per tile of the score pass (tile maxima)
 constexpr int kSampleRuns = 64;
 constexpr int kSampleRun = 64;
 constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 4096
@@ -294,7 +295,192 @@ __global__ __launch_bounds__(256) void threshold_kernel(const float* scores, int
     mrow[n] = (n < vn && row[n] > threshold) ? 1 : 0;
 }
 
+// Top-K finished from the score pass's histograms and tile maxima (the
+// selection folded into fm_score_topk).  grid = B, block = 1024.  Per row:
+//   1. the row's histogram: the global one (rows a block reached past its
+//      two slots) plus slot 0 of every block whose first row is this row and
+//      slot 1 of every block whose first row is the one before;
+//   2. the bin c holding the K-th largest score, the count A above it and
+//      its own count n_c (K <= A + n_c);
+//   3. the tiles whose largest score falls in bin c or above (at most
+//      A + n_c of them);
+//   4. their chunks: above bin c the mask byte is set (every such chunk is
+//      among the top K), in bin c the (key, index) pair becomes a candidate;
+//   5. the K - A candidates kept: all of them, or an exact radix selection
+//      (key descending, index ascending).
+// When the tiles or the candidates overflow LDS (many equal or nearly equal
+// scores), the row is selected exactly from all its scores instead.  The
+// result is the mask fm_select_topk gives for the same scores.
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishTiles = 2048;      // qualifying tiles held in LDS
+constexpr int kFinishCand = 4096;       // candidates of bin c held in LDS
+constexpr int kFinishBatch = 16;        // loads issued together
+
+__device__ __forceinline__ int fused_bin(float e) {
+  const int b = (int)(e * (float)kHistBins);
+  return b < kHistBins - 1 ? b : kHistBins - 1;
+}
+
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, int64_t N, const int32_t* __restrict__ valid_n, int32_t top_k,
+    const uint32_t* __restrict__ sel_hist, const int32_t* __restrict__ block_row0, int nblocks,
+    const uint32_t* __restrict__ hist_x, const float* __restrict__ tile_max, uint8_t* __restrict__ mask) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int64_t vn = row_valid(valid_n, b, N);
+  uint8_t* mrow = mask + (size_t)b * N;
+  const float* row = scores + (size_t)b * N;
+  if (top_k == 0 || vn == 0) return;  // the score pass wrote zeros
+  if ((int64_t)top_k >= vn) {
+    for (int64_t n = t; n < vn; n += kFinishThreads) mrow[n] = 1;
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
+  __shared__ uint32_t s_q[kFinishTiles];
+  __shared__ uint2 s_c[kFinishCand];
+  __shared__ uint32_t s_wtot[kFinishThreads / 64];
+  __shared__ uint32_t s_out[3];
+  __shared__ unsigned long long s_bm[2][kFinishThreads / 64];
+  __shared__ uint32_t s_blk[kMaxScoreBlocks];  // a block matches at most one of the two slots
+  __shared__ uint32_t s_nblk, s_nq, s_nc;
+
+  // 1. Histogram slots of this row.
+  {
+    bool h0 = false, h1 = false;
+    if (t < nblocks) {
+      const int r0 = block_row0[t];
+      h0 = r0 == b;
+      h1 = r0 >= 0 && r0 == b - 1;
+    }
+    const unsigned long long m0 = __ballot(h0), m1 = __ballot(h1);
+    if (lane == 0) {
+      s_bm[0][wave] = m0;
+      s_bm[1][wave] = m1;
+    }
+    __syncthreads();
+    if (t == 0) {
+      uint32_t n = 0;
+      for (int slot = 0; slot < 2; ++slot)
+        for (int w = 0; w < kFinishThreads / 64; ++w)
+          for (unsigned long long m = s_bm[slot][w]; m; m &= m - 1)
+            s_blk[n++] = (uint32_t)(2 * (w * 64 + __builtin_ctzll(m)) + slot);
+      s_nblk = n;
+      s_nq = 0;
+      s_nc = 0;
+    }
+    __syncthreads();
+    uint2 c = *(const uint2*)(hist_x + (size_t)b * kHistBins + 2 * t);
+    const uint32_t nblk = s_nblk;
+    for (uint32_t base = 0; base < nblk; base += kFinishBatch) {
+      uint2 x[kFinishBatch];
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j)
+        x[j] = base + j < nblk ? *(const uint2*)(sel_hist + (size_t)s_blk[base + j] * kHistBins + 2 * t)
+                               : make_uint2(0u, 0u);
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j) {
+        c.x += x[j].x;
+        c.y += x[j].y;
+      }
+    }
+    *(uint2*)(h + 2 * t) = c;
+  }
+  __syncthreads();
+  // 2. The cut-off bin.
+  block_find<kFinishThreads>(h, (uint32_t)top_k, s_wtot, s_out, true);
+  const int cbin = (int)s_out[0];
+  const uint32_t above = s_out[1], n_c = s_out[2];
+  const uint32_t need = (uint32_t)top_k - above;
+  bool exact_row = n_c > (uint32_t)kFinishCand;
+  if (!exact_row) {
+    // 3. Qualifying tiles.
+    const int64_t nt = (vn + kTile16 - 1) / kTile16;
+    const float* trow = tile_max + (size_t)b * ((N + kTile16 - 1) / kTile16);
+    for (int64_t base = t; base < nt; base += (int64_t)kFinishThreads * kFinishBatch) {
+      float m[kFinishBatch];
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j) {
+        const int64_t i = base + (int64_t)j * kFinishThreads;
+        m[j] = i < nt ? trow[i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j) {
+        const int64_t i = base + (int64_t)j * kFinishThreads;
+        if (i < nt && fused_bin(m[j]) >= cbin) {
+          const uint32_t pos = atomicAdd(&s_nq, 1u);
+          if (pos < (uint32_t)kFinishTiles) s_q[pos] = (uint32_t)i;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nq = s_nq;
+    exact_row = nq > (uint32_t)kFinishTiles;
+    if (!exact_row) {
+      // 4. Their chunks.
+      const uint32_t total = nq * kTile16;
+      for (uint32_t base = t; base < total; base += kFinishThreads * kFinishBatch) {
+        float e[kFinishBatch];
+        int64_t n[kFinishBatch];
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+          const uint32_t x = base + j * kFinishThreads;
+          n[j] = x < total ? (int64_t)s_q[x / kTile16] * kTile16 + (x % kTile16) : vn;
+          e[j] = n[j] < vn ? row[n[j]] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+          if (n[j] < vn) {
+            const int bn = fused_bin(e[j]);
+            if (bn > cbin) {
+              mrow[n[j]] = 1;
+            } else if (bn == cbin) {
+              const uint32_t pos = atomicAdd(&s_nc, 1u);
+              if (pos < (uint32_t)kFinishCand) s_c[pos] = make_uint2(order_key(e[j]), (uint32_t)n[j]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // 5. The K - A kept of bin c.
+      const uint32_t nc = s_nc < (uint32_t)kFinishCand ? s_nc : (uint32_t)kFinishCand;
+      if (need >= nc) {
+        for (uint32_t i = t; i < nc; i += kFinishThreads) mrow[s_c[i].y] = 1;
+      } else {
+        auto each = [&](auto f) {
+          for (uint32_t i = t; i < nc; i += kFinishThreads) f(s_c[i]);
+        };
+        uint32_t T, last;
+        radix_select<kFinishThreads>(each, need, index_bits(vn), h, s_wtot, s_out, &T, &last);
+        each([&](uint2 e) {
+          if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
+        });
+      }
+      return;
+    }
+  }
+  // Too many equal or nearly equal scores for LDS: exact selection over the
+  // whole row (the mask bytes set in step 4 are all among the top K).
+  auto each = [&](auto f) {
+    for (int64_t n = t; n < vn; n += kFinishThreads) f(make_uint2(order_key(row[n]), (uint32_t)n));
+  };
+  uint32_t T, last;
+  radix_select<kFinishThreads>(each, (uint32_t)top_k, index_bits(vn), h, s_wtot, s_out, &T, &last);
+  each([&](uint2 e) {
+    if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
+  });
+}
+
 }  // namespace
+
+hipError_t launch_topk_finish(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
+                              int32_t top_k, uint8_t* mask, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k,
+                     (const uint32_t*)ws.sel_hist, (const int32_t*)ws.block_row0, ws.score_blocks,
+                     (const uint32_t*)ws.sel_hist_x, (const float*)ws.tile_max, mask);
+  return hipGetLastError();
+}
 
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream) {

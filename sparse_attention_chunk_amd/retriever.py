@@ -113,6 +113,33 @@ class FlashMemoryRetriever:
         fn(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], scores, pl)
         return (scores, pl) if per_layer else scores
 
+    def score_select(self, q, w, comp_k, valid_n=None, mode="max", top_k=None, threshold=None, per_layer=False):
+        """Scores and keep mask with the selection folded into the score pass
+        (fm_score_topk + fm_select_topk_finish, or fm_score_threshold).
+        Exactly one of top_k and threshold.  Returns (scores, mask) or, with
+        per_layer, (scores, mask, per_layer)."""
+        if (top_k is None) == (threshold is None):
+            raise ValueError("pass exactly one of top_k and threshold")
+        _need(comp_k, torch.uint8, "comp_k", 3)
+        _need(q, torch.float32, "q", 4)
+        _need(w, torch.float32, "w", 3)
+        B, N = comp_k.shape[0], comp_k.shape[1]
+        if comp_k.shape[2] != 132:
+            raise ValueError("comp_k records must be 132 bytes")
+        if valid_n is not None:
+            _need(valid_n, torch.int32, "valid_n", 1)
+        dev = comp_k.device
+        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        mask = torch.empty((B, N), dtype=torch.bool, device=dev)
+        pl = torch.empty((3, B, N), dtype=torch.float32, device=dev) if per_layer else None
+        if top_k is not None:
+            _lib.fm_score_topk(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], int(top_k), scores, mask, pl)
+            _lib.fm_select_topk_finish(self._ctx, scores, B, N, valid_n, int(top_k), mask)
+        else:
+            _lib.fm_score_threshold(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], float(threshold), scores,
+                                    mask, pl)
+        return (scores, mask, pl) if per_layer else (scores, mask)
+
     def keep_topk(self, scores, top_k: int, valid_n=None):
         _need(scores, torch.float32, "scores", 2)
         B, N = scores.shape
@@ -195,10 +222,8 @@ class FlashMemoryRetriever:
     def select_topk(self, hidden, comp_k, positions, top_k=None, threshold=None, mode="max", valid_n=None):
         if (top_k is None) == (threshold is None):
             raise ValueError("pass exactly one of top_k and threshold")
-        scores = self.ensemble(hidden, comp_k, positions, mode, valid_n)
-        if top_k is not None:
-            return self.keep_topk(scores, top_k, valid_n)
-        return self.keep_threshold(scores, threshold, valid_n)
+        q, w = self.prepare_query(hidden, positions)
+        return self.score_select(q, w, comp_k, valid_n, mode, top_k=top_k, threshold=threshold)[1]
 
 
 def weights_to_device(weights_np, device="cuda"):
