@@ -396,8 +396,9 @@ def resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, 
 
 def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
     """The same workload's other ensemble and selection modes (mean ensemble
-    with top-512, max ensemble with the 0.5 threshold), score + select per
-    call pair from HIP events on the launch stream (median): launched in
+    with top-512, max ensemble with the 0.5 threshold by fm_score_threshold,
+    and the same threshold by fm_score + fm_select_threshold), score + select
+    per call pair from HIP events on the launch stream (median): launched in
     turn, so all see the same thermal state."""
     import numpy as np
     import torch
@@ -407,6 +408,9 @@ def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
         L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
 
     def max_threshold():
+        L.fm_score_threshold(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, 0.5, scores, mask, None, sh)
+
+    def max_threshold_separate():
         L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
         L.fm_select_threshold(r.ctx, scores, B, N, None, 0.5, mask, sh)
 
@@ -414,7 +418,8 @@ def variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, steps):
         L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
         L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
 
-    fns = (("max_top512", max_topk), ("mean_top512", mean_topk), ("max_threshold_0.5", max_threshold))
+    fns = (("max_top512", max_topk), ("mean_top512", mean_topk), ("max_threshold_0.5", max_threshold),
+           ("max_threshold_0.5_separate_calls", max_threshold_separate))
     for _, fn in fns:
         fn()
     torch.cuda.synchronize()
@@ -554,9 +559,9 @@ def mask_logits_leg(L, r, mask, B, N, sh, stream, steps, heads=64):
 
 def config_leg(cid: int, weights_dev, steps: int, settle_s: float, config_inputs: dict, flush_bytes: int = 1 << 29):
     """One of the other seeded workloads on its own context: the whole pass
-    (fm_prepare_query, fm_score with the workload's ensemble, its top-K or
-    threshold selection, valid_n for ragged rows) timed like the headline
-    (settle, then `steps` back-to-back steps between two HIP events), plus
+    (fm_prepare_query, then fm_score + fm_select_topk, or fm_score_threshold,
+    with the workload's ensemble and selection, valid_n for ragged rows)
+    timed like the headline (settle, then `steps` back-to-back steps between two HIP events), plus
     per-phase events on a second run of `steps` steps (medians).  Workloads
     whose inputs fit the 256 MB Infinity Cache (B=1 N=4096, B=8 N=65536) are
     also timed flushed: a 512 MB device fill before each step evicts it, and
@@ -605,13 +610,14 @@ def config_leg(cid: int, weights_dev, steps: int, settle_s: float, config_inputs
         L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, sh)
         if ev is not None:
             ev[1].record(stream)
-        L.fm_score(r.ctx, q, w, comp_k, B, N, valid_n, mode, scores, None, sh)
+        if wl.top_k is not None:
+            L.fm_score(r.ctx, q, w, comp_k, B, N, valid_n, mode, scores, None, sh)
+        else:
+            L.fm_score_threshold(r.ctx, q, w, comp_k, B, N, valid_n, mode, wl.threshold, scores, mask, None, sh)
         if ev is not None:
             ev[2].record(stream)
         if wl.top_k is not None:
             L.fm_select_topk(r.ctx, scores, B, N, valid_n, wl.top_k, mask, sh)
-        else:
-            L.fm_select_threshold(r.ctx, scores, B, N, valid_n, wl.threshold, mask, sh)
         if ev is not None:
             ev[3].record(stream)
 

@@ -147,31 +147,6 @@ fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* posi
 fm_status fm_score(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
                    const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream);
 
-/* fm_score with the keep-mask selection folded into the score pass
- * ("Inference flow": keep mask = top-K of the scores; "Usage" select_topk
- * with top_k=...).  Arguments as fm_score, plus:
- *   top_k  >= 0, as in fm_select_topk
- *   mask   device uint8 [B][N]
- * The pass writes the scores (and per_layer) as fm_score does, zeros into
- * the mask, and per-row score histograms and per-16-chunk maxima into the
- * context.  fm_select_topk_finish, called next on the same context and
- * stream with the same scores, mask, valid_n, B, N and top_k, completes the
- * mask; together they give exactly fm_score followed by fm_select_topk.
- * A later fm_score_topk on the context replaces the pending state.
- * B in [0, max_batch], N in [0, max_n]. */
-fm_status fm_score_topk(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
-                        const int32_t* valid_n, fm_ensemble mode, int32_t top_k, float* scores, uint8_t* mask,
-                        float* per_layer, void* stream);
-
-/* Completes the top-K mask begun by the last fm_score_topk on this context
- * (same scores, mask, valid_n, B, N and top_k, else FM_EINVAL): per row,
- * the chunks whose score lies above the histogram bin of the top_k-th
- * score are kept, and the rest of the top_k come from that bin by an exact
- * selection (ties to the lower chunk index).  Rows with many equal or
- * nearly equal scores fall back to an exact selection over the whole row. */
-fm_status fm_select_topk_finish(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
-                                int32_t top_k, uint8_t* mask, void* stream);
-
 /* fm_score with the threshold keep mask ("Usage" select_topk with
  * threshold=...; "Inference flow" sigmoid > thresh) written by the score
  * pass itself: mask[b][n] = score > threshold (strict), 0 at or beyond

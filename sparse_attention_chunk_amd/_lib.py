@@ -34,9 +34,9 @@ STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUN
                 FM_ENOMEM: "FM_ENOMEM", FM_EHIP: "FM_EHIP"}
 
 # Exported symbols, in header order.
-EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_topk",
-           "fm_select_topk_finish", "fm_score_threshold", "fm_score_fp8", "fm_select_topk", "fm_select_topk_subset",
-           "fm_select_threshold", "fm_resident_delta", "fm_mask_logits", "fm_last_error")
+EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_threshold",
+           "fm_score_fp8", "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta",
+           "fm_mask_logits", "fm_last_error")
 
 
 class FmConfig(ctypes.Structure):
@@ -86,10 +86,6 @@ def _load() -> ctypes.CDLL:
     lib.fm_prepare_query.restype = ctypes.c_int
     lib.fm_score.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, vp, vp, vp]
     lib.fm_score.restype = ctypes.c_int
-    lib.fm_score_topk.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i32, vp, vp, vp, vp]
-    lib.fm_score_topk.restype = ctypes.c_int
-    lib.fm_select_topk_finish.argtypes = [vp, vp, i32, i64, vp, i32, vp, vp]
-    lib.fm_select_topk_finish.restype = ctypes.c_int
     lib.fm_score_threshold.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp]
     lib.fm_score_threshold.restype = ctypes.c_int
     lib.fm_score_fp8.argtypes = [vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, vp, vp, vp]
@@ -155,18 +151,6 @@ def fm_score(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer=None, str
     s = current_stream() if stream is None else stream
     check(LIB.fm_score(ctx, ptr(q), ptr(w), ptr(comp_k), B, N, ptr(valid_n), mode, ptr(scores), ptr(per_layer), s),
           "fm_score")
-
-
-def fm_score_topk(ctx, q, w, comp_k, B, N, valid_n, mode, top_k, scores, mask, per_layer=None, stream=None) -> None:
-    s = current_stream() if stream is None else stream
-    check(LIB.fm_score_topk(ctx, ptr(q), ptr(w), ptr(comp_k), B, N, ptr(valid_n), mode, top_k, ptr(scores), ptr(mask),
-                            ptr(per_layer), s), "fm_score_topk")
-
-
-def fm_select_topk_finish(ctx, scores, B, N, valid_n, top_k, mask, stream=None) -> None:
-    s = current_stream() if stream is None else stream
-    check(LIB.fm_select_topk_finish(ctx, ptr(scores), B, N, ptr(valid_n), top_k, ptr(mask), s),
-          "fm_select_topk_finish")
 
 
 def fm_score_threshold(ctx, q, w, comp_k, B, N, valid_n, mode, threshold, scores, mask, per_layer=None,

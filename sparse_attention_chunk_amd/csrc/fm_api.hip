@@ -145,10 +145,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
     const int b = g * kProjRowsPerWave < max_batch ? g * kProjRowsPerWave : max_batch;
     p1_rows = std::max(p1_rows, (size_t)proj1_splits(b) * b);
   }
-  const size_t sel_blocks = (size_t)((max_n + kSelSlice - 1) / kSelSlice);
   enum {
     kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
-    kSelState, kSelCand, kSelCount, kResCount, kSelHist, kBlockRow0, kSelHistX, kTileMax, kNumBuffers
+    kSubStage, kResCount, kTileInfo, kNumBuffers
   };
   size_t sizes[kNumBuffers];
   sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
@@ -165,14 +164,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kW8] = sizeof(float) * kLayers * kW8Stride * mb;
   sizes[kRowTiles] = sizeof(int64_t) * (mb + 1);
   sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
-  sizes[kSelState] = sizeof(uint32_t) * mb * 4;
-  sizes[kSelCand] = 2 * sizeof(uint32_t) * mb * (size_t)max_n;  // (key, index) pairs
-  sizes[kSelCount] = sizeof(uint32_t) * mb * sel_blocks;
+  sizes[kSubStage] = sizeof(uint32_t) * mb * kSubStageRowWords;
   sizes[kResCount] = 3 * sizeof(uint32_t) * mb * (size_t)((max_n + kResSlice - 1) / kResSlice);
-  sizes[kSelHist] = sizeof(uint32_t) * (size_t)cus * 2 * kHistBins;
-  sizes[kBlockRow0] = sizeof(int32_t) * (size_t)cus;
-  sizes[kSelHistX] = sizeof(uint32_t) * mb * kHistBins;
-  sizes[kTileMax] = sizeof(float) * mb * (size_t)((max_n + 15) / 16);
+  sizes[kTileInfo] = sizeof(uint2) * mb * (size_t)fm::tile_info_stride(max_n);
   size_t offs[kNumBuffers];
   size_t total = 0;
   for (int i = 0; i < kNumBuffers; ++i) {
@@ -207,15 +201,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.row_tiles = (int64_t*)(p + offs[kRowTiles]);
   ctx->ws.wave_row = (int32_t*)(p + offs[kWaveRow]);
   ctx->ws.score_blocks = cus;
-  ctx->ws.sel_state = (uint32_t*)(p + offs[kSelState]);
-  ctx->ws.sel_cand = (void*)(p + offs[kSelCand]);
-  ctx->ws.sel_cand_bytes = sizes[kSelCand];
-  ctx->ws.sel_count = (uint32_t*)(p + offs[kSelCount]);
+  ctx->ws.sub_stage = (uint32_t*)(p + offs[kSubStage]);
   ctx->ws.res_count = (uint32_t*)(p + offs[kResCount]);
-  ctx->ws.sel_hist = (uint32_t*)(p + offs[kSelHist]);
-  ctx->ws.block_row0 = (int32_t*)(p + offs[kBlockRow0]);
-  ctx->ws.sel_hist_x = (uint32_t*)(p + offs[kSelHistX]);
-  ctx->ws.tile_max = (float*)(p + offs[kTileMax]);
+  ctx->ws.tile_info = (uint2*)(p + offs[kTileInfo]);
 
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
@@ -286,60 +274,23 @@ fm_status fm_score_fp8(fm_ctx* ctx, const float* q, const float* w, const uint8_
   return score_common(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer, stream, true);
 }
 
-static fm_status score_select_common(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B,
-                                     int64_t N, const int32_t* valid_n, fm_ensemble mode, int sel, int32_t top_k,
-                                     float threshold, float* scores, uint8_t* mask, float* per_layer, void* stream) {
+fm_status fm_score_threshold(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
+                             const int32_t* valid_n, fm_ensemble mode, float threshold, float* scores, uint8_t* mask,
+                             float* per_layer, void* stream) {
   g_err.clear();
-  const char* name = sel == fm::kSelTopK ? "fm_score_topk" : "fm_score_threshold";
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
   if (mode != FM_ENSEMBLE_MAX && mode != FM_ENSEMBLE_MEAN) return fail(FM_EINVAL, "unknown ensemble mode %d", (int)mode);
-  if (sel == fm::kSelTopK && top_k < 0) return fail(FM_EINVAL, "top_k = %d < 0", top_k);
-  if (sel == fm::kSelThreshold && !std::isfinite(threshold)) return fail(FM_EINVAL, "threshold must be finite");
-  if (sel == fm::kSelTopK) ctx->topk.valid = false;
-  if (B == 0 || N == 0) {
-    if (sel == fm::kSelTopK) ctx->topk = fm_topk_pending{true, scores, mask, valid_n, B, N, top_k};
-    return FM_OK;
-  }
-  if (!q || !w || !comp_k || !scores || !mask) return fail(FM_EINVAL, "null pointer to %s", name);
+  if (!std::isfinite(threshold)) return fail(FM_EINVAL, "threshold must be finite");
+  if (B == 0 || N == 0) return FM_OK;
+  if (!q || !w || !comp_k || !scores || !mask) return fail(FM_EINVAL, "null pointer to fm_score_threshold");
   if (!aligned(q, 16) || !aligned(w, 16) || !aligned(comp_k, 4) || !aligned(scores, 4) ||
       (per_layer && !aligned(per_layer, 4)) || (valid_n && !aligned(valid_n, 4)))
     return fail(FM_EINVAL, "q, w must be 16-byte aligned; comp_k, scores, per_layer, valid_n 4-byte aligned");
-  hipError_t e = fm::launch_score_select(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, sel, threshold, scores, mask,
-                                         per_layer, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, sel == fm::kSelTopK ? "fm_score_topk launch" : "fm_score_threshold launch");
-  if (sel == fm::kSelTopK) ctx->topk = fm_topk_pending{true, scores, mask, valid_n, B, N, top_k};
-  return FM_OK;
-}
-
-fm_status fm_score_topk(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
-                        const int32_t* valid_n, fm_ensemble mode, int32_t top_k, float* scores, uint8_t* mask,
-                        float* per_layer, void* stream) {
-  return score_select_common(ctx, q, w, comp_k, B, N, valid_n, mode, fm::kSelTopK, top_k, 0.f, scores, mask, per_layer,
-                             stream);
-}
-
-fm_status fm_score_threshold(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
-                             const int32_t* valid_n, fm_ensemble mode, float threshold, float* scores, uint8_t* mask,
-                             float* per_layer, void* stream) {
-  return score_select_common(ctx, q, w, comp_k, B, N, valid_n, mode, fm::kSelThreshold, 0, threshold, scores, mask,
-                             per_layer, stream);
-}
-
-fm_status fm_select_topk_finish(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
-                                int32_t top_k, uint8_t* mask, void* stream) {
-  g_err.clear();
-  fm_status st = check_ctx(ctx);
-  if (st != FM_OK) return st;
-  const fm_topk_pending& p = ctx->topk;
-  if (!p.valid || p.scores != scores || p.mask != mask || p.valid_n != valid_n || p.B != B || p.N != N ||
-      p.top_k != top_k)
-    return fail(FM_EINVAL, "fm_select_topk_finish must follow fm_score_topk on this context with the same scores, "
-                           "mask, valid_n, B, N and top_k");
-  if (B == 0 || N == 0) return FM_OK;
-  hipError_t e = fm::launch_topk_finish(ctx->ws, scores, B, N, valid_n, top_k, mask, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "fm_select_topk_finish launch");
+  hipError_t e = fm::launch_score_threshold(ctx->ws, q, w, comp_k, B, N, valid_n, (int)mode, threshold, scores, mask,
+                                            per_layer, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_score_threshold launch");
   return FM_OK;
 }
 

@@ -54,23 +54,21 @@ constexpr int kW8Stride = kHeads + 4;
 // takes an equal share of the row-major list of 16-chunk tiles.
 constexpr int kMaxScoreBlocks = 1024;
 
-// Top-K selection: a block covers kSelSlice consecutive chunks of one row.
-constexpr int kSelThreads = 256;
-constexpr int kSelItems = 16;
-constexpr int kSelSlice = kSelThreads * kSelItems;
+// Histogram bins of the exact selections.
 constexpr int kSelBins = 2048;
+
+// Subset top-K: words staged per row for a list's gathered keys (32 rounds
+// of 1024 keys, then 32 validity words per round).
+constexpr size_t kSubStageRowWords = 32 * 1024 + 32 * 32;
 
 // Resident-set compaction: a block covers kResSlice chunks of one row.
 constexpr int kResSlice = 4096;
 
-// Selection folded into the score pass (fm_score_topk, fm_score_threshold).
-// Top-K: the score kernel counts every valid chunk's ensemble score into a
-// kHistBins-bin histogram over [0, 1] (bin = min(floor(score kHistBins),
-// kHistBins - 1)), per block and row in LDS, and writes each 16-chunk
-// tile's largest score; the finish kernel then reads only what lies at or
-// above the row's cut-off bin.
-constexpr int kHistBins = 2048;
-enum SelMode { kSelNone = 0, kSelTopK = 1, kSelThreshold = 2 };
+// Top-K selection: the scan kernel writes a 64-bit word per tile of 16 or
+// more chunks (histogram bins and positions of its largest scores); rows of
+// tile words are ceil(N / 16) rounded up to a multiple of 2 long (16-byte
+// aligned rows).
+inline __host__ __device__ int64_t tile_info_stride(int64_t N) { return ((N + 15) / 16 + 1) & ~(int64_t)1; }
 
 struct Workspace {
   // Weights packed at context creation: each row scaled by a power of two
@@ -91,21 +89,9 @@ struct Workspace {
   int64_t* row_tiles = nullptr;  // [max_batch + 1]: first tile of each row in the list of valid tiles
   int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
   int score_blocks = 0;          // compute units of the device
-  uint32_t* sel_state = nullptr; // [max_batch][4]
-  void* sel_cand = nullptr;      // [max_batch][max_n] uint2: candidate (key, chunk index) pairs, a region per slice
-                                 // (the subset top-K stages its gathered keys here too)
-  size_t sel_cand_bytes = 0;
-  uint32_t* sel_count = nullptr; // [max_batch][ceil(max_n / kSelSlice)]: candidates per slice
+  uint32_t* sub_stage = nullptr; // [max_batch][kSubStageRowWords]: the subset top-K's gathered keys
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
-  // Fused top-K: per score block the histograms of its first row and the
-  // row after it, the block's first row (-1 for a block with no tiles), a
-  // per-row histogram for rows a block reaches beyond those two (global
-  // atomics, zeroed by the query packing), and the largest score of every
-  // 16-chunk tile.
-  uint32_t* sel_hist = nullptr;  // [score_blocks][2][kHistBins]
-  int32_t* block_row0 = nullptr; // [score_blocks]
-  uint32_t* sel_hist_x = nullptr;// [max_batch][kHistBins]
-  float* tile_max = nullptr;     // [max_batch][ceil(max_n / 16)]
+  uint2* tile_info = nullptr;    // [max_batch][tile_info_stride(max_n)]: per tile, for the top-K finish
 };
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
@@ -132,14 +118,11 @@ hipError_t launch_score_plan(const Workspace& ws, const int32_t* valid_n, int B,
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream);
 
-// The score pass with the selection folded in (sel = kSelTopK or
-// kSelThreshold): scores as launch_score, plus the mask (threshold: final;
-// top-K: zeros, the histograms and tile maxima for launch_topk_finish).
-hipError_t launch_score_select(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
-                               int64_t N, const int32_t* valid_n, int mode, int sel, float threshold, float* scores,
-                               uint8_t* mask, float* per_layer, hipStream_t stream);
-hipError_t launch_topk_finish(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
-                              int32_t top_k, uint8_t* mask, hipStream_t stream);
+// The score pass writing the threshold keep mask as well (scores as
+// launch_score; mask[b][n] = score > threshold, 0 at or beyond valid_n).
+hipError_t launch_score_threshold(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
+                                  int64_t N, const int32_t* valid_n, int mode, float threshold, float* scores,
+                                  uint8_t* mask, float* per_layer, hipStream_t stream);
 
 // Subset top-K: init raises the LDS limit of the in-LDS variant (once, at
 // context creation).
@@ -160,18 +143,6 @@ hipError_t launch_resident_delta(const Workspace& ws, const uint8_t* prev, const
 
 }  // namespace fm
 
-// The arguments of the last fm_score_topk on a context: fm_select_topk_finish
-// must name the same ones (the histograms it reads belong to that call).
-struct fm_topk_pending {
-  bool valid = false;
-  const float* scores = nullptr;
-  uint8_t* mask = nullptr;
-  const int32_t* valid_n = nullptr;
-  int32_t B = 0;
-  int64_t N = 0;
-  int32_t top_k = 0;
-};
-
 struct fm_ctx {
   int device = 0;
   fm_config cfg{};
@@ -181,5 +152,4 @@ struct fm_ctx {
   fm::Workspace ws{};
   void* ws_base = nullptr;  // one allocation holding every workspace buffer
   size_t ws_bytes = 0;
-  fm_topk_pending topk{};
 };

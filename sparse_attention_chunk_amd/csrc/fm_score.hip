@@ -79,7 +79,7 @@ __device__ __forceinline__ int part_exponent(float m) {
 // layer's rows of the linear fragment.  The layer-0 block also writes the
 // zero rows.
 __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q, const float* __restrict__ w, int B,
-                                                     f16x8* __restrict__ qpack, uint32_t* __restrict__ hist_x) {
+                                                     f16x8* __restrict__ qpack) {
   __shared__ __attribute__((aligned(16))) _Float16 qs[kHeads][kHeadDim + 8];
   __shared__ float red[2][kHeadDim];
   __shared__ float vmax[2];
@@ -89,9 +89,6 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q
   const int t = threadIdx.x;
   const float* qb = q + ((size_t)layer * B + b) * kHeads * kHeadDim;
   f16x8* out = qpack + (size_t)b * kQFrags * 64;
-  // The fused top-K's global histogram row of this request row starts at zero.
-  if (hist_x && layer == 0)
-    for (int i = t; i < kHistBins; i += 256) hist_x[(size_t)b * kHistBins + i] = 0u;
   float4 v[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -215,10 +212,13 @@ __device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], cons
 
 // Head reduction, sigmoid, ensemble and store of one tile.  wh = w / 2,
 // ub[l] = 2^-b_l.
-template <bool MEAN, bool PER_LAYER, int SEL, bool HGLB>
+// With the threshold mask folded in (THR), also writes the mask of the tile
+// before (its scores in e_pend) and leaves this tile's scores in e_pend.
+template <bool MEAN, bool PER_LAYER, bool THR>
 __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
                                             const f32x4 (&wh)[kLayers][4], const float (&ub)[kLayers], float s,
-                                            int tile) {
+                                            int tile, float& e_pend) {
+  if (THR) threshold_tile(cx, e_pend, tile - 1);
   float t[kLayers];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -231,7 +231,8 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
     // add the three parts of the linear term, group 3 holds zero there.
     t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  store_tile<MEAN, PER_LAYER, SEL, HGLB>(cx, t, fabsf(s), tile);
+  const float e = store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
+  if (THR) e_pend = e;
 }
 
 // Instruction order of one phase for the scheduler: the fp8 MFMA (32
@@ -263,30 +264,15 @@ __device__ __forceinline__ void interleave_phase() {
 // and the decode of tile i+1; the records of tile i+6 are requested in the
 // same phase (6 tiles in flight).  Tiles past the run's chunks read as zeros
 // and their stores are dropped by the buffer range checks.
-// What the selection folded into the pass needs besides the scores.
-struct SelArgs {
-  uint8_t* mask;        // [B][N]
-  float* tile_max;      // [B][ceil(N / 16)]
-  uint32_t* hist_x;     // [B][kHistBins]: rows past a block's two LDS slots
-  uint32_t* sel_hist;   // [blocks][2][kHistBins]
-  int32_t* block_row0;  // [blocks]
-  float threshold;
-};
-
-template <bool MEAN, bool PER_LAYER, int SEL, bool HGLB>
+template <bool MEAN, bool PER_LAYER, bool THR>
 __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const float* __restrict__ w,
                                           const uint8_t* __restrict__ comp_k, int B, int64_t N, int b, int64_t start,
                                           int64_t count, int lane, float* __restrict__ scores,
-                                          float* __restrict__ per_layer, const SelArgs& sa, int hist_off) {
+                                          float* __restrict__ per_layer, uint8_t* __restrict__ mask, float threshold) {
   Ctx cx = make_ctx<PER_LAYER>(comp_k, B, N, b, start, count, lane, scores, per_layer);
-  if (SEL != kSelNone) {
-    cx.mask = sa.mask + (size_t)b * N + start;
-    cx.threshold = sa.threshold;
-  }
-  if (SEL == kSelTopK) {
-    cx.tmax = sa.tile_max + (size_t)b * ((N + kTile - 1) / kTile) + start / kTile;
-    cx.hist_off = hist_off;
-    cx.hist_glb = sa.hist_x + (size_t)b * kHistBins;
+  if (THR) {
+    cx.mask = mask + (size_t)b * N + start;
+    cx.threshold = threshold;
   }
 
   // Query fragments, the linear-term fragment and its scales, and w: every load is issued
@@ -351,6 +337,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   f16x8 kf[2][4];
   f32x4 acc[2][kLayers][4];
   f32x4 lin[2];
+  float e_pend = 0.f;  // scores of the tile whose threshold mask is still to be written
 
   // Phase of tile i, P = i mod 8 (compile-time, so every register index is
   // static): MFMAs of tile i; finish tile i-1 (its scale still in its ring
@@ -359,8 +346,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 #define FM_PHASE(P, I)                                                                                \
   {                                                                                                   \
     mfma_tile(qf, qlin, ring[(P) & 7], kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                     \
-    finish_tile<MEAN, PER_LAYER, SEL, HGLB>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,       \
-                                 ring[((P) + 7) & 7].s, (I) - 1);                                     \
+    finish_tile<MEAN, PER_LAYER, THR>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,             \
+                                            ring[((P) + 7) & 7].s, (I) - 1, e_pend);                  \
     decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
     interleave_phase();                                                                               \
@@ -387,17 +374,15 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
     FM_PHASE(0, i + 7)
     i += 8;
   } while (i < tiles);
-  finish_tile<MEAN, PER_LAYER, SEL, HGLB>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1);  // tile i - 1 = 0 mod 8
+  finish_tile<MEAN, PER_LAYER, THR>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, e_pend);  // tile i - 1 = 0 mod 8
+  if (THR) threshold_tile(cx, e_pend, i - 1);
 #undef FM_PHASE
 }
 
 // grid = number of compute units, block = 256 (one wave per SIMD); each wave
-// scores its share of the tile list (walk_share).  With the top-K folded in,
-// the block counts its rows' scores in LDS: slot 0 for the row of the
-// block's first tile, slot 1 for the next row, the global per-row histogram
-// for any further row; the slots go to the block's global histograms when
-// every wave is done.
-template <bool MEAN, bool PER_LAYER, int SEL>
+// scores its share of the tile list (walk_share).  THR: the threshold mask
+// is written by the pass.
+template <bool MEAN, bool PER_LAYER, bool THR>
 __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__ qpack, const float* __restrict__ w,
                                                        const uint8_t* __restrict__ comp_k, int B, int64_t N,
                                                        const int32_t* __restrict__ valid_n,
@@ -405,34 +390,12 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
                                                        const int32_t* __restrict__ wave_row,
                                                        int64_t total_tiles,  // used when row_tiles is null
                                                        float* __restrict__ scores, float* __restrict__ per_layer,
-                                                       SelArgs sa) {
+                                                       uint8_t* __restrict__ mask, float threshold) {
   const int lane = threadIdx.x & 63;
-  uint32_t* const lds_hist = fm_score_lds;  // 2 x kHistBins with the top-K folded in
-  int row0 = 0;
-  if (SEL == kSelTopK) {
-    for (int i = threadIdx.x; i < 2 * kHistBins; i += 256) lds_hist[i] = 0u;
-    const int64_t waves = 4 * (int64_t)gridDim.x;
-    const int64_t total = row_tiles ? row_tiles[B] : total_tiles;
-    const int64_t t0 = 4 * (int64_t)blockIdx.x * total / waves;
-    const int64_t t1 = 4 * ((int64_t)blockIdx.x + 1) * total / waves;
-    row0 = t1 > t0 ? (row_tiles ? wave_row[4 * blockIdx.x] : (int)(t0 / ((N + kTile - 1) / kTile))) : -1;
-    __syncthreads();
-  }
   walk_share(B, N, valid_n, row_tiles, wave_row, total_tiles, [&](int b, int64_t start, int64_t count) {
-    const int slot = b - row0;
-    if (SEL == kSelTopK && slot >= 2)
-      score_run<MEAN, PER_LAYER, SEL, true>(qpack, w, comp_k, B, N, b, start, count, lane, scores, per_layer, sa, -1);
-    else
-      score_run<MEAN, PER_LAYER, SEL, false>(qpack, w, comp_k, B, N, b, start, count, lane, scores, per_layer, sa,
-                                             slot * kHistBins);
+    score_run<MEAN, PER_LAYER, THR>(qpack, w, comp_k, B, N, b, start, count, lane, scores, per_layer, mask,
+                                    threshold);
   });
-  if (SEL == kSelTopK) {
-    __syncthreads();
-    uint4* dst = (uint4*)(sa.sel_hist + (size_t)blockIdx.x * 2 * kHistBins);
-    const uint4* src = (const uint4*)lds_hist;
-    for (int i = threadIdx.x; i < 2 * kHistBins / 4; i += 256) dst[i] = src[i];
-    if (threadIdx.x == 0) sa.block_row0[blockIdx.x] = row0;
-  }
 }
 
 // Plan for ragged rows (one block of 1024 threads): row_tiles[b] = sum of
@@ -508,6 +471,24 @@ __global__ __launch_bounds__(256) void score_tail_kernel(const int32_t* __restri
   }
 }
 
+// Threshold mask of each row's last N % 4 chunks: the score pass writes the
+// mask in whole words and stops at the row's last whole word (runs start on
+// 16-chunk tiles, so that word ends at N - N % 4 in every run of the row).
+// grid = B, block = 64.
+__global__ __launch_bounds__(64) void threshold_edge_kernel(const float* __restrict__ scores,
+                                                            const int32_t* __restrict__ valid_n, int64_t N,
+                                                            float threshold, uint8_t* __restrict__ mask) {
+  const int b = blockIdx.x;
+  const int64_t n = (N & ~(int64_t)3) + threadIdx.x;
+  if (n >= N) return;
+  int64_t vn = N;
+  if (valid_n) {
+    const int64_t v = valid_n[b];
+    vn = v < 0 ? 0 : (v > N ? N : v);
+  }
+  mask[(size_t)b * N + n] = (n < vn && scores[(size_t)b * N + n] > threshold) ? 1 : 0;
+}
+
 }  // namespace
 
 namespace {
@@ -532,25 +513,26 @@ hipError_t plan_and_tail(const Workspace& ws, const int32_t* valid_n, int B, int
   return hipGetLastError();
 }
 
-template <int SEL>
+template <bool THR>
 hipError_t launch_score_sel(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
                             int64_t N, const int32_t* valid_n, int mode, float threshold, float* scores,
                             uint8_t* mask, float* per_layer, hipStream_t stream) {
   f16x8* qpack = (f16x8*)ws.qpack;
-  hipLaunchKernelGGL(pack_q_kernel, dim3(B * kLayers), dim3(256), 0, stream, q, w, B, qpack,
-                     SEL == kSelTopK ? ws.sel_hist_x : (uint32_t*)nullptr);
+  hipLaunchKernelGGL(pack_q_kernel, dim3(B * kLayers), dim3(256), 0, stream, q, w, B, qpack);
   const int64_t* row_tiles;
   int64_t total_tiles;
-  hipError_t e = plan_and_tail(ws, valid_n, B, N, scores, per_layer, SEL == kSelNone ? nullptr : mask, stream,
-                               &row_tiles, &total_tiles);
+  hipError_t e = plan_and_tail(ws, valid_n, B, N, scores, per_layer, THR ? mask : nullptr, stream, &row_tiles,
+                               &total_tiles);
   if (e != hipSuccess) return e;
-  SelArgs sa{mask, ws.tile_max, ws.sel_hist_x, ws.sel_hist, ws.block_row0, threshold};
   const bool mean = mode == FM_ENSEMBLE_MEAN;
-  auto kern = mean ? (per_layer ? score_kernel<true, true, SEL> : score_kernel<true, false, SEL>)
-                   : (per_layer ? score_kernel<false, true, SEL> : score_kernel<false, false, SEL>);
-  const size_t lds = SEL == kSelTopK ? 2 * kHistBins * sizeof(uint32_t) : 0;
-  hipLaunchKernelGGL(kern, dim3(ws.score_blocks), dim3(256), lds, stream, (const f16x8*)qpack, w, comp_k, B, N,
-                     valid_n, row_tiles, (const int32_t*)ws.wave_row, total_tiles, scores, per_layer, sa);
+  auto kern = mean ? (per_layer ? score_kernel<true, true, THR> : score_kernel<true, false, THR>)
+                   : (per_layer ? score_kernel<false, true, THR> : score_kernel<false, false, THR>);
+  hipLaunchKernelGGL(kern, dim3(ws.score_blocks), dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N,
+                     valid_n, row_tiles, (const int32_t*)ws.wave_row, total_tiles, scores, per_layer, mask,
+                     threshold);
+  if (THR && (N & 3))
+    hipLaunchKernelGGL(threshold_edge_kernel, dim3(B), dim3(64), 0, stream, (const float*)scores, valid_n, N,
+                       threshold, mask);
   return hipGetLastError();
 }
 
@@ -563,17 +545,13 @@ hipError_t launch_score_plan(const Workspace& ws, const int32_t* valid_n, int B,
 
 hipError_t launch_score(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B, int64_t N,
                         const int32_t* valid_n, int mode, float* scores, float* per_layer, hipStream_t stream) {
-  return launch_score_sel<kSelNone>(ws, q, w, comp_k, B, N, valid_n, mode, 0.f, scores, nullptr, per_layer, stream);
+  return launch_score_sel<false>(ws, q, w, comp_k, B, N, valid_n, mode, 0.f, scores, nullptr, per_layer, stream);
 }
 
-hipError_t launch_score_select(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
-                               int64_t N, const int32_t* valid_n, int mode, int sel, float threshold, float* scores,
-                               uint8_t* mask, float* per_layer, hipStream_t stream) {
-  if (sel == kSelTopK)
-    return launch_score_sel<kSelTopK>(ws, q, w, comp_k, B, N, valid_n, mode, threshold, scores, mask, per_layer,
-                                      stream);
-  return launch_score_sel<kSelThreshold>(ws, q, w, comp_k, B, N, valid_n, mode, threshold, scores, mask, per_layer,
-                                         stream);
+hipError_t launch_score_threshold(const Workspace& ws, const float* q, const float* w, const uint8_t* comp_k, int B,
+                                  int64_t N, const int32_t* valid_n, int mode, float threshold, float* scores,
+                                  uint8_t* mask, float* per_layer, hipStream_t stream) {
+  return launch_score_sel<true>(ws, q, w, comp_k, B, N, valid_n, mode, threshold, scores, mask, per_layer, stream);
 }
 
 }  // namespace fm

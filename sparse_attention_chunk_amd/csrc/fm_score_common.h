@@ -54,13 +54,18 @@ __device__ __forceinline__ float sum4rows(float v) {
   swap16(v, w);
   return v + w;
 }
+// max(a, b) as the median of (a, b, +inf): one instruction, with no
+// quieting of the lane-swapped operands (NaN scores are not ordered).
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_huge_valf());
+}
 __device__ __forceinline__ float max4rows(float v) {
   float w = v;
   swap32(v, w);
-  v = fmaxf(v, w);
+  v = max2(v, w);
   w = v;
   swap16(v, w);
-  return fmaxf(v, w);
+  return max2(v, w);
 }
 
 // The three layers' logits of every chunk from the lanes' partial sums:
@@ -106,14 +111,12 @@ struct Ctx {
   uint32_t lane_out_off;                 // 4 c in lane group 0, out of range elsewhere
   uint32_t lane_pl_off[kLayers];         // 4 c in the lane row holding layer l's total, out of range elsewhere
   int c, g;
-  // Selection folded into the pass (unused without it).
+  // Threshold mask folded into the pass (unused without it).
   uint8_t* mask;                         // mask bytes of this run's chunks
-  float* tmax;                           // largest score of each of this run's tiles
-  int32_t hist_off;                      // the row's histogram slot in fm_score_lds, or -1: hist_glb
-  uint32_t* hist_glb;                    // the row's global histogram (rows past the block's two slots)
   int32_t count;                         // chunks in the run
-  uint32_t lane_mask_off;                // c in lane group 0, out of range elsewhere
-  uint32_t lane_tmax_off;                // 0 in lane 15, out of range elsewhere
+  int32_t mask_words;                    // mask bytes written as whole words: the run's words inside its row
+  uint32_t lane_mask_off;                // 4 l in lanes l = 0..3 (one word of 4 mask bytes each), out of range elsewhere
+  uint32_t nib_shift;                    // 4 (l % 4): lane l's four chunks in the tile's compare mask
   float threshold;
 };
 
@@ -133,11 +136,17 @@ __device__ __forceinline__ Ctx make_ctx(const uint8_t* comp_k, int B, int64_t N,
   cx.out_bytes = (int32_t)(count * 4);
   cx.count = (int32_t)count;
   cx.mask = nullptr;
-  cx.tmax = nullptr;
-  cx.hist_off = -1;
-  cx.hist_glb = nullptr;
-  cx.lane_mask_off = cx.g == 0 ? (uint32_t)cx.c : kDropOffset;
-  cx.lane_tmax_off = lane == 15 ? 0u : kDropOffset;
+  cx.lane_mask_off = lane < 4 ? (uint32_t)(4 * lane) : kDropOffset;
+  cx.nib_shift = 4u * (uint32_t)(lane & 3);
+  {
+    // Words up to the run's last chunk rounded up to a word, but never past
+    // the row's last whole word (bytes beyond a row's valid chunks are zero
+    // in the mask, so a word may cover them; the row's last N % 4 bytes are
+    // written by a separate kernel after the pass).
+    const int64_t words = (count + 3) & ~(int64_t)3;
+    const int64_t row_words = (N - start) & ~(int64_t)3;
+    cx.mask_words = (int32_t)(words < row_words ? words : row_words);
+  }
   cx.threshold = 0.f;
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -147,8 +156,10 @@ __device__ __forceinline__ Ctx make_ctx(const uint8_t* comp_k, int B, int64_t N,
   return cx;
 }
 
+// A buffer from byte `from` to `bytes` of a run's buffer (empty when `from`
+// is past the end, or negative: the tile before the run's first).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int32_t bytes, int32_t from) {
-  const int32_t left = bytes - from;
+  const int32_t left = from < 0 ? 0 : bytes - from;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + from), 0, left > 0 ? left : 0,
                                            kBufferWord3);
 }
@@ -160,59 +171,32 @@ __device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
   t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, cx.lane_scale_off, 0, 0));
 }
 
-// Dynamic LDS of the score kernels: the fused top-K's two histogram slots
-// (none otherwise).
-extern __shared__ uint32_t fm_score_lds[];
-
-// Largest of the 16 lanes of each lane row, in lane 15 of the row (scores
-// are >= 0, so their bit patterns order as unsigned integers; a lane with no
-// source contributes 0).
-__device__ __forceinline__ uint32_t row_max_bits(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
-  return v;
-}
-
-// Histogram bin of an ensemble score in [0, 1].
-__device__ __forceinline__ int score_bin(float e) {
-  const int b = (int)(e * (float)kHistBins);
-  return b < kHistBins - 1 ? b : kHistBins - 1;
-}
-
-// The selection's share of a tile's epilogue: threshold mode stores the
-// mask byte (score > threshold); top-K mode stores a zero mask byte, counts
-// the score into the row's histogram and stores the tile's largest score.
-// Chunks past the run are neither stored nor counted.
-// Every lane takes part in the histogram atomic, adding 1 in lane group 0
-// for a valid chunk and 0 otherwise: no branch splits the phase (the other
-// groups hold the same scores, so they only touch the same bins).
-// HGLB: the row's histogram is the global one (chosen per run).
-template <int SEL, bool HGLB>
-__device__ __forceinline__ void select_tile(const Ctx& cx, float e, int tile) {
+// Threshold mode folded into the score pass: the tile's 16 mask bytes,
+// score > threshold, go out as four words from lanes 0..3, built from the
+// compare mask (bit c is chunk c: lane l spreads bits 4l..4l+3 to the bytes
+// of its word; chunks past the run give 0).  The score pipeline runs it one
+// phase after the tile's scores (for tile i - 2 in the phase of tile i), so
+// that it does not wait on the phase's own epilogue chain; the tile before
+// the first (tile -1) writes nothing.
+__device__ __forceinline__ void threshold_tile(const Ctx& cx, float e, int tile) {
   const int32_t n0 = tile * kTile;
-  const uint32_t mb = SEL == kSelThreshold ? (e > cx.threshold ? 1u : 0u) : 0u;
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)mb, tile_rsrc(cx.mask, cx.count, n0), cx.lane_mask_off, 0, 0);
-  if (SEL == kSelTopK) {
-    const bool valid = n0 + cx.c < cx.count;
-    const uint32_t inc = cx.g == 0 && valid ? 1u : 0u;
-    if (HGLB) atomicAdd(cx.hist_glb + score_bin(e), inc);
-    else atomicAdd(&fm_score_lds[cx.hist_off + score_bin(e)], inc);
-    const uint32_t m = row_max_bits(valid ? __float_as_uint(e) : 0u);
-    __builtin_amdgcn_raw_buffer_store_b32(m, tile_rsrc(cx.tmax, (cx.count + kTile - 1) / kTile * 4, tile * 4),
-                                          cx.lane_tmax_off, 0, 0);
-  }
+  const int32_t tile_valid = n0 < 0 ? 0 : cx.count - n0;  // chunks of this tile inside the run (wave-uniform)
+  const uint64_t keep = __ballot(e > cx.threshold && cx.c < tile_valid);
+  const uint32_t nib = (uint32_t)(keep >> cx.nib_shift) & 0xfu;
+  const uint32_t word = (nib * 0x204081u) & 0x01010101u;  // bit k -> byte k (a 24-bit multiply)
+  __builtin_amdgcn_raw_buffer_store_b32(word, tile_rsrc(cx.mask, cx.mask_words, n0), cx.lane_mask_off, 0, 0);
 }
 
-// Ensemble and store of one tile.  u[l] is this lane's part of layer l's
+// Ensemble and score store of one tile; returns the tile's ensemble scores
+// (lane c and its copies in the other lane groups: chunk c).  u[l] is this
+// lane's part of layer l's
 // logit divided by |s| (as = |s|, the chunk's scale magnitude): the logit is
 // |s| times the sum of u[l] over the four lane groups, and since |s| >= 0,
 // max_l sigmoid(|s| T_l) = sigmoid(|s| max_l T_l) takes one sigmoid.  For
 // the mean and per-layer outputs each lane row computes the sigmoid of the
 // layer total it holds.
-template <bool MEAN, bool PER_LAYER, int SEL = kSelNone, bool HGLB = false>
-__device__ __forceinline__ void store_tile(const Ctx& cx, const float (&u)[kLayers], float as, int tile) {
+template <bool MEAN, bool PER_LAYER>
+__device__ __forceinline__ float store_tile(const Ctx& cx, const float (&u)[kLayers], float as, int tile) {
   const int32_t to = tile * (kTile * 4);
   float e;
   if (MEAN || PER_LAYER) {
@@ -230,7 +214,7 @@ __device__ __forceinline__ void store_tile(const Ctx& cx, const float (&u)[kLaye
     e = sigmoid(as * max4rows(layer_totals(u, false)));
   }
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), tile_rsrc(cx.out, cx.out_bytes, to), cx.lane_out_off, 0, 0);
-  if (SEL != kSelNone) select_tile<SEL, HGLB>(cx, e, tile);
+  return e;
 }
 
 // The persistent grid's work split: the valid tiles of all rows, in

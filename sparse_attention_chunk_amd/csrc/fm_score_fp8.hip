@@ -220,7 +220,7 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
     // add the three parts of the linear term, group 3 holds zero there.
     t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
+  (void)store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
 }
 
 // Instruction order of one phase: every MFMA followed by up to four

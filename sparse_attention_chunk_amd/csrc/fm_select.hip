@@ -4,22 +4,28 @@
 //
 // Top-K is an exact per-row selection on order-preserving 32-bit keys of the
 // fp32 scores; ties at the K-th key go to the lowest chunk indices, which
-// makes the mask unique.  Three kernels per call:
-//   1. sample: one block per row reads 4096 keys (64 runs of 64 chunks
-//      spread over the row; the whole row when it is shorter) and picks a
-//      cut-off L, the m-th largest sampled key, with m chosen so that about
-//      K plus four standard deviations of the row's keys are expected at or
-//      above L (a row that fits in the sample gets its exact K-th key);
-//   2. collect: one pass over the row writes the mask (0 everywhere, 1 for
-//      every valid chunk when K keeps them all) and writes the (key, index)
-//      pairs of keys >= L to the row's candidate list, one region per block;
-//   3. final: one block per row selects exactly among the candidates: radix
-//      passes over the key give the K-th largest key T and how many keys equal
-//      to T are kept, radix passes over the index of the keys equal to T (only
-//      when some are left out) give the last index kept; those candidates'
-//      mask bytes are set.  When fewer
-//      than K keys reached L (the sample was unrepresentative), the same
-//      passes run over the whole row instead, so the result is always exact.
+// makes the mask unique.  Two kernels per call:
+//   1. scan (every chunk, all compute units): the mask bytes (0, or 1 for
+//      every valid chunk of a row whose K keeps them all) and a word per
+//      tile of the row: the histogram bins of the tile's three largest
+//      scores and the positions of the largest two.  A tile is 16, 32 or 64
+//      chunks, the largest that still leaves 4 K tiles in the row;
+//   2. finish (one block per row): the histogram of the row's tile maxima
+//      gives the bin c of the K-th largest tile maximum L (bin 0 when the
+//      row has fewer than K tiles).  The K tiles with the largest maxima hold
+//      K distinct chunks scoring at least L, so the K-th largest score is
+//      >= L: every chunk of the top K is in bin c or above, and so is its
+//      tile's maximum.  Of a tile whose maximum is in bin c or above, only
+//      the chunks of its largest scores down to the first one below bin c
+//      can be: one or two known chunks, or, when the third largest is in bin
+//      c or above too, all the tile's chunks.  Those in bin c or above
+//      (about K) are the candidates.  One more histogram, of the candidates'
+//      keys between their smallest and largest, gives the bin of the K-th
+//      largest candidate: the candidates above it are kept, those in it are
+//      ranked (key descending, index ascending) for the rest.
+// When the listed chunks or the candidates overflow LDS (many equal or
+// nearly equal scores), the finish selects exactly over the whole row with
+// radix passes instead, so the result is always the exact top-K.
 #include "fm_radix.h"
 
 namespace fm {
@@ -33,473 +39,496 @@ __device__ inline int64_t row_valid(const int32_t* valid_n, int b, int64_t N) {
   return v < 0 ? 0 : (v > N ? N : v);
 }
 
-// state[b] = {cut-off L, unused, mode, unused}
-enum : uint32_t { kSelect = 0, kKeepAll = 1, kKeepNone = 2 };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile16 = 16;  // chunks per tile of the score pass (tile maxima)
-constexpr int kSampleRuns = 64;
-constexpr int kSampleRun = 64;
-constexpr int kSampleSize = kSampleRuns * kSampleRun;  // 4096
-constexpr int kSampleThreads = 1024;
-constexpr int kSamplePerThread = kSampleSize / kSampleThreads;  // 4
+constexpr int kSub = 16;             // chunks per scan thread (a tile is 1, 2 or 4 of these)
+constexpr int kScanThreads = 256;
+constexpr int kScanSlice = kScanThreads * kSub;
+constexpr int kFinishThreads = 256;
+constexpr int kFinishRegPairs = 8;   // pairs of tile words per thread read into registers (4096 tiles a row)
+constexpr int kFinishRegEntries = 4; // listed chunks per thread held in registers (1024 a row)
+constexpr int kFinishList = 4096;    // listed chunks held in LDS
+constexpr int kFinishFull = 256;     // tiles listed whole
+constexpr int kFinishCand = 4096;    // candidates held in LDS
+constexpr float kHistScale = kSelBins - 0.25f;
+constexpr int kRawBuffer = 0x00020000;         // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x40000000u;  // a byte offset past every buffer here: loads give 0
+constexpr uint32_t kNone = 0xffffffffu;        // no chunk
 
-// 1. Cut-off per row from a sample.  grid = B, block = kSampleThreads.
-__global__ __launch_bounds__(kSampleThreads) void sel_sample_kernel(const float* scores, int64_t N,
-                                                                    const int32_t* valid_n, int32_t top_k,
-                                                                    uint32_t* state) {
-  const int b = blockIdx.x;
-  const int64_t vn = row_valid(valid_n, b, N);
-  uint32_t mode = kSelect;
-  if (top_k == 0 || vn == 0) mode = kKeepNone;
-  else if ((int64_t)top_k >= vn) mode = kKeepAll;
-  if (mode != kSelect) {
-    if (threadIdx.x == 0) {
-      state[4 * b + 0] = 0;
-      state[4 * b + 2] = mode;
-    }
-    return;
-  }
-  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
-  __shared__ uint32_t s_wtot[kSampleThreads / 64];
-  __shared__ uint32_t s_out[3];
-  const float* row = scores + (size_t)b * N;
-  const bool whole = vn <= kSampleSize;
-  const uint32_t S = whole ? (uint32_t)vn : (uint32_t)kSampleSize;
-  // Sample i = t + kSampleThreads * j sits in run r = i / kSampleRun at
-  // offset t % kSampleRun; run r starts at r (vn - kSampleRun) / 63 (32-bit:
-  // 63 * 2^26 fits).  Loads go through a descriptor over the row's valid
-  // scores with no branch, all issued before the first use.
-  const int t = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, (int)(vn * 4), 0x00020000);
-  const uint32_t span = whole ? 0u : (uint32_t)(vn - kSampleRun);
-  float v[kSamplePerThread];
-#pragma unroll
-  for (int j = 0; j < kSamplePerThread; ++j) {
-    const uint32_t i = (uint32_t)t + kSampleThreads * j;
-    const uint32_t r = i / kSampleRun;
-    const uint32_t n = whole ? i : r * span / (kSampleRuns - 1) + (i % kSampleRun);
-    v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, 4u * n, 0, 0));
-  }
-  uint32_t kr[kSamplePerThread];
-#pragma unroll
-  for (int j = 0; j < kSamplePerThread; ++j) kr[j] = order_key(v[j]);
-  uint32_t m;
-  if (whole) {
-    m = (uint32_t)top_k;  // the sample is the row: its K-th key exactly
-  } else {
-    const double expect = (double)top_k * (double)S / (double)vn;
-    const double mm = ceil(expect + 4.0 * sqrt(expect) + 16.0);
-    m = mm >= (double)S ? S : (uint32_t)mm;
-  }
-  uint32_t L, unused;
-  radix_select<kSampleThreads, false>(
-      [&](auto f) {
-#pragma unroll
-        for (int j = 0; j < kSamplePerThread; ++j) {
-          const uint32_t i = (uint32_t)t + kSampleThreads * j;
-          if (i < S) f(make_uint2(kr[j], i));
-        }
-      },
-      m, 0, h, s_wtot, s_out, &L, &unused);
-  if (threadIdx.x == 0) {
-    state[4 * b + 0] = L;
-    state[4 * b + 2] = mode;
-  }
+// Histogram bin of a score, floor(score (kSelBins - 1/4)) clamped to
+// [0, kSelBins): non-decreasing in the score, one bin per 1/2048 of [0, 1]
+// where sigmoid scores lie.
+__device__ __forceinline__ int score_bin(float e) {
+  const float x = e * kHistScale;
+  return !(x > 0.f) ? 0 : (x >= (float)(kSelBins - 1) ? kSelBins - 1 : (int)x);  // NaN: bin 0
+}
+// score_bin(e) >= c, for c in [0, kSelBins): x >= c when c >= 1, as the
+// integer part of x > 0 is at least c exactly when x is.
+__device__ __forceinline__ bool bin_at_least(float e, int c) { return c == 0 || e * kHistScale >= (float)c; }
+
+// log2 of the tile's kSub-chunk parts in a row of vn chunks (0..2): the
+// largest leaving at least 4 K tiles.
+__device__ __forceinline__ int tile_shift(int64_t vn, int32_t k) {
+  const int64_t need = 4 * (int64_t)k;
+  return (vn >> 6) >= need ? 2 : ((vn >> 5) >= need ? 1 : 0);
 }
 
-// 2. Mask and candidates.  grid = (blocks per row, B); thread t handles
-// kSelItems consecutive chunks.
-__global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const float* scores, int64_t N,
-                                                                  const int32_t* valid_n, const uint32_t* state,
-                                                                  uint2* cand, uint32_t* cand_count, uint8_t* mask) {
-  const int b = blockIdx.y;
-  const uint32_t L = state[4 * b + 0];
-  const uint32_t mode = state[4 * b + 2];
-  const int64_t vn = row_valid(valid_n, b, N);
-  const int64_t n0 = (int64_t)blockIdx.x * kSelSlice + (int64_t)threadIdx.x * kSelItems;
-  const float* row = scores + (size_t)b * N;
-  uint8_t* mrow = mask + (size_t)b * N;
-  // Candidates of this block go to its own region of the row's list (the
-  // region has room for the whole slice), counted without atomics.
-  uint2* crow = cand + (size_t)b * N + (size_t)blockIdx.x * kSelSlice;
+// Tile word: x bits 0-10 the largest score's bin, 11-16 its position in the
+// tile, 17-27 the second largest's bin; y bits 0-5 the second largest's
+// position, 6-16 the third largest's bin (bin 0 where there is none).  Ties
+// count as separate scores.
+__device__ __forceinline__ int tw_bin1(uint2 w) { return (int)(w.x & 0x7ffu); }
+__device__ __forceinline__ uint32_t tw_pos1(uint2 w) { return (w.x >> 11) & 0x3fu; }
+__device__ __forceinline__ int tw_bin2(uint2 w) { return (int)((w.x >> 17) & 0x7ffu); }
+__device__ __forceinline__ uint32_t tw_pos2(uint2 w) { return w.y & 0x3fu; }
+__device__ __forceinline__ int tw_bin3(uint2 w) { return (int)((w.y >> 6) & 0x7ffu); }
 
-  const uint8_t keep = mode == kKeepAll ? 1 : 0;
-  uint32_t ck[kSelItems];
-  uint32_t is_cand = 0;  // bit j: chunk n0 + j is a candidate
-  const bool full = n0 + kSelItems <= vn && ((((uintptr_t)(row + n0)) & 15) == 0);
-  if (full) {
-#pragma unroll
-    for (int q = 0; q < kSelItems / 4; ++q) {
-      const float4 v = *(const float4*)(row + n0 + 4 * q);
-      const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * q + e;
-        ck[j] = order_key(f[e]);
-        if (mode == kSelect && ck[j] >= L) is_cand |= 1u << j;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
-      const int64_t n = n0 + j;
-      ck[j] = 0;
-      if (n < vn) {
-        ck[j] = order_key(row[n]);
-        if (mode == kSelect && ck[j] >= L) is_cand |= 1u << j;
-      }
-    }
-  }
-  // Mask bytes: one 16-byte store when the run is whole, valid and aligned.
-  if (n0 + kSelItems <= vn && ((((uintptr_t)(mrow + n0)) & 15) == 0)) {
-    const uint32_t w = keep * 0x01010101u;
-    *(uint4*)(mrow + n0) = make_uint4(w, w, w, w);
-  } else {
-    for (int j = 0; j < kSelItems && n0 + j < N; ++j) mrow[n0 + j] = n0 + j < vn ? keep : 0;
-  }
-  // Candidates at each thread's prefix within the block.
-  __shared__ uint32_t s_wave[kSelThreads / 64];
-  const uint32_t mine = __popc(is_cand);
-  const uint32_t incl = wave_prefix_sum(mine);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    before += w < wave ? s_wave[w] : 0u;
-    tot += s_wave[w];
-  }
-  if (threadIdx.x == 0) cand_count[(size_t)b * gridDim.x + blockIdx.x] = tot;
-  uint32_t pos = before + incl - mine;
-#pragma unroll
-  for (int j = 0; j < kSelItems; ++j) {  // static indices keep ck[] in registers
-    if (is_cand & (1u << j)) crow[pos++] = make_uint2(ck[j], (uint32_t)(n0 + j));
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)bytes, kRawBuffer);
 }
 
-// 3. Exact selection among the candidates (or the whole row).  grid = B.
-constexpr int kFinThreads = 1024;
-constexpr int kFinLds = 8192;  // candidates held in registers (8 per thread); more are read from their regions each pass
+// The three largest of a set of scores: values m1 >= m2 >= m3, positions of
+// the first two.
+struct Top3 {
+  float m1, m2, m3;
+  uint32_t p1, p2;
+};
 
-__global__ __launch_bounds__(kFinThreads) void sel_final_kernel(const float* scores, int64_t N,
-                                                                const int32_t* valid_n, int blocks_per_row,
-                                                                int32_t top_k, const uint32_t* state,
-                                                                const uint2* cand, const uint32_t* cand_count,
-                                                                uint8_t* mask) {
-  const int b = blockIdx.x;
-  if (state[4 * b + 2] != kSelect) return;
-  const int64_t vn = row_valid(valid_n, b, N);
-  const float* row = scores + (size_t)b * N;
-  const uint2* crow = cand + (size_t)b * N;
-  const uint32_t* counts = cand_count + (size_t)b * blocks_per_row;
-  uint8_t* mrow = mask + (size_t)b * N;
-  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
-  __shared__ uint32_t s_wtot[kFinThreads / 64];
-  __shared__ uint32_t s_out[3];
-  __shared__ uint32_t s_off[kFinThreads];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-
-  // Candidate total, and the region offsets when a row has at most
-  // kFinThreads slices (N <= 2^22).
-  const bool small_rows = blocks_per_row <= kFinThreads;
-  uint32_t C = 0;
-  if (small_rows) {
-    const int r = threadIdx.x;
-    const uint32_t v = r < blocks_per_row ? counts[r] : 0u;
-    const uint32_t incl = wave_prefix_sum(v);
-    if (lane == 63) s_wtot[wave] = incl;
-    __syncthreads();
-    uint32_t below = 0;
-    for (int w = 0; w < kFinThreads / 64; ++w) {
-      below += w < wave ? s_wtot[w] : 0u;
-      C += s_wtot[w];
-    }
-    if (r < blocks_per_row) s_off[r] = below + incl - v;
-  } else {
-    uint32_t part = 0;
-    for (int r = threadIdx.x; r < blocks_per_row; r += kFinThreads) part += counts[r];
-    part = wave_sum_u32(part);
-    if (lane == 0) s_wtot[wave] = part;
-    __syncthreads();
-    for (int w = 0; w < kFinThreads / 64; ++w) C += s_wtot[w];
-  }
-  __syncthreads();
-
-  const uint32_t k = (uint32_t)top_k;
-  const int ib = index_bits(vn);
-  uint32_t T, last;
-  if (C >= k && small_rows && C <= (uint32_t)kFinLds) {
-    // The candidates stay in registers for every pass.  Candidate c lies in
-    // the slice r with s_off[r] <= c < s_off[r + 1] (binary search); all of a
-    // thread's loads are issued together.
-    constexpr int kPer = kFinLds / kFinThreads;
-    uint2 v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t c = threadIdx.x + kFinThreads * j;
-      v[j] = make_uint2(0u, 0u);
-      if (c < C) {
-        int lo = 0, hi = blocks_per_row - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_off[mid] <= c) lo = mid;
-          else hi = mid - 1;
-        }
-        v[j] = crow[(size_t)lo * kSelSlice + (c - s_off[lo])];
-      }
-    }
-    auto each = [&](auto f) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (threadIdx.x + kFinThreads * j < C) f(v[j]);
-    };
-    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
-    each([&](uint2 e) {
-      if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
-    });
-  } else if (C >= k) {
-    // Many candidates: read them from their regions in every pass.
-    auto each = [&](auto f) {
-      for (int r = wave; r < blocks_per_row; r += kFinThreads / 64) {
-        const uint32_t n_r = counts[r];
-        for (uint32_t i = lane; i < n_r; i += 64) f(crow[(size_t)r * kSelSlice + i]);
-      }
-    };
-    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
-    each([&](uint2 e) {
-      if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
-    });
-  } else {
-    // Fewer than K keys reached the cut-off: select over the whole row.
-    auto each = [&](auto f) {
-      for (int64_t n = threadIdx.x; n < vn; n += kFinThreads) f(make_uint2(order_key(row[n]), (uint32_t)n));
-    };
-    radix_select<kFinThreads>(each, k, ib, h, s_wtot, s_out, &T, &last);
-    each([&](uint2 e) {
-      if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
-    });
-  }
+__device__ __forceinline__ void top3_take(Top3& a, float v, uint32_t pos) {
+  const bool gt1 = v > a.m1;
+  const bool gt2 = v > a.m2;
+  a.m3 = gt2 ? a.m2 : fmaxf(a.m3, v);
+  a.m2 = gt1 ? a.m1 : (gt2 ? v : a.m2);
+  a.p2 = gt1 ? a.p1 : (gt2 ? pos : a.p2);
+  a.m1 = gt1 ? v : a.m1;
+  a.p1 = gt1 ? pos : a.p1;
 }
 
-__global__ __launch_bounds__(256) void threshold_kernel(const float* scores, int64_t N, const int32_t* valid_n,
-                                                        float threshold, uint8_t* mask) {
+// The three largest of the union of two disjoint sets' (ties to the lower
+// position).
+__device__ __forceinline__ Top3 top3_merge(const Top3& a, const Top3& b) {
+  const bool af = a.m1 > b.m1 || (a.m1 == b.m1 && a.p1 < b.p1);  // a holds the largest
+  const float w1 = af ? a.m1 : b.m1, w2 = af ? a.m2 : b.m2, w3 = af ? a.m3 : b.m3;
+  const uint32_t wp1 = af ? a.p1 : b.p1, wp2 = af ? a.p2 : b.p2;
+  const float l1 = af ? b.m1 : a.m1, l2 = af ? b.m2 : a.m2;
+  const uint32_t lp1 = af ? b.p1 : a.p1;
+  const bool w_second = w2 > l1 || (w2 == l1 && wp2 < lp1);
+  Top3 r;
+  r.m1 = w1;
+  r.p1 = wp1;
+  r.m2 = w_second ? w2 : l1;
+  r.p2 = w_second ? wp2 : lp1;
+  r.m3 = w_second ? fmaxf(w3, l1) : fmaxf(w2, l2);
+  return r;
+}
+
+// 1. Mask bytes and tile words.  grid = (ceil(N / kScanSlice), B), block =
+// kScanThreads; thread t covers the 16 chunks of part g = blockIdx.x 256 + t,
+// and the 2^s threads of a tile (adjacent lanes) merge their parts.
+__global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(const float* __restrict__ scores, int64_t N,
+                                                                 const int32_t* __restrict__ valid_n, int32_t top_k,
+                                                                 uint2* __restrict__ tile_info,
+                                                                 uint8_t* __restrict__ mask) {
   const int b = blockIdx.y;
   const int64_t vn = row_valid(valid_n, b, N);
+  const int64_t g = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
+  const int64_t n0 = g * kSub;
   const float* row = scores + (size_t)b * N;
   uint8_t* mrow = mask + (size_t)b * N;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += stride)
-    mrow[n] = (n < vn && row[n] > threshold) ? 1 : 0;
+  const bool keep_all = (int64_t)top_k >= vn;  // also vn = 0
+  // Rows the finish selects in (uniform over the block): the tile words.
+  if (!keep_all && top_k > 0 && (int64_t)blockIdx.x * kScanSlice < vn) {
+    const int s = tile_shift(vn, top_k);
+    const uint32_t p0 = (uint32_t)(g & ((1 << s) - 1)) * kSub;  // the part's first position in its tile
+    Top3 a = {-INFINITY, -INFINITY, -INFINITY, p0, p0};     // parts past vn hold -inf
+    if (n0 + kSub <= vn && ((((uintptr_t)(row + n0)) & 15) == 0)) {
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(row + n0 + 4 * q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        top3_take(a, v[q].x, p0 + 4 * q);
+        top3_take(a, v[q].y, p0 + 4 * q + 1);
+        top3_take(a, v[q].z, p0 + 4 * q + 2);
+        top3_take(a, v[q].w, p0 + 4 * q + 3);
+      }
+    } else {
+      for (int j = 0; j < kSub && n0 + j < vn; ++j) top3_take(a, row[n0 + j], p0 + j);
+    }
+    for (int i = 0; i < s; ++i) {
+      Top3 o;
+      o.m1 = __shfl_xor(a.m1, 1 << i);
+      o.m2 = __shfl_xor(a.m2, 1 << i);
+      o.m3 = __shfl_xor(a.m3, 1 << i);
+      o.p1 = (uint32_t)__shfl_xor((int)a.p1, 1 << i);
+      o.p2 = (uint32_t)__shfl_xor((int)a.p2, 1 << i);
+      a = top3_merge(a, o);
+    }
+    const int64_t tile = g >> s;
+    if (p0 == 0 && (tile << (4 + s)) < vn)
+      tile_info[(size_t)b * tile_info_stride(N) + tile] =
+          make_uint2((uint32_t)score_bin(a.m1) | (a.p1 << 11) | ((uint32_t)score_bin(a.m2) << 17),
+                     a.p2 | ((uint32_t)score_bin(a.m3) << 6));
+  }
+  if (n0 >= N) return;
+  const uint8_t keep = keep_all ? 1 : 0;
+  if (n0 + kSub <= N && ((((uintptr_t)(mrow + n0)) & 15) == 0) && (!keep_all || n0 + kSub <= vn)) {
+    const uint32_t wv = keep * 0x01010101u;
+    *(uint4*)(mrow + n0) = make_uint4(wv, wv, wv, wv);
+  } else {
+    for (int j = 0; j < kSub && n0 + j < N; ++j) mrow[n0 + j] = n0 + j < vn ? keep : 0;
+  }
 }
 
-// Top-K finished from the score pass's histograms and tile maxima (the
-// selection folded into fm_score_topk).  grid = B, block = 1024.  Per row:
-//   1. the row's histogram: the global one (rows a block reached past its
-//      two slots) plus slot 0 of every block whose first row is this row and
-//      slot 1 of every block whose first row is the one before;
-//   2. the bin c holding the K-th largest score, the count A above it and
-//      its own count n_c (K <= A + n_c);
-//   3. the tiles whose largest score falls in bin c or above (at most
-//      A + n_c of them);
-//   4. their chunks: above bin c the mask byte is set (every such chunk is
-//      among the top K), in bin c the (key, index) pair becomes a candidate;
-//   5. the K - A candidates kept: all of them, or an exact radix selection
-//      (key descending, index ascending).
-// When the tiles or the candidates overflow LDS (many equal or nearly equal
-// scores), the row is selected exactly from all its scores instead.  The
-// result is the mask fm_select_topk gives for the same scores.
-constexpr int kFinishThreads = 1024;
-constexpr int kFinishTiles = 2048;      // qualifying tiles held in LDS
-constexpr int kFinishCand = 4096;       // candidates of bin c held in LDS
-constexpr int kFinishBatch = 16;        // loads issued together
-
-__device__ __forceinline__ int fused_bin(float e) {
-  const int b = (int)(e * (float)kHistBins);
-  return b < kHistBins - 1 ? b : kHistBins - 1;
+// Exclusive block-wide prefix sum of v; *total receives the sum.  Ends with
+// a barrier, so s_wtot may be reused right after.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wtot, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_prefix_sum(v);
+  if (lane == 63) s_wtot[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFinishThreads / 64; ++w) {
+    const uint32_t x = s_wtot[w];
+    before += w < wave ? x : 0u;
+    all += x;
+  }
+  *total = all;
+  __syncthreads();
+  return before + incl - v;
 }
 
-__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
-    const float* __restrict__ scores, int64_t N, const int32_t* __restrict__ valid_n, int32_t top_k,
-    const uint32_t* __restrict__ sel_hist, const int32_t* __restrict__ block_row0, int nblocks,
-    const uint32_t* __restrict__ hist_x, const float* __restrict__ tile_max, uint8_t* __restrict__ mask) {
+// 2. Exact top-K of each row.  grid = B, block = kFinishThreads.
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t N,
+                                                                     const int32_t* __restrict__ valid_n,
+                                                                     int32_t top_k,
+                                                                     const uint2* __restrict__ tile_info,
+                                                                     uint8_t* __restrict__ mask) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
   const int64_t vn = row_valid(valid_n, b, N);
+  if (top_k == 0 || (int64_t)top_k >= vn) return;  // the scan wrote the whole mask
   uint8_t* mrow = mask + (size_t)b * N;
   const float* row = scores + (size_t)b * N;
-  if (top_k == 0 || vn == 0) return;  // the score pass wrote zeros
-  if ((int64_t)top_k >= vn) {
-    for (int64_t n = t; n < vn; n += kFinishThreads) mrow[n] = 1;
-    return;
-  }
+  const uint32_t K = (uint32_t)top_k;
+  const uint32_t vn32 = (uint32_t)vn;  // below 2^26
   __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
-  __shared__ uint32_t s_q[kFinishTiles];
+  __shared__ uint32_t s_e[kFinishList];
+  __shared__ uint32_t s_f[kFinishFull];
   __shared__ uint2 s_c[kFinishCand];
+  __shared__ uint2 s_r[kFinishThreads];
   __shared__ uint32_t s_wtot[kFinishThreads / 64];
+  __shared__ uint32_t s_mm[2 * (kFinishThreads / 64)];
   __shared__ uint32_t s_out[3];
-  __shared__ unsigned long long s_bm[2][kFinishThreads / 64];
-  __shared__ uint32_t s_blk[kMaxScoreBlocks];  // a block matches at most one of the two slots
-  __shared__ uint32_t s_nblk, s_nq, s_nc;
 
-  // 1. Histogram slots of this row.
-  {
-    bool h0 = false, h1 = false;
-    if (t < nblocks) {
-      const int r0 = block_row0[t];
-      h0 = r0 == b;
-      h1 = r0 >= 0 && r0 == b - 1;
-    }
-    const unsigned long long m0 = __ballot(h0), m1 = __ballot(h1);
-    if (lane == 0) {
-      s_bm[0][wave] = m0;
-      s_bm[1][wave] = m1;
-    }
-    __syncthreads();
-    if (t == 0) {
-      uint32_t n = 0;
-      for (int slot = 0; slot < 2; ++slot)
-        for (int w = 0; w < kFinishThreads / 64; ++w)
-          for (unsigned long long m = s_bm[slot][w]; m; m &= m - 1)
-            s_blk[n++] = (uint32_t)(2 * (w * 64 + __builtin_ctzll(m)) + slot);
-      s_nblk = n;
-      s_nq = 0;
-      s_nc = 0;
-    }
-    __syncthreads();
-    uint2 c = *(const uint2*)(hist_x + (size_t)b * kHistBins + 2 * t);
-    const uint32_t nblk = s_nblk;
-    for (uint32_t base = 0; base < nblk; base += kFinishBatch) {
-      uint2 x[kFinishBatch];
+  // Tile words: thread t holds tiles 512 (j / 2) + 2 t + j % 2 (16-byte
+  // loads through a descriptor over the row's slot, a multiple of 16 bytes:
+  // zeros past it); their maxima are counted in the row's histogram.
+  const int s = tile_shift(vn, top_k);
+  const int lt = 4 + s;  // log2 of the tile's chunks
+  const uint32_t nt = (uint32_t)((vn + (1 << lt) - 1) >> lt);
+  const int64_t tstride = tile_info_stride(N);
+  const uint2* irow = tile_info + (size_t)b * tstride;
+  const __amdgpu_buffer_rsrc_t ir = buffer(irow, tstride * 8);
+  constexpr int kRegTiles = 2 * kFinishRegPairs;
+  uint2 info[kRegTiles];
 #pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j)
-        x[j] = base + j < nblk ? *(const uint2*)(sel_hist + (size_t)s_blk[base + j] * kHistBins + 2 * t)
-                               : make_uint2(0u, 0u);
-#pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j) {
-        c.x += x[j].x;
-        c.y += x[j].y;
-      }
-    }
-    *(uint2*)(h + 2 * t) = c;
+  for (int j = 0; j < kFinishRegPairs; ++j) {
+    const u32x4 v = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ir, 16u * (kFinishThreads * j + t), 0, 0));
+    info[2 * j] = make_uint2(v.x, v.y);
+    info[2 * j + 1] = make_uint2(v.z, v.w);
   }
+  auto tile_of = [&](int j) { return (uint32_t)(2 * kFinishThreads * (j >> 1) + 2 * t + (j & 1)); };
+  constexpr uint32_t kBlockTiles = (uint32_t)kRegTiles * kFinishThreads;
+  clear_bins<kFinishThreads>(h);
   __syncthreads();
-  // 2. The cut-off bin.
-  block_find<kFinishThreads>(h, (uint32_t)top_k, s_wtot, s_out, true);
-  const int cbin = (int)s_out[0];
-  const uint32_t above = s_out[1], n_c = s_out[2];
-  const uint32_t need = (uint32_t)top_k - above;
-  bool exact_row = n_c > (uint32_t)kFinishCand;
-  if (!exact_row) {
-    // 3. Qualifying tiles.
-    const int64_t nt = (vn + kTile16 - 1) / kTile16;
-    const float* trow = tile_max + (size_t)b * ((N + kTile16 - 1) / kTile16);
-    for (int64_t base = t; base < nt; base += (int64_t)kFinishThreads * kFinishBatch) {
-      float m[kFinishBatch];
 #pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j) {
-        const int64_t i = base + (int64_t)j * kFinishThreads;
-        m[j] = i < nt ? trow[i] : 0.f;
+  for (int j = 0; j < kRegTiles; ++j)
+    if (tile_of(j) < nt) atomicAdd(&h[tw_bin1(info[j])], 1u);
+  for (uint32_t i = kBlockTiles + t; i < nt; i += kFinishThreads) atomicAdd(&h[tw_bin1(irow[i])], 1u);
+  __syncthreads();
+  int c = 0;
+  if (K <= nt) {
+    block_find<kFinishThreads>(h, K, s_wtot, s_out, true);
+    c = (int)s_out[0];
+  }
+
+  // The listed chunks of each tile whose maximum is in bin c or above: its
+  // largest one or two (s_e), or, when its third largest is in bin c or
+  // above too, the whole tile (s_f).  Each thread first stages its tiles'
+  // entries in LDS (slot k of thread t at k 256 + t, in the space of s_c):
+  // (chunk, second chunk or kNone), or (tile | 2^31, kNone) for a whole
+  // tile.  One scan then places both lists (counts in the low and high 16
+  // bits).
+  uint2* s_stage = s_c;
+  uint32_t ne = 0, nf = 0;
+  {
+    uint32_t cnt = 0, nloc = 0;
+#pragma unroll
+    for (int j = 0; j < kRegTiles; ++j) {
+      const uint2 w = info[j];
+      const uint32_t tile = tile_of(j);
+      if (tile < nt && tw_bin1(w) >= c) {
+        const uint32_t first = tile << lt;
+        uint2 st;
+        if (tw_bin2(w) < c) {
+          st = make_uint2(first + tw_pos1(w), kNone);
+          cnt += 1u;
+        } else if (tw_bin3(w) < c) {
+          st = make_uint2(first + tw_pos1(w), first + tw_pos2(w));
+          cnt += 2u;
+        } else {
+          st = make_uint2(tile | 0x80000000u, kNone);
+          cnt += 0x10000u;
+        }
+        s_stage[nloc * kFinishThreads + t] = st;
+        ++nloc;
       }
-#pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j) {
-        const int64_t i = base + (int64_t)j * kFinishThreads;
-        if (i < nt && fused_bin(m[j]) >= cbin) {
-          const uint32_t pos = atomicAdd(&s_nq, 1u);
-          if (pos < (uint32_t)kFinishTiles) s_q[pos] = (uint32_t)i;
+    }
+    uint32_t tot;
+    const uint32_t pos = block_excl_scan(cnt, s_wtot, &tot);
+    ne = tot & 0xffffu;
+    nf = tot >> 16;
+    uint32_t pe = pos & 0xffffu, pf = pos >> 16;
+    for (uint32_t k = 0; k < nloc; ++k) {
+      const uint2 st = s_stage[k * kFinishThreads + t];
+      if (st.x & 0x80000000u) {
+        if (pf < (uint32_t)kFinishFull) s_f[pf] = st.x & 0x7fffffffu;
+        ++pf;
+      } else {
+        if (pe < (uint32_t)kFinishList) s_e[pe] = st.x;
+        ++pe;
+        if (st.y != kNone) {
+          if (pe < (uint32_t)kFinishList) s_e[pe] = st.y;
+          ++pe;
         }
       }
     }
-    __syncthreads();
-    const uint32_t nq = s_nq;
-    exact_row = nq > (uint32_t)kFinishTiles;
-    if (!exact_row) {
-      // 4. Their chunks.
-      const uint32_t total = nq * kTile16;
-      for (uint32_t base = t; base < total; base += kFinishThreads * kFinishBatch) {
-        float e[kFinishBatch];
-        int64_t n[kFinishBatch];
-#pragma unroll
-        for (int j = 0; j < kFinishBatch; ++j) {
-          const uint32_t x = base + j * kFinishThreads;
-          n[j] = x < total ? (int64_t)s_q[x / kTile16] * kTile16 + (x % kTile16) : vn;
-          e[j] = n[j] < vn ? row[n[j]] : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < kFinishBatch; ++j) {
-          if (n[j] < vn) {
-            const int bn = fused_bin(e[j]);
-            if (bn > cbin) {
-              mrow[n[j]] = 1;
-            } else if (bn == cbin) {
-              const uint32_t pos = atomicAdd(&s_nc, 1u);
-              if (pos < (uint32_t)kFinishCand) s_c[pos] = make_uint2(order_key(e[j]), (uint32_t)n[j]);
-            }
-          }
-        }
+  }
+  for (uint32_t base = kBlockTiles; base < nt; base += kFinishThreads) {  // rows of more than kBlockTiles tiles
+    const uint32_t i = base + t;
+    const uint2 w = i < nt ? irow[i] : make_uint2(0u, 0u);
+    const bool q = i < nt && tw_bin1(w) >= c;
+    const uint32_t cnt = q ? (tw_bin2(w) < c ? 1u : (tw_bin3(w) < c ? 2u : 0x10000u)) : 0u;
+    uint32_t tot;
+    const uint32_t pos = block_excl_scan(cnt, s_wtot, &tot);
+    const uint32_t pe = ne + (pos & 0xffffu), pf = nf + (pos >> 16);
+    if (q) {
+      const uint32_t first = i << lt;
+      if (cnt < 0x10000u) {
+        if (pe < (uint32_t)kFinishList) s_e[pe] = first + tw_pos1(w);
+        if (cnt == 2u && pe + 1 < (uint32_t)kFinishList) s_e[pe + 1] = first + tw_pos2(w);
+      } else if (pf < (uint32_t)kFinishFull) {
+        s_f[pf] = i;
       }
+    }
+    ne += tot & 0xffffu;
+    nf += tot >> 16;
+  }
+  __syncthreads();  // s_e, s_f complete
+
+  if (ne <= (uint32_t)kFinishList && nf <= (uint32_t)kFinishFull) {
+    // Listed entry x: s_e[x], then the chunks of the whole tiles in order.
+    const uint32_t total = ne + (nf << lt);
+    auto entry = [&](uint32_t x) -> uint32_t {
+      if (x < ne) return s_e[x];
+      const uint32_t y = x - ne;
+      return (s_f[y >> lt] << lt) + (y & ((1u << lt) - 1));
+    };
+    // The candidates: listed chunks in bin c or above, with their keys.  A
+    // descriptor over the row's valid scores gives 0 past them.
+    const __amdgpu_buffer_rsrc_t rr = buffer(row, vn * 4);
+    auto final_select = [&](auto each) {
+      // Bins of the keys between the smallest and the largest candidate:
+      // (key - kmin) >> sh < kSelBins.
+      const int lane = t & 63;
+      const int wave = t >> 6;
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+      each([&](uint2 e) {
+        kmin = e.x < kmin ? e.x : kmin;
+        kmax = e.x > kmax ? e.x : kmax;
+      });
+      kmin = wave_min_u32(kmin);
+      kmax = wave_max_u32(kmax);
+      if (lane == 0) {
+        s_mm[2 * wave] = kmin;
+        s_mm[2 * wave + 1] = kmax;
+      }
+      clear_bins<kFinishThreads>(h);
       __syncthreads();
-      // 5. The K - A kept of bin c.
-      const uint32_t nc = s_nc < (uint32_t)kFinishCand ? s_nc : (uint32_t)kFinishCand;
-      if (need >= nc) {
-        for (uint32_t i = t; i < nc; i += kFinishThreads) mrow[s_c[i].y] = 1;
+      kmin = 0xffffffffu;
+      kmax = 0u;
+#pragma unroll
+      for (int w = 0; w < kFinishThreads / 64; ++w) {
+        kmin = s_mm[2 * w] < kmin ? s_mm[2 * w] : kmin;
+        kmax = s_mm[2 * w + 1] > kmax ? s_mm[2 * w + 1] : kmax;
+      }
+      const uint32_t span = kmax - kmin;
+      const int width = span ? 32 - __builtin_clz(span) : 0;  // bits of the largest offset
+      const int sh = width > 11 ? width - 11 : 0;
+      each([&](uint2 e) { atomicAdd(&h[(e.x - kmin) >> sh], 1u); });
+      __syncthreads();
+      block_find<kFinishThreads>(h, K, s_wtot, s_out, true);
+      const uint32_t c2 = s_out[0];
+      const uint32_t need = K - s_out[1];  // of the candidates in bin c2
+      // Those above bin c2 are kept; those in it are listed in s_r.
+      uint32_t mine = 0;
+      each([&](uint2 e) { mine += ((e.x - kmin) >> sh) == c2 ? 1u : 0u; });
+      uint32_t in_c2;
+      uint32_t pos = block_excl_scan(mine, s_wtot, &in_c2);
+      each([&](uint2 e) {
+        const uint32_t bn = (e.x - kmin) >> sh;
+        if (bn > c2) mrow[e.y] = 1;
+        if (bn == c2) {
+          if (pos < (uint32_t)kFinishThreads) s_r[pos] = e;
+          ++pos;
+        }
+      });
+      __syncthreads();  // s_r complete
+      if (in_c2 <= (uint32_t)kFinishThreads) {
+        if ((uint32_t)t < in_c2) {
+          const uint2 me = s_r[t];
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < in_c2; ++j) {
+            const uint2 o = s_r[j];
+            rank += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+          }
+          if (rank < need) mrow[me.y] = 1;
+        }
       } else {
-        auto each = [&](auto f) {
-          for (uint32_t i = t; i < nc; i += kFinishThreads) f(s_c[i]);
+        auto in_bin = [&](auto f) {
+          each([&](uint2 e) {
+            if (((e.x - kmin) >> sh) == c2) f(e);
+          });
         };
         uint32_t T, last;
-        radix_select<kFinishThreads>(each, need, index_bits(vn), h, s_wtot, s_out, &T, &last);
-        each([&](uint2 e) {
+        radix_select<kFinishThreads>(in_bin, need, index_bits(vn), h, s_wtot, s_out, &T, &last);
+        in_bin([&](uint2 e) {
           if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
         });
       }
+    };
+    if (total <= (uint32_t)(kFinishThreads * kFinishRegEntries)) {
+      // Each thread holds its listed chunks in registers.
+      uint32_t n[kFinishRegEntries];
+      float e[kFinishRegEntries];
+#pragma unroll
+      for (int r = 0; r < kFinishRegEntries; ++r) {
+        const uint32_t x = t + r * kFinishThreads;
+        n[r] = x < total ? entry(x) : kNone;
+      }
+#pragma unroll
+      for (int r = 0; r < kFinishRegEntries; ++r)
+        e[r] = __builtin_bit_cast(float,
+                                  __builtin_amdgcn_raw_buffer_load_b32(rr, n[r] != kNone ? 4u * n[r] : kOutOfRange, 0, 0));
+      uint2 cand[kFinishRegEntries];
+      bool ok[kFinishRegEntries];
+#pragma unroll
+      for (int r = 0; r < kFinishRegEntries; ++r) {
+        ok[r] = n[r] < vn32 && bin_at_least(e[r], c);
+        cand[r] = make_uint2(order_key(e[r]), n[r]);
+      }
+      final_select([&](auto f) {
+#pragma unroll
+        for (int r = 0; r < kFinishRegEntries; ++r)
+          if (ok[r]) f(cand[r]);
+      });
+      return;
+    }
+    // More listed chunks: the candidates go to LDS first.
+    uint32_t nc = 0;
+    for (uint32_t base = 0; base < total; base += kFinishThreads * 4) {
+      uint32_t n[4];
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = base + t + r * kFinishThreads;
+        n[r] = x < total ? entry(x) : kNone;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        e[r] = __builtin_bit_cast(float,
+                                  __builtin_amdgcn_raw_buffer_load_b32(rr, n[r] != kNone ? 4u * n[r] : kOutOfRange, 0, 0));
+      uint32_t okb = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n[r] < vn32 && bin_at_least(e[r], c)) okb |= 1u << r;
+      uint32_t tot;
+      uint32_t pos = nc + block_excl_scan(__popc(okb), s_wtot, &tot);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (okb & (1u << r)) {
+          if (pos < (uint32_t)kFinishCand) s_c[pos] = make_uint2(order_key(e[r]), n[r]);
+          ++pos;
+        }
+      nc += tot;
+    }
+    __syncthreads();  // s_c complete
+    if (nc <= (uint32_t)kFinishCand) {
+      final_select([&](auto f) {
+        for (uint32_t i = t; i < nc; i += kFinishThreads) f(s_c[i]);
+      });
       return;
     }
   }
   // Too many equal or nearly equal scores for LDS: exact selection over the
-  // whole row (the mask bytes set in step 4 are all among the top K).
+  // whole row (nothing has been set yet).
   auto each = [&](auto f) {
     for (int64_t n = t; n < vn; n += kFinishThreads) f(make_uint2(order_key(row[n]), (uint32_t)n));
   };
   uint32_t T, last;
-  radix_select<kFinishThreads>(each, (uint32_t)top_k, index_bits(vn), h, s_wtot, s_out, &T, &last);
+  radix_select<kFinishThreads>(each, K, index_bits(vn), h, s_wtot, s_out, &T, &last);
   each([&](uint2 e) {
     if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
   });
 }
 
-}  // namespace
-
-hipError_t launch_topk_finish(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
-                              int32_t top_k, uint8_t* mask, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k,
-                     (const uint32_t*)ws.sel_hist, (const int32_t*)ws.block_row0, ws.score_blocks,
-                     (const uint32_t*)ws.sel_hist_x, (const float*)ws.tile_max, mask);
-  return hipGetLastError();
+// Threshold mask: 16 chunks per thread, one 16-byte store when the run is
+// whole and aligned.  grid = (ceil(N / kScanSlice), B), block = kScanThreads.
+__global__ __launch_bounds__(kScanThreads) void threshold_kernel(const float* __restrict__ scores, int64_t N,
+                                                                 const int32_t* __restrict__ valid_n,
+                                                                 float threshold, uint8_t* __restrict__ mask) {
+  const int b = blockIdx.y;
+  const int64_t vn = row_valid(valid_n, b, N);
+  const int64_t n0 = ((int64_t)blockIdx.x * kScanThreads + threadIdx.x) * kSub;
+  if (n0 >= N) return;
+  const float* row = scores + (size_t)b * N;
+  uint8_t* mrow = mask + (size_t)b * N;
+  if (n0 + kSub <= vn && ((((uintptr_t)(row + n0)) & 15) == 0) && ((((uintptr_t)(mrow + n0)) & 15) == 0)) {
+    float4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(row + n0 + 4 * q);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (v[q].x > threshold ? 1u : 0u) | (v[q].y > threshold ? 0x100u : 0u) |
+             (v[q].z > threshold ? 0x10000u : 0u) | (v[q].w > threshold ? 0x1000000u : 0u);
+    *(uint4*)(mrow + n0) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    for (int j = 0; j < kSub && n0 + j < N; ++j) mrow[n0 + j] = (n0 + j < vn && row[n0 + j] > threshold) ? 1 : 0;
+  }
 }
+
+}  // namespace
 
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream) {
-  const int blocks_per_row = (int)((N + kSelSlice - 1) / kSelSlice);
-  hipLaunchKernelGGL(sel_sample_kernel, dim3(B), dim3(kSampleThreads), 0, stream, scores, N, valid_n, top_k,
-                     ws.sel_state);
-  hipLaunchKernelGGL(sel_collect_kernel, dim3(blocks_per_row, B), dim3(kSelThreads), 0, stream, scores, N, valid_n,
-                     (const uint32_t*)ws.sel_state, (uint2*)ws.sel_cand, ws.sel_count, mask);
-  hipLaunchKernelGGL(sel_final_kernel, dim3(B), dim3(kFinThreads), 0, stream, scores, N, valid_n, blocks_per_row,
-                     top_k, (const uint32_t*)ws.sel_state, (const uint2*)ws.sel_cand, (const uint32_t*)ws.sel_count,
-                     mask);
+  const unsigned slices = (unsigned)((N + kScanSlice - 1) / kScanSlice);
+  hipLaunchKernelGGL(topk_scan_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, valid_n, top_k,
+                     ws.tile_info, mask);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k,
+                     (const uint2*)ws.tile_info, mask);
   return hipGetLastError();
 }
 
 hipError_t launch_select_threshold(const float* scores, int B, int64_t N, const int32_t* valid_n, float threshold,
                                    uint8_t* mask, hipStream_t stream) {
-  const int64_t per_block = 256 * 16;
-  const unsigned gx = (unsigned)((N + per_block - 1) / per_block);
-  hipLaunchKernelGGL(threshold_kernel, dim3(gx, B), dim3(256), 0, stream, scores, N, valid_n, threshold, mask);
+  const unsigned slices = (unsigned)((N + kScanSlice - 1) / kScanSlice);
+  hipLaunchKernelGGL(threshold_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, valid_n, threshold,
+                     mask);
   return hipGetLastError();
 }
 

@@ -64,8 +64,9 @@ __device__ __forceinline__ bool in_range(int32_t i, int64_t N) { return i >= 0 &
 // Keys of a list held in LDS, gathered beforehand by many blocks (the
 // gathers are random reads, which one block per row issues too slowly):
 // per row, kSubLdsRounds x 1024 keys then the validity bitmap (32 words per
-// round), in the top-K candidate workspace.
+// round), in the workspace's staging rows.
 constexpr size_t kSubPreRow = (size_t)kSubLdsRounds * kSubThreads + (size_t)kSubLdsRounds * 2 * kSubWaves;
+static_assert(kSubPreRow == kSubStageRowWords, "staging row size");
 
 // grid = (rounds, B), 256 threads: round r of row b, positions r 1024 + 256 u
 // + t (u = 0..3).  Writes each position's key and the round's bitmap words.
@@ -374,8 +375,8 @@ hipError_t launch_select_topk_subset(const Workspace& ws, const float* scores, i
                                      const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                      int32_t* out, int32_t* n_out, hipStream_t stream) {
   if (cap <= kSubLdsRounds * kSubThreads) {
-    uint32_t* pre = (uint32_t*)ws.sel_cand;
-    if (B > 0 && cap > 0 && (size_t)B * kSubPreRow * 4 <= ws.sel_cand_bytes) {
+    uint32_t* pre = ws.sub_stage;
+    if (B > 0 && cap > 0) {
       const dim3 grid((unsigned)((cap + kSubThreads - 1) / kSubThreads), (unsigned)B);
       hipLaunchKernelGGL(sub_gather_kernel, grid, dim3(256), 0, stream, scores, N, subset, n_subset, cap, pre);
       hipLaunchKernelGGL((sel_subset_kernel<true, true>), dim3(B), dim3(kSubThreads), kSubLdsBytes, stream, scores, N,

@@ -114,8 +114,8 @@ class FlashMemoryRetriever:
         return (scores, pl) if per_layer else scores
 
     def score_select(self, q, w, comp_k, valid_n=None, mode="max", top_k=None, threshold=None, per_layer=False):
-        """Scores and keep mask with the selection folded into the score pass
-        (fm_score_topk + fm_select_topk_finish, or fm_score_threshold).
+        """Scores and keep mask: fm_score + fm_select_topk, or
+        fm_score_threshold (the threshold mask written by the score pass).
         Exactly one of top_k and threshold.  Returns (scores, mask) or, with
         per_layer, (scores, mask, per_layer)."""
         if (top_k is None) == (threshold is None):
@@ -133,8 +133,8 @@ class FlashMemoryRetriever:
         mask = torch.empty((B, N), dtype=torch.bool, device=dev)
         pl = torch.empty((3, B, N), dtype=torch.float32, device=dev) if per_layer else None
         if top_k is not None:
-            _lib.fm_score_topk(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], int(top_k), scores, mask, pl)
-            _lib.fm_select_topk_finish(self._ctx, scores, B, N, valid_n, int(top_k), mask)
+            _lib.fm_score(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], scores, pl)
+            _lib.fm_select_topk(self._ctx, scores, B, N, valid_n, int(top_k), mask)
         else:
             _lib.fm_score_threshold(self._ctx, q, w, comp_k, B, N, valid_n, MODES[mode], float(threshold), scores,
                                     mask, pl)

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score",
-                                  "fm_score_topk", "fm_select_topk_finish", "fm_score_threshold", "fm_score_fp8",
+                                  "fm_score_threshold", "fm_score_fp8",
                                   "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold",
                                   "fm_mask_logits", "fm_resident_delta", "fm_last_error"])
 
@@ -55,8 +55,6 @@ def test_null_context_is_rejected_before_any_launch():
     assert "null context" in _lib.last_error()
     assert L.fm_score(None, None, None, None, 1, 1, None, 0, None, None, None) == _lib.FM_EINVAL
     assert L.fm_score_fp8(None, None, None, None, 1, 1, None, 0, None, None, None) == _lib.FM_EINVAL
-    assert L.fm_score_topk(None, None, None, None, 1, 1, None, 0, 1, None, None, None, None) == _lib.FM_EINVAL
-    assert L.fm_select_topk_finish(None, None, 1, 1, None, 1, None, None) == _lib.FM_EINVAL
     assert L.fm_score_threshold(None, None, None, None, 1, 1, None, 0, 0.5, None, None, None, None) == _lib.FM_EINVAL
     assert L.fm_select_topk(None, None, 1, 1, None, 1, None, None) == _lib.FM_EINVAL
     assert L.fm_select_threshold(None, None, 1, 1, None, 0.5, None, None) == _lib.FM_EINVAL

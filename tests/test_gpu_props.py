@@ -210,15 +210,14 @@ def test_threshold_strict_exact(retr, tau):
         assert np.array_equal(m[b].astype(np.uint8), oracle.select_threshold(s[b].astype(np.float64), int(vn[b]), tau))
 
 
-def test_topk_sample_miss_falls_back_to_whole_row(retr):
-    """The top-K cut-off comes from 64 sampled runs of 64 chunks spread over
-    the row; here the sampled chunks hold the largest scores and the rest are
-    low, so fewer than K chunks reach the cut-off and the selection must fall
-    back to the whole row.  The result is still the exact top-K."""
+def test_topk_top_scores_packed_in_few_tiles(retr):
+    """The top scores fill runs of consecutive 16-chunk tiles, so the K-th
+    largest tile maximum lies far below the K-th score: most of the row's
+    candidates come from low tiles, and the finish may overflow LDS and
+    select over the whole row.  The result is still the exact top-K."""
     n, k, run = 65536, 512, 64
-    s = np.full((2, n), 0.1, np.float32)
     rng = np.random.default_rng(21)
-    s[:, :] = rng.uniform(0.05, 0.2, (2, n)).astype(np.float32)
+    s = rng.uniform(0.05, 0.2, (2, n)).astype(np.float32)
     starts = [r * (n - run) // 63 for r in range(64)]
     vals = np.linspace(0.9, 0.99, 64 * run).astype(np.float32)
     i = 0
@@ -226,9 +225,79 @@ def test_topk_sample_miss_falls_back_to_whole_row(retr):
         s[0, st:st + run] = vals[i:i + run]
         i += run
     s[1] = s[0][::-1]                       # second row: a different layout, same values
-    m = host(retr.keep_topk(dev(s), k))
-    for b in range(2):
-        assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), n, k)), b
+    for kk in (k, 4096, 5000):
+        m = host(retr.keep_topk(dev(s), kk))
+        for b in range(2):
+            assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), n, kk)), (b, kk)
+
+
+def test_topk_many_candidates_in_the_last_bin(retr):
+    """3000 scattered chunks within one histogram bin (1/2048 wide) above a
+    low background, K = 1500: the candidates fit in LDS but more than 1024 of
+    them share the K-th score's bin, which is then split by radix passes."""
+    n = 65536
+    rng = np.random.default_rng(23)
+    s = rng.uniform(0.0, 0.5, (2, n)).astype(np.float32)
+    pos = rng.choice(n, 3000, replace=False)
+    s[0, pos] = (0.9 + rng.integers(0, 400, 3000) * 1e-7).astype(np.float32)   # ties too
+    s[1, pos] = np.float32(0.9)                                                # all equal
+    for k in (1, 1500, 2999, 3000, 3001):
+        m = host(retr.keep_topk(dev(s), k))
+        for b in range(2):
+            assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), n, k)), (b, k)
+
+
+def test_topk_many_short_rows(retr):
+    """64 rows of at most 40 chunks (one to three tiles), every K edge."""
+    rng = np.random.default_rng(24)
+    B, n = 64, 40
+    s = np.round(rng.uniform(0, 1, (B, n)), 2).astype(np.float32)
+    vn = rng.integers(0, n + 1, B).astype(np.int32)
+    for k in (0, 1, 2, 15, 16, 17, 39, 40):
+        m = host(retr.keep_topk(dev(s), k, dev(vn)))
+        for b in range(B):
+            assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), int(vn[b]), k))
+
+
+def test_topk_rows_beyond_the_register_tiles(weights_np):
+    """Rows of more than 16384 tiles (N > 262144): the tile maxima beyond the
+    registers are read again for the histogram and the compaction."""
+    import sparse_attention_chunk_amd as fm
+    r = fm.FlashMemoryRetriever(fm.weights_to_device(weights_np), max_batch=2, max_n=600000)
+    try:
+        rng = np.random.default_rng(25)
+        n = 600000
+        s = rng.uniform(0, 1, (2, n)).astype(np.float32)
+        s[1, 590000:] += 0.5                     # the top of row 1 sits past the register tiles
+        vn = np.array([n, 599999], np.int32)
+        for k in (512, 2048):
+            m = host(r.keep_topk(dev(s), k, dev(vn)))
+            for b in range(2):
+                assert np.array_equal(m[b].astype(np.uint8),
+                                      oracle.select_topk(s[b].astype(np.float64), int(vn[b]), k)), (b, k)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("n,k", [(5003, 17), (77, 5), (40000, 512), (3, 1)])
+def test_topk_and_threshold_write_every_byte(retr, n, k):
+    """Masks filled with ones beforehand: every byte of the [B][N] mask is
+    written (N odd, ragged rows, rows kept whole and empty)."""
+    from sparse_attention_chunk_amd import _lib as L
+    rng = np.random.default_rng(n)
+    B = 5
+    s = rng.uniform(0, 1, (B, n)).astype(np.float32)
+    vn = np.array([n, n - 1, min(k, n), 0, max(1, n // 3)], np.int32)
+    sd, vd = dev(s), dev(vn)
+    m = torch.ones((B, n), dtype=torch.bool, device="cuda")
+    L.fm_select_topk(retr.ctx, sd, B, n, vd, k, m)
+    mt = torch.ones((B, n), dtype=torch.bool, device="cuda")
+    L.fm_select_threshold(retr.ctx, sd, B, n, vd, 0.5, mt)
+    m, mt = host(m), host(mt)
+    for b in range(B):
+        assert np.array_equal(m[b].astype(np.uint8), oracle.select_topk(s[b].astype(np.float64), int(vn[b]), k)), b
+        assert np.array_equal(mt[b].astype(np.uint8), oracle.select_threshold(s[b].astype(np.float64), int(vn[b]),
+                                                                                0.5)), b
 
 
 def test_topk_large_candidate_lists(retr):
