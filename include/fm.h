@@ -180,6 +180,19 @@ fm_status fm_score_fp8(fm_ctx* ctx, const float* q, const float* w, const uint8_
 fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                          int32_t top_k, uint8_t* mask, void* stream);
 
+/* fm_select_topk without a context and without any allocation, for callers
+ * that cannot allocate (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus ctx), result
+ * and tie-breaking as fm_select_topk; its scratch (the scan's tile words,
+ * 8 bytes per 16 chunks of each row) is a static 8 MiB device array that
+ * each GPU holds until the process ends: B * 8 * (ceil(N / 16) rounded up
+ * to even) must not exceed 8 MiB (B = 30, N = 262144 needs 3.75 MiB), else
+ * FM_EINVAL.  B in [0, 65535], N in [0, 2^26].  Every call on a GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other
+ * threads) race; the first call on a device looks the array's address up. */
+fm_status fm_select_topk_static(const float* scores, int32_t B, int64_t N, const int32_t* valid_n, int32_t top_k,
+                                uint8_t* mask, void* stream);
+
 /* Per-step top-K confined to a subset of the chunks (model card "How it
  * works", Level 2: the Lightning Indexer's top-512 runs only over the
  * resident_set that the Memory Indexer recalled).  The pages define the

@@ -35,7 +35,7 @@ STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUN
 
 # Exported symbols, in header order.
 EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_threshold",
-           "fm_score_fp8", "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta",
+           "fm_score_fp8", "fm_select_topk", "fm_select_topk_static", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta",
            "fm_mask_logits", "fm_last_error")
 
 
@@ -92,6 +92,8 @@ def _load() -> ctypes.CDLL:
     lib.fm_score_fp8.restype = ctypes.c_int
     lib.fm_select_topk.argtypes = [vp, vp, i32, i64, vp, i32, vp, vp]
     lib.fm_select_topk.restype = ctypes.c_int
+    lib.fm_select_topk_static.argtypes = [vp, i32, i64, vp, i32, vp, vp]
+    lib.fm_select_topk_static.restype = ctypes.c_int
     lib.fm_select_topk_subset.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, vp, vp, vp]
     lib.fm_select_topk_subset.restype = ctypes.c_int
     lib.fm_select_threshold.argtypes = [vp, vp, i32, i64, vp, ctypes.c_float, vp, vp]
@@ -169,6 +171,11 @@ def fm_score_fp8(ctx, q, w, comp_k, B, N, valid_n, mode, scores, per_layer=None,
 def fm_select_topk(ctx, scores, B, N, valid_n, top_k, mask, stream=None) -> None:
     s = current_stream() if stream is None else stream
     check(LIB.fm_select_topk(ctx, ptr(scores), B, N, ptr(valid_n), top_k, ptr(mask), s), "fm_select_topk")
+
+
+def fm_select_topk_static(scores, B, N, valid_n, top_k, mask, stream=None) -> None:
+    s = current_stream() if stream is None else stream
+    check(LIB.fm_select_topk_static(ptr(scores), B, N, ptr(valid_n), top_k, ptr(mask), s), "fm_select_topk_static")
 
 
 def fm_select_topk_subset(ctx, scores, B, N, subset, n_subset, cap, top_k, out, n_out, stream=None) -> None:

@@ -5,23 +5,25 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <string>
+#include <mutex>
 
 #include "fm_internal.h"
 
 namespace {
 
-thread_local std::string g_err;
+// The calling thread's last error message (a fixed buffer: no call
+// allocates, on any path).
+thread_local char g_err[512];
 
 fm_status fail(fm_status st, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
-  g_err = buf;
   return st;
 }
+
+void clear_err() { g_err[0] = 0; }
 
 fm_status hip_fail(hipError_t e, const char* what) {
   return fail(FM_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -83,6 +85,36 @@ fm_status check_shape(const fm_ctx* ctx, int32_t B, int64_t N, bool with_n) {
 
 }  // namespace
 
+// Device scratch of fm_select_topk_static, for callers that cannot allocate:
+// the top-K scan's tile words.  Every GPU the library runs on holds its own
+// copy until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress gives on that device (the array's name is a
+// host-side stand-in, not a device address).
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device `dev`, looked up on
+// the first call there and kept.
+hipError_t static_scratch(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 void fm_config_default(fm_config* cfg) {
@@ -101,11 +133,11 @@ void fm_config_default(fm_config* cfg) {
   cfg->yarn_beta_slow = 1.0;
 }
 
-const char* fm_last_error(void) { return g_err.c_str(); }
+const char* fm_last_error(void) { return g_err; }
 
 fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max_batch, int64_t max_n,
                     fm_ctx** out) {
-  g_err.clear();
+  clear_err();
   if (!cfg || !weights || !out) return fail(FM_EINVAL, "null argument to fm_create");
   *out = nullptr;
   using namespace fm;
@@ -228,7 +260,7 @@ void fm_destroy(fm_ctx* ctx) {
 
 fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* positions, int32_t B, float* q_out,
                            float* w_out, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, 0, false)) != FM_OK) return st;
@@ -245,7 +277,7 @@ fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* posi
 static fm_status score_common(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
                               const int32_t* valid_n, fm_ensemble mode, float* scores, float* per_layer, void* stream,
                               bool fp8) {
-  g_err.clear();
+  clear_err();
   const char* name = fp8 ? "fm_score_fp8" : "fm_score";
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
@@ -277,7 +309,7 @@ fm_status fm_score_fp8(fm_ctx* ctx, const float* q, const float* w, const uint8_
 fm_status fm_score_threshold(fm_ctx* ctx, const float* q, const float* w, const uint8_t* comp_k, int32_t B, int64_t N,
                              const int32_t* valid_n, fm_ensemble mode, float threshold, float* scores, uint8_t* mask,
                              float* per_layer, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
@@ -296,7 +328,7 @@ fm_status fm_score_threshold(fm_ctx* ctx, const float* q, const float* w, const 
 
 fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                          int32_t top_k, uint8_t* mask, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
@@ -310,10 +342,37 @@ fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N,
   return FM_OK;
 }
 
+fm_status fm_select_topk_static(const float* scores, int32_t B, int64_t N, const int32_t* valid_n, int32_t top_k,
+                                uint8_t* mask, void* stream) {
+  clear_err();
+  if (B < 0 || B > 65535) return fail(FM_EINVAL, "B = %d outside [0, 65535]", B);
+  if (N < 0 || N > (int64_t(1) << 26)) return fail(FM_EINVAL, "N = %lld outside [0, 2^26]", (long long)N);
+  if (top_k < 0) return fail(FM_EINVAL, "top_k = %d < 0", top_k);
+  const size_t need = sizeof(uint2) * (size_t)B * (size_t)fm::tile_info_stride(N);
+  if (need > kStaticScratchBytes)
+    return fail(FM_EINVAL, "B = %d, N = %lld need %zu scratch bytes; the static scratch holds %zu", B, (long long)N,
+                need, kStaticScratchBytes);
+  if (B == 0 || N == 0) return FM_OK;
+  if (!scores || !mask) return fail(FM_EINVAL, "null pointer to fm_select_topk_static");
+  if (!aligned(scores, 4) || (valid_n && !aligned(valid_n, 4)))
+    return fail(FM_EINVAL, "scores and valid_n must be 4-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FM_EINVAL, "device %d beyond the %d supported", dev, kMaxDevices);
+  void* p = nullptr;
+  if ((e = static_scratch(dev, &p)) != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  fm::Workspace ws;
+  ws.tile_info = (uint2*)p;
+  e = fm::launch_select_topk(ws, scores, B, N, valid_n, top_k, mask, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fm_select_topk_static launch");
+  return FM_OK;
+}
+
 fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* subset,
                                 const int32_t* n_subset, int32_t cap, int32_t top_k, int32_t* out, int32_t* n_out,
                                 void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
@@ -331,7 +390,7 @@ fm_status fm_select_topk_subset(fm_ctx* ctx, const float* scores, int32_t B, int
 
 fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                               float threshold, uint8_t* mask, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
@@ -347,7 +406,7 @@ fm_status fm_select_threshold(fm_ctx* ctx, const float* scores, int32_t B, int64
 
 fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, int32_t R, int64_t N,
                          const uint8_t* mask, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;
@@ -364,7 +423,7 @@ fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, i
 fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t* mask, int32_t B, int64_t N,
                             int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
                             int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, void* stream) {
-  g_err.clear();
+  clear_err();
   fm_status st = check_ctx(ctx);
   if (st != FM_OK) return st;
   if ((st = check_shape(ctx, B, N, true)) != FM_OK) return st;

@@ -21,7 +21,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score",
                                   "fm_score_threshold", "fm_score_fp8",
-                                  "fm_select_topk", "fm_select_topk_subset", "fm_select_threshold",
+                                  "fm_select_topk", "fm_select_topk_static", "fm_select_topk_subset",
+                                  "fm_select_threshold",
                                   "fm_mask_logits", "fm_resident_delta", "fm_last_error"])
 
 
@@ -61,6 +62,21 @@ def test_null_context_is_rejected_before_any_launch():
     assert L.fm_select_topk_subset(None, None, 1, 1, None, None, 1, 1, None, None, None) == _lib.FM_EINVAL
     assert L.fm_mask_logits(None, None, 0, 1, 1, 1, None, None) == _lib.FM_EINVAL
     L.fm_destroy(None)  # no-op
+
+
+def test_static_topk_rejects_sizes_beyond_its_scratch_before_touching_the_device():
+    from sparse_attention_chunk_amd import _lib
+    L = _lib.LIB
+    assert L.fm_select_topk_static(None, 70000, 16, None, 1, None, None) == _lib.FM_EINVAL
+    assert "65535" in _lib.last_error()
+    assert L.fm_select_topk_static(None, 1, (1 << 26) + 1, None, 1, None, None) == _lib.FM_EINVAL
+    # 8 bytes per 16 chunks (rounded up to an even count) of each row: B = 64, N = 262144 needs 8 MiB exactly
+    assert L.fm_select_topk_static(None, 65, 262144, None, 512, None, None) == _lib.FM_EINVAL
+    assert "static scratch" in _lib.last_error()
+    assert L.fm_select_topk_static(None, 64, 262144, None, 512, None, None) == _lib.FM_EINVAL
+    assert "null pointer" in _lib.last_error()
+    assert L.fm_select_topk_static(None, 1, 16, None, -1, None, None) == _lib.FM_EINVAL
+    assert L.fm_select_topk_static(None, 0, 16, None, 1, None, None) == _lib.FM_OK
 
 
 def test_create_rejects_bad_config_before_touching_the_device():
