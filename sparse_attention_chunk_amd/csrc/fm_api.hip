@@ -178,7 +178,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
     p1_rows = std::max(p1_rows, (size_t)proj1_splits(b) * b);
   }
   enum {
-    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHat, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
+    kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHatHi, kAHatLo, kAHatInv, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
     kSubStage, kResCount, kTileInfo, kNumBuffers
   };
   size_t sizes[kNumBuffers];
@@ -188,7 +188,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kW2Inv] = sizeof(float) * kLayers * kHeads * kHeadDim;
   sizes[kGain] = sizeof(float) * kLayers * kQLora;
   sizes[kPart1] = sizeof(float) * kLayers * p1_rows * kProj1Out;
-  sizes[kAHat] = sizeof(float) * kLayers * mb * kQLora;
+  sizes[kAHatHi] = sizeof(_Float16) * kLayers * mb * kQLora;
+  sizes[kAHatLo] = sizeof(_Float16) * kLayers * mb * kQLora;
+  sizes[kAHatInv] = sizeof(float) * kLayers * mb * (kQLora / 128);
   sizes[kFreq] = sizeof(double) * (kRopeDim / 2);
   sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
   sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
@@ -224,7 +226,9 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.w2_inv = (float*)(p + offs[kW2Inv]);
   ctx->ws.q_norm = (float*)(p + offs[kGain]);
   ctx->ws.proj1_part = (float*)(p + offs[kPart1]);
-  ctx->ws.a_hat = (float*)(p + offs[kAHat]);
+  ctx->ws.ahat_hi = (_Float16*)(p + offs[kAHatHi]);
+  ctx->ws.ahat_lo = (_Float16*)(p + offs[kAHatLo]);
+  ctx->ws.ahat_inv = (float*)(p + offs[kAHatInv]);
   ctx->ws.rope_freq = (double*)(p + offs[kFreq]);
   ctx->ws.rope_cs = (float*)(p + offs[kCosSin]);
   ctx->ws.qpack = (void*)(p + offs[kQPack]);

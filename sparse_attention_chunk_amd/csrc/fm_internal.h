@@ -80,7 +80,9 @@ struct Workspace {
   float* w2_inv = nullptr;       // [3][kHeads * kHeadDim]
   float* q_norm = nullptr;       // [3][kQLora] RMSNorm gains
   float* proj1_part = nullptr;   // [proj1_splits(B)][3][B][kProj1Out]
-  float* a_hat = nullptr;        // [3][max_batch][kQLora]
+  _Float16* ahat_hi = nullptr;   // [3][max_batch][kQLora]: RMSNorm output, each 128-chunk of a row scaled by a
+  _Float16* ahat_lo = nullptr;   //   power of two and split into f16 hi + lo parts (wq_b's operand)
+  float* ahat_inv = nullptr;     // [3][max_batch][kQLora / 128]: 2^-e of each chunk
   double* rope_freq = nullptr;   // [kRopeDim / 2]
   float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16

@@ -378,7 +378,8 @@ __device__ inline void rope_cos_sin(int64_t pos, double freq, float* out2) {
 template <int S>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* part, GainPtrs gains, int B, float eps,
                                                       float w_scale, const int64_t* positions, const double* freq,
-                                                      float* rope_cs, float* a_hat, float* w_out) {
+                                                      float* rope_cs, _Float16* ahat_hi, _Float16* ahat_lo,
+                                                      float* ahat_inv, float* w_out) {
   const int layer = blockIdx.x / B;
   const int b = blockIdx.x % B;
   const int t = threadIdx.x;
@@ -408,9 +409,27 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* part, GainPtr
   ss = (red[0] + red[1]) + (red[2] + red[3]);
   const float rs = 1.0f / sqrtf(ss * (1.0f / kQLora) + eps);
   const float* gain = gains.g[layer];
-  float* dst = a_hat + ((size_t)layer * B + b) * kQLora;
   const f32x4 gv = {gain[4 * t], gain[4 * t + 1], gain[4 * t + 2], gain[4 * t + 3]};
-  *(f32x4*)(dst + 4 * t) = a * rs * gv;
+  {
+    // a_hat as wq_b's operand: each 128-chunk (32 lanes) scaled by the power
+    // of two that puts its largest entry in [2^14, 2^15), split into f16
+    // hi + lo, and the chunk's 2^-e.
+    const f32x4 v = a * rs * gv;
+    const float m = max32(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    const int e = split_exponent(m);
+    const float sc = ldexpf(1.f, e);
+    f16x4 h, l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float y = v[q] * sc;
+      h[q] = (_Float16)y;
+      l[q] = (_Float16)(y - (float)h[q]);
+    }
+    const size_t o = ((size_t)layer * B + b) * kQLora + 4 * t;
+    *(f16x4*)(ahat_hi + o) = h;
+    *(f16x4*)(ahat_lo + o) = l;
+    if ((t & 31) == 0) ahat_inv[((size_t)layer * B + b) * (kQLora / kKChunk) + (t >> 5)] = ldexpf(1.f, -e);
+  }
   if (t < kHeads) {
     float wv = wpart[0];
 #pragma unroll
@@ -422,12 +441,45 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* part, GainPtr
   }
 }
 
+// The value of lane l ^ M, for M = 1, 2, 4, 8, 16, 32: DPP lane moves in
+// the vector ALU (quad permutes; row shifts by M from either side within
+// each row of 16 lanes) and the gfx950 row swaps (permlane16/32_swap
+// exchange the odd 16-lane rows of the first operand with the even rows of
+// the second, or the wave's halves).
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  if constexpr (M == 1) {
+    return dpp_move<0xb1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return dpp_move<0x4e>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4 || M == 8) {
+    const float up = dpp_move<0x100 + M>(v);    // row_shl:M, lane l receives lane l + M
+    const float down = dpp_move<0x110 + M>(v);  // row_shr:M, lane l receives lane l - M
+    return (lane & M) ? down : up;
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void butterfly(float& a0, float& a1, int lane) {
+  const float p0 = xor_lane<M>(a0, lane);
+  const float p1 = xor_lane<M>(a1, lane);
+  const bool upper = lane & M;
+  a0 = upper ? p0 - a0 : a0 + p0;
+  a1 = upper ? p1 - a1 : a1 + p1;
+}
+
 // RoPE and the normalized Hadamard transform of one head's 128 dims, held
 // by a wave as dims 2l and 2l+1 in lane l (x, y).  RoPE: lanes 32..63 hold
 // the rotated dims 64..127; pair j = l - 32 is turned counter-clockwise by
 // pos * freq[j] (cosine and sine from the RMSNorm kernel), the rotation in
-// fp32.  Then the 128-point Walsh-Hadamard butterfly in Sylvester order,
-// scaled by 128^-0.5.
+// fp32.  Then the 128-point Walsh-Hadamard butterfly in Sylvester order
+// (dims 2l, 2l+1 within the lane, then the lane bits), scaled by 128^-0.5.
 __device__ __forceinline__ float2 rope_hadamard(float x, float y, const float* cs_row, int lane) {
   if (lane >= 32) {
     const float2 c = *(const float2*)(cs_row + 2 * (lane - 32));
@@ -438,18 +490,12 @@ __device__ __forceinline__ float2 rope_hadamard(float x, float y, const float* c
   }
   float a0 = x + y;
   float a1 = x - y;
-#pragma unroll
-  for (int m = 1; m <= 32; m <<= 1) {
-    const float p0 = __shfl_xor(a0, m, 64);
-    const float p1 = __shfl_xor(a1, m, 64);
-    if (lane & m) {
-      a0 = p0 - a0;
-      a1 = p1 - a1;
-    } else {
-      a0 = a0 + p0;
-      a1 = a1 + p1;
-    }
-  }
+  butterfly<1>(a0, a1, lane);
+  butterfly<2>(a0, a1, lane);
+  butterfly<4>(a0, a1, lane);
+  butterfly<8>(a0, a1, lane);
+  butterfly<16>(a0, a1, lane);
+  butterfly<32>(a0, a1, lane);
   const float inv_sqrt = 0.08838834764831845f;  // 128^-0.5
   return make_float2(a0 * inv_sqrt, a1 * inv_sqrt);
 }
@@ -473,7 +519,9 @@ static_assert(2 * kProjRowsPerWave * kHeadDim * 4 <= kHeadProjLds, "slice sums f
 struct HeadProjArgs {
   const _Float16* w[kLayers];  // packed wq_b of each layer
   const float* winv[kLayers];  // [kHeads * kHeadDim]: 2^-e of each row
-  const float* a_hat;          // [3][B][kQLora]
+  const _Float16* ahat_hi;     // [3][B][kQLora], split a_hat (hi, lo parts)
+  const _Float16* ahat_lo;
+  const float* ahat_inv;       // [3][B][kQLora / 128]
   const float* rope_cs;        // [B][kRopeDim / 2][2]
   float* q_out;                // [3][B][kHeads][kHeadDim]
   int B;
@@ -509,8 +557,6 @@ __global__ __launch_bounds__(kHeadThreads, 1) void head_proj_kernel(HeadProjArgs
       const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
       pl[tt].w = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, 0, (int)(tile_halves * 2), kBufferWord3);
-      pl[tt].x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_hat + (size_t)layer * p.B * kQLora), 0,
-                                                   p.B * kQLora * 4, kBufferWord3);
       pl[tt].K = kQLora;
       pl[tt].b_base = b_base;
     }
@@ -521,11 +567,37 @@ __global__ __launch_bounds__(kHeadThreads, 1) void head_proj_kernel(HeadProjArgs
   for (int q = 0; q < kHeadRing - 1; ++q)
     proj_load_w(pl[q / kSliceChunks], k_begin + (q % kSliceChunks) * kKChunk, wbuf[q]);
   {
-    f32x4 xr[kSliceChunks][kStage];
+    // The half's slice of the split a_hat rows b_base .. b_base + 31 (zeros
+    // past B) copied to LDS: thread u of the half moves 16-byte vectors
+    // u + 256 j of each part, vector v = row 64 ... column 8 (v % 64).
+    const int u = threadIdx.x & 255;
+    const size_t lo_row = (size_t)layer * p.B;
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.ahat_hi + lo_row * kQLora), 0, p.B * kQLora * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.ahat_lo + lo_row * kQLora), 0, p.B * kQLora * 2, kBufferWord3);
+    constexpr int kVec = kProjRowsPerWave * kSliceK / 8 / 256;  // 16-byte vectors per thread and part
+    f16x8 vh[kVec], vl[kVec];
 #pragma unroll
-    for (int c = 0; c < kSliceChunks; ++c) proj_load_x(pl[0], k_begin + c * kKChunk, xr[c]);
+    for (int j = 0; j < kVec; ++j) {
+      const int v = u + 256 * j;
+      const uint32_t off = 2u * ((uint32_t)(b_base + v / 64) * kQLora + k_begin + 8 * (v % 64));
+      vh[j] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+      vl[j] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+    }
+    float inv = 0.f;
+    if (u < kSliceChunks * kProjRowsPerWave) {  // xs_inv[c][row], c = u / 32
+      const int row = u % kProjRowsPerWave, c = u / kProjRowsPerWave;
+      const int b = b_base + row;
+      inv = b < p.B ? p.ahat_inv[(lo_row + b) * (kQLora / kKChunk) + k_begin / kKChunk + c] : 0.f;
+    }
 #pragma unroll
-    for (int c = 0; c < kSliceChunks; ++c) proj_store_x(xr[c], c, xs_hi, xs_lo, xs_inv);
+    for (int j = 0; j < kVec; ++j) {
+      const int v = u + 256 * j;
+      *(f16x8*)(xs_hi + (v / 64) * kXsStride + 8 * (v % 64)) = vh[j];
+      *(f16x8*)(xs_lo + (v / 64) * kXsStride + 8 * (v % 64)) = vl[j];
+    }
+    if (u < kSliceChunks * kProjRowsPerWave) xs_inv[u] = inv;
   }
   lds_barrier();
 
@@ -612,7 +684,7 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
     const float w_scale = (float)(1.0 / std::sqrt((double)cfg.head_dim * (double)cfg.n_heads));
     auto kern = rmsnorm_kernel<kHidden / kSliceK>;
     hipLaunchKernelGGL(kern, dim3(kLayers * B), dim3(256), 0, stream, ws.proj1_part, gp, B, cfg.rms_eps, w_scale,
-                       positions, ws.rope_freq, ws.rope_cs, ws.a_hat, w_out);
+                       positions, ws.rope_freq, ws.rope_cs, ws.ahat_hi, ws.ahat_lo, ws.ahat_inv, w_out);
   }
   // wq_b, RoPE (YaRN) and the normalized Hadamard transform, per head.
   {
@@ -621,7 +693,9 @@ hipError_t launch_prepare_query(const fm_config& cfg, const fm_weights& wts, con
       p.w[l] = ws.w2 + (size_t)l * kHeads * kHeadDim * kQLora * 2;
       p.winv[l] = ws.w2_inv + (size_t)l * kHeads * kHeadDim;
     }
-    p.a_hat = ws.a_hat;
+    p.ahat_hi = ws.ahat_hi;
+    p.ahat_lo = ws.ahat_lo;
+    p.ahat_inv = ws.ahat_inv;
     p.rope_cs = ws.rope_cs;
     p.q_out = q_out;
     p.B = B;
