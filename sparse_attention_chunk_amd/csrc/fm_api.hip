@@ -179,7 +179,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   }
   enum {
     kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHatHi, kAHatLo, kAHatInv, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
-    kSubStage, kResCount, kTileInfo, kNumBuffers
+    kSubStage, kResCount, kResBits, kTileInfo, kNumBuffers
   };
   size_t sizes[kNumBuffers];
   sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
@@ -200,6 +200,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
   sizes[kSubStage] = sizeof(uint32_t) * mb * kSubStageRowWords;
   sizes[kResCount] = 3 * sizeof(uint32_t) * mb * (size_t)((max_n + kResSlice - 1) / kResSlice);
+  sizes[kResBits] = sizeof(unsigned long long) * mb * (size_t)((max_n + kResSlice - 1) / kResSlice) * (kResSlice / 16);
   sizes[kTileInfo] = sizeof(uint2) * mb * (size_t)fm::tile_info_stride(max_n);
   size_t offs[kNumBuffers];
   size_t total = 0;
@@ -239,6 +240,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.score_blocks = cus;
   ctx->ws.sub_stage = (uint32_t*)(p + offs[kSubStage]);
   ctx->ws.res_count = (uint32_t*)(p + offs[kResCount]);
+  ctx->ws.res_bits = (unsigned long long*)(p + offs[kResBits]);
   ctx->ws.tile_info = (uint2*)(p + offs[kTileInfo]);
 
   double freq[kRopeDim / 2];

@@ -93,6 +93,8 @@ struct Workspace {
   int score_blocks = 0;          // compute units of the device
   uint32_t* sub_stage = nullptr; // [max_batch][kSubStageRowWords]: the subset top-K's gathered keys
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
+  unsigned long long* res_bits = nullptr;  // [max_batch][ceil(max_n / kResSlice) * 256]: per 16 chunks, the
+                                           //   three sets' bits (16 each), from the count pass
   uint2* tile_info = nullptr;    // [max_batch][tile_info_stride(max_n)]: per tile, for the top-K finish
 };
 

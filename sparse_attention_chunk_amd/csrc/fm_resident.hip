@@ -11,10 +11,12 @@
 // A mask byte counts as set when it is non-zero.
 //
 // Two passes over slices of kResSlice chunks (grid = slices x rows):
-//   1. count: each block counts its slice's three sets;
+//   1. count: each block counts its slice's three sets, and each thread
+//      keeps its 16 chunks' membership bits (one 8-byte word);
 //   2. write: each block adds the counts of the slices before it (the list
-//      offsets), scans its threads' counts, and writes its indices in order;
-//      the first slice's block also writes the row totals.
+//      offsets), scans its threads' counts, and writes its indices in order
+//      from the kept bits (the masks are read once); the first slice's block
+//      also writes the row totals.
 // Every list is ascending because slices, threads and bytes are visited in
 // index order.  Lists are capped at `cap` entries per row (the counts are
 // the full sizes).
@@ -100,11 +102,13 @@ __device__ __forceinline__ uint3 block_sum3(uint3 v, uint32_t* s_w) {
 }
 
 __global__ __launch_bounds__(kResThreads) void res_count_kernel(const uint8_t* prev, const uint8_t* mask, int64_t N,
-                                                                uint32_t* counts) {
+                                                                uint32_t* counts, unsigned long long* bits) {
   __shared__ uint32_t s_w[3 * (kResThreads / 64)];
   const int b = blockIdx.y;
   const int64_t n0 = (int64_t)blockIdx.x * kResSlice + (int64_t)threadIdx.x * kResPer;
   const SliceBits sb = load_bits(prev, mask, b, N, n0);
+  bits[((size_t)b * gridDim.x + blockIdx.x) * kResThreads + threadIdx.x] =
+      (unsigned long long)sb.cur | ((unsigned long long)sb.enter << 16) | ((unsigned long long)sb.leave << 32);
   const uint3 t = block_sum3(make_uint3(__popc(sb.cur), __popc(sb.enter), __popc(sb.leave)), s_w);
   if (threadIdx.x == 0) {
     uint32_t* c = counts + ((size_t)b * gridDim.x + blockIdx.x) * 3;
@@ -123,7 +127,7 @@ __device__ __forceinline__ void write_list(uint32_t bits, int64_t n0, uint32_t p
   }
 }
 
-__global__ __launch_bounds__(kResThreads) void res_write_kernel(const uint8_t* prev, const uint8_t* mask, int64_t N,
+__global__ __launch_bounds__(kResThreads) void res_write_kernel(const unsigned long long* bits,
                                                                 const uint32_t* counts, int32_t cap, int32_t* resident,
                                                                 int32_t* n_resident, int32_t* entering,
                                                                 int32_t* n_entering, int32_t* leaving,
@@ -133,7 +137,8 @@ __global__ __launch_bounds__(kResThreads) void res_write_kernel(const uint8_t* p
   const int slice = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)slice * kResSlice + (int64_t)threadIdx.x * kResPer;
-  const SliceBits sb = load_bits(prev, mask, b, N, n0);
+  const unsigned long long kept = bits[((size_t)b * gridDim.x + slice) * kResThreads + threadIdx.x];
+  const SliceBits sb{(uint32_t)kept & 0xffffu, (uint32_t)(kept >> 16) & 0xffffu, (uint32_t)(kept >> 32) & 0xffffu};
 
   // List offsets of this slice: the counts of the slices before it (and,
   // for slice 0, the row totals over all slices).
@@ -183,8 +188,8 @@ hipError_t launch_resident_delta(const Workspace& ws, const uint8_t* prev, const
                                  int32_t cap, int32_t* resident, int32_t* n_resident, int32_t* entering,
                                  int32_t* n_entering, int32_t* leaving, int32_t* n_leaving, hipStream_t stream) {
   const dim3 grid((unsigned)((N + kResSlice - 1) / kResSlice), (unsigned)B);
-  hipLaunchKernelGGL(res_count_kernel, grid, dim3(kResThreads), 0, stream, prev, mask, N, ws.res_count);
-  hipLaunchKernelGGL(res_write_kernel, grid, dim3(kResThreads), 0, stream, prev, mask, N,
+  hipLaunchKernelGGL(res_count_kernel, grid, dim3(kResThreads), 0, stream, prev, mask, N, ws.res_count, ws.res_bits);
+  hipLaunchKernelGGL(res_write_kernel, grid, dim3(kResThreads), 0, stream, (const unsigned long long*)ws.res_bits,
                      (const uint32_t*)ws.res_count, cap, resident, n_resident, entering, n_entering, leaving,
                      n_leaving);
   return hipGetLastError();

@@ -124,3 +124,14 @@ def test_argument_errors(retr):
     assert L.fm_resident_delta(ctx, None, None, 2, 100, 100, out.data_ptr(), cnt.data_ptr(), None, None, None, None,
                                None) == _lib.FM_EINVAL
     assert L.fm_resident_delta(ctx, None, None, 0, 0, 0, None, None, None, None, None, None, None) == _lib.FM_OK
+
+
+def test_many_calls_in_a_row_on_one_context(retr):
+    """Back-to-back calls of different shapes on one context: no call sees
+    another's intermediate counts."""
+    rng = np.random.default_rng(78)
+    for it, (B, N) in enumerate([(4, 262144), (2, 5000), (4, 262144), (3, 77777), (1, 4096), (4, 262144)]):
+        mask = (rng.uniform(size=(B, N)) < 0.01 * (it + 1)).astype(np.uint8)
+        prev = (rng.uniform(size=(B, N)) < 0.02).astype(np.uint8)
+        lists, counts = run_raw(retr, torch.from_numpy(mask).cuda(), torch.from_numpy(prev).cuda(), N)
+        check_rows(mask, prev, lists, counts, N)
