@@ -58,8 +58,11 @@ constexpr int kMaxScoreBlocks = 1024;
 constexpr int kSelBins = 2048;
 
 // Subset top-K: words staged per row for a list's gathered keys (32 rounds
-// of 1024 keys, then 32 validity words per round).
+// of 1024 keys, then 32 validity words per round) on the long-list path;
+// lists of up to kSubFastCap entries take the scan + finish path, with the
+// keys and tile words in their own buffers.
 constexpr size_t kSubStageRowWords = 32 * 1024 + 32 * 32;
+constexpr int kSubFastCap = 32768;
 
 // Resident-set compaction: a block covers kResSlice chunks of one row.
 constexpr int kResSlice = 4096;
@@ -92,6 +95,8 @@ struct Workspace {
   int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
   int score_blocks = 0;          // compute units of the device
   uint32_t* sub_stage = nullptr; // [max_batch][kSubStageRowWords]: the subset top-K's gathered keys
+  uint32_t* sub_keys = nullptr;  // [max_batch][kSubFastCap]: keys of the list positions (scan + finish path)
+  uint2* sub_tiles = nullptr;    // [max_batch][kSubFastCap / 16]: their tile words
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
   unsigned long long* res_bits = nullptr;  // [max_batch][ceil(max_n / kResSlice) * 256]: per 16 chunks, the
                                            //   three sets' bits (16 each), from the count pass
@@ -131,6 +136,9 @@ hipError_t launch_score_threshold(const Workspace& ws, const float* q, const flo
 // Subset top-K: init raises the LDS limit of the in-LDS variant (once, at
 // context creation).
 hipError_t init_select_topk_subset();
+hipError_t launch_select_topk_subset_fast(const Workspace& ws, const float* scores, int B, int64_t N,
+                                          const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
+                                          int32_t* out, int32_t* n_out, hipStream_t stream);
 hipError_t launch_select_topk_subset(const Workspace& ws, const float* scores, int B, int64_t N,
                                      const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                      int32_t* out, int32_t* n_out, hipStream_t stream);

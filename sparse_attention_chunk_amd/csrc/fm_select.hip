@@ -62,9 +62,18 @@ __device__ __forceinline__ int score_bin(float e) {
   const float x = e * kHistScale;
   return !(x > 0.f) ? 0 : (x >= (float)(kSelBins - 1) ? kSelBins - 1 : (int)x);  // NaN: bin 0
 }
-// score_bin(e) >= c, for c in [0, kSelBins): x >= c when c >= 1, as the
+// The float whose order_key is k.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// The bin of an entry's key; key 0 (no order_key of a score is 0) marks an
+// entry that is never chosen and sits in bin 0.
+__device__ __forceinline__ int key_bin(uint32_t k) { return k == 0 ? 0 : score_bin(key_float(k)); }
+// key_bin(k) >= c, for c in [0, kSelBins): x >= c when c >= 1, as the
 // integer part of x > 0 is at least c exactly when x is.
-__device__ __forceinline__ bool bin_at_least(float e, int c) { return c == 0 || e * kHistScale >= (float)c; }
+__device__ __forceinline__ bool key_at_least(uint32_t k, int c) {
+  return c == 0 || (k != 0 && key_float(k) * kHistScale >= (float)c);
+}
 
 // log2 of the tile's kSub-chunk parts in a row of vn chunks (0..2): the
 // largest leaving at least 4 K tiles.
@@ -73,31 +82,33 @@ __device__ __forceinline__ int tile_shift(int64_t vn, int32_t k) {
   return (vn >> 6) >= need ? 2 : ((vn >> 5) >= need ? 1 : 0);
 }
 
-// Tile word: x bits 0-10 the largest score's bin, 11-16 its position in the
+// Tile word: x bits 0-10 the largest key's bin, 11-16 its position in the
 // tile, 17-27 the second largest's bin; y bits 0-5 the second largest's
-// position, 6-16 the third largest's bin (bin 0 where there is none).  Ties
-// count as separate scores.
+// position, 6-16 the third largest's bin (bin 0 where there is none), 17-23
+// the tile's entries with a key (not 0).  Ties count as separate entries.
 __device__ __forceinline__ int tw_bin1(uint2 w) { return (int)(w.x & 0x7ffu); }
 __device__ __forceinline__ uint32_t tw_pos1(uint2 w) { return (w.x >> 11) & 0x3fu; }
 __device__ __forceinline__ int tw_bin2(uint2 w) { return (int)((w.x >> 17) & 0x7ffu); }
 __device__ __forceinline__ uint32_t tw_pos2(uint2 w) { return w.y & 0x3fu; }
 __device__ __forceinline__ int tw_bin3(uint2 w) { return (int)((w.y >> 6) & 0x7ffu); }
+__device__ __forceinline__ uint32_t tw_count(uint2 w) { return (w.y >> 17) & 0x7fu; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)bytes, kRawBuffer);
 }
 
-// The three largest of a set of scores: values m1 >= m2 >= m3, positions of
-// the first two.
+// The three largest keys of a set of entries: m1 >= m2 >= m3 (0 where
+// there is none), positions of the first two, and the entries with a key.
 struct Top3 {
-  float m1, m2, m3;
-  uint32_t p1, p2;
+  uint32_t m1, m2, m3;
+  uint32_t p1, p2, n;
 };
 
-__device__ __forceinline__ void top3_take(Top3& a, float v, uint32_t pos) {
+__device__ __forceinline__ void top3_take(Top3& a, uint32_t v, uint32_t pos) {
   const bool gt1 = v > a.m1;
   const bool gt2 = v > a.m2;
-  a.m3 = gt2 ? a.m2 : fmaxf(a.m3, v);
+  a.n += v != 0 ? 1u : 0u;
+  a.m3 = gt2 ? a.m2 : max(a.m3, v);
   a.m2 = gt1 ? a.m1 : (gt2 ? v : a.m2);
   a.p2 = gt1 ? a.p1 : (gt2 ? pos : a.p2);
   a.m1 = gt1 ? v : a.m1;
@@ -108,9 +119,9 @@ __device__ __forceinline__ void top3_take(Top3& a, float v, uint32_t pos) {
 // position).
 __device__ __forceinline__ Top3 top3_merge(const Top3& a, const Top3& b) {
   const bool af = a.m1 > b.m1 || (a.m1 == b.m1 && a.p1 < b.p1);  // a holds the largest
-  const float w1 = af ? a.m1 : b.m1, w2 = af ? a.m2 : b.m2, w3 = af ? a.m3 : b.m3;
+  const uint32_t w1 = af ? a.m1 : b.m1, w2 = af ? a.m2 : b.m2, w3 = af ? a.m3 : b.m3;
   const uint32_t wp1 = af ? a.p1 : b.p1, wp2 = af ? a.p2 : b.p2;
-  const float l1 = af ? b.m1 : a.m1, l2 = af ? b.m2 : a.m2;
+  const uint32_t l1 = af ? b.m1 : a.m1, l2 = af ? b.m2 : a.m2;
   const uint32_t lp1 = af ? b.p1 : a.p1;
   const bool w_second = w2 > l1 || (w2 == l1 && wp2 < lp1);
   Top3 r;
@@ -118,8 +129,26 @@ __device__ __forceinline__ Top3 top3_merge(const Top3& a, const Top3& b) {
   r.p1 = wp1;
   r.m2 = w_second ? w2 : l1;
   r.p2 = w_second ? wp2 : lp1;
-  r.m3 = w_second ? fmaxf(w3, l1) : fmaxf(w2, l2);
+  r.m3 = w_second ? max(w3, l1) : max(w2, l2);
+  r.n = a.n + b.n;
   return r;
+}
+
+// Merges the Top3 of the 2^s adjacent lanes of a tile (lane groups of 2^s),
+// then encodes the tile word (every lane of the group holds it).
+__device__ __forceinline__ uint2 tile_word(Top3 a, int s) {
+  for (int i = 0; i < s; ++i) {
+    Top3 o;
+    o.m1 = (uint32_t)__shfl_xor((int)a.m1, 1 << i);
+    o.m2 = (uint32_t)__shfl_xor((int)a.m2, 1 << i);
+    o.m3 = (uint32_t)__shfl_xor((int)a.m3, 1 << i);
+    o.p1 = (uint32_t)__shfl_xor((int)a.p1, 1 << i);
+    o.p2 = (uint32_t)__shfl_xor((int)a.p2, 1 << i);
+    o.n = (uint32_t)__shfl_xor((int)a.n, 1 << i);
+    a = top3_merge(a, o);
+  }
+  return make_uint2((uint32_t)key_bin(a.m1) | (a.p1 << 11) | ((uint32_t)key_bin(a.m2) << 17),
+                    a.p2 | ((uint32_t)key_bin(a.m3) << 6) | (a.n << 17));
 }
 
 // 1. Mask bytes and tile words.  grid = (ceil(N / kScanSlice), B), block =
@@ -140,35 +169,24 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(const float* __
   if (!keep_all && top_k > 0 && (int64_t)blockIdx.x * kScanSlice < vn) {
     const int s = tile_shift(vn, top_k);
     const uint32_t p0 = (uint32_t)(g & ((1 << s) - 1)) * kSub;  // the part's first position in its tile
-    Top3 a = {-INFINITY, -INFINITY, -INFINITY, p0, p0};     // parts past vn hold -inf
+    Top3 a = {0u, 0u, 0u, p0, p0, 0u};  // parts past vn hold no entry
     if (n0 + kSub <= vn && ((((uintptr_t)(row + n0)) & 15) == 0)) {
       float4 v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(row + n0 + 4 * q);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        top3_take(a, v[q].x, p0 + 4 * q);
-        top3_take(a, v[q].y, p0 + 4 * q + 1);
-        top3_take(a, v[q].z, p0 + 4 * q + 2);
-        top3_take(a, v[q].w, p0 + 4 * q + 3);
+        top3_take(a, order_key(v[q].x), p0 + 4 * q);
+        top3_take(a, order_key(v[q].y), p0 + 4 * q + 1);
+        top3_take(a, order_key(v[q].z), p0 + 4 * q + 2);
+        top3_take(a, order_key(v[q].w), p0 + 4 * q + 3);
       }
     } else {
-      for (int j = 0; j < kSub && n0 + j < vn; ++j) top3_take(a, row[n0 + j], p0 + j);
+      for (int j = 0; j < kSub && n0 + j < vn; ++j) top3_take(a, order_key(row[n0 + j]), p0 + j);
     }
-    for (int i = 0; i < s; ++i) {
-      Top3 o;
-      o.m1 = __shfl_xor(a.m1, 1 << i);
-      o.m2 = __shfl_xor(a.m2, 1 << i);
-      o.m3 = __shfl_xor(a.m3, 1 << i);
-      o.p1 = (uint32_t)__shfl_xor((int)a.p1, 1 << i);
-      o.p2 = (uint32_t)__shfl_xor((int)a.p2, 1 << i);
-      a = top3_merge(a, o);
-    }
+    const uint2 word = tile_word(a, s);
     const int64_t tile = g >> s;
-    if (p0 == 0 && (tile << (4 + s)) < vn)
-      tile_info[(size_t)b * tile_info_stride(N) + tile] =
-          make_uint2((uint32_t)score_bin(a.m1) | (a.p1 << 11) | ((uint32_t)score_bin(a.m2) << 17),
-                     a.p2 | ((uint32_t)score_bin(a.m3) << 6));
+    if (p0 == 0 && (tile << (4 + s)) < vn) tile_info[(size_t)b * tile_info_stride(N) + tile] = word;
   }
   if (n0 >= N) return;
   const uint8_t keep = keep_all ? 1 : 0;
@@ -200,20 +218,65 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wtot
   return before + incl - v;
 }
 
-// 2. Exact top-K of each row.  grid = B, block = kFinishThreads.
-__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t N,
-                                                                     const int32_t* __restrict__ valid_n,
-                                                                     int32_t top_k,
-                                                                     const uint2* __restrict__ tile_info,
-                                                                     uint8_t* __restrict__ mask) {
+// 1b. Keys and tile words of subset lists (the per-step top-K over the
+// resident set).  grid = (ceil(cap / kSubScanSlice), B), block =
+// kScanThreads; thread t covers list positions 4 g .. 4 g + 3, g =
+// blockIdx.x 256 + t (many threads, so many index -> score gathers in
+// flight), and the 4 2^s threads of a tile merge their parts.  The key of a
+// position is the order_key of its chunk's score, or 0 when the position is
+// past the row's list or its chunk is outside [0, N).
+constexpr int kSubPart = 4;
+constexpr int kSubScanSlice = kScanThreads * kSubPart;
+__global__ __launch_bounds__(kScanThreads) void subset_scan_kernel(const float* __restrict__ scores, int64_t N,
+                                                                   const int32_t* __restrict__ subset,
+                                                                   const int32_t* __restrict__ n_subset,
+                                                                   int32_t cap, int32_t top_k,
+                                                                   uint32_t* __restrict__ keys,
+                                                                   uint2* __restrict__ tile_info) {
+  const int b = blockIdx.y;
+  const int64_t n64 = n_subset ? (int64_t)n_subset[b] : (int64_t)cap;
+  const uint32_t n = (uint32_t)(n64 < 0 ? 0 : (n64 > cap ? cap : n64));
+  if (top_k == 0 || (uint32_t)blockIdx.x * kSubScanSlice >= n) return;  // uniform over the block
+  const uint32_t g = blockIdx.x * kScanThreads + threadIdx.x;
+  const uint32_t p0 = g * kSubPart;
+  const __amdgpu_buffer_rsrc_t rs = buffer(subset + (size_t)b * cap, 4 * (int64_t)n);
+  const __amdgpu_buffer_rsrc_t rv = buffer(scores + (size_t)b * N, N < 0x20000000 ? 4 * N : 0x7fffffff);
+  const u32x4 iv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4u * p0, 0, 0));
+  const int32_t idx[kSubPart] = {(int32_t)iv.x, (int32_t)iv.y, (int32_t)iv.z, (int32_t)iv.w};
+  uint32_t k[kSubPart];
+#pragma unroll
+  for (int j = 0; j < kSubPart; ++j) {
+    const bool ok = p0 + j < n && idx[j] >= 0 && (int64_t)idx[j] < N;
+    const float v = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rv, ok ? 4u * (uint32_t)idx[j] : kOutOfRange, 0, 0));
+    k[j] = ok ? order_key(v) : 0u;
+  }
+  const int s = tile_shift(n, top_k);
+  const int m = s + 2;                                  // log2 of the parts per tile
+  const uint32_t pt = (g & ((1u << m) - 1)) * kSubPart;  // the part's first position in its tile
+  Top3 a = {0u, 0u, 0u, pt, pt, 0u};
+#pragma unroll
+  for (int j = 0; j < kSubPart; ++j) top3_take(a, k[j], pt + j);
+  const uint2 word = tile_word(a, m);
+  uint32_t* krow = keys + (size_t)b * kSubFastCap;
+  if (p0 < n) *(uint4*)(krow + p0) = make_uint4(k[0], k[1], k[2], k[3]);
+  const uint32_t tile = g >> m;
+  if (pt == 0 && (tile << (4 + s)) < n) tile_info[(size_t)b * (kSubFastCap / kSub) + tile] = word;
+}
+
+// 2. Exact top-K of each row.  grid = B, block = kFinishThreads.  SUBSET:
+// the entries are the positions of the row's subset list (keys staged by
+// subset_scan_kernel; the chosen ones written as chunk indices in list
+// order to out, their number to n_out); else the row's chunks (keys from
+// the scores; the chosen ones' mask bytes set).
+template <bool SUBSET>
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, int64_t N, const int32_t* __restrict__ valid_n, int32_t top_k,
+    const uint2* __restrict__ tile_info, uint8_t* __restrict__ mask, const uint32_t* __restrict__ keys,
+    const int32_t* __restrict__ subset, const int32_t* __restrict__ n_subset, int32_t cap, int32_t* __restrict__ out,
+    int32_t* __restrict__ n_out) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t vn = row_valid(valid_n, b, N);
-  if (top_k == 0 || (int64_t)top_k >= vn) return;  // the scan wrote the whole mask
-  uint8_t* mrow = mask + (size_t)b * N;
-  const float* row = scores + (size_t)b * N;
-  const uint32_t K = (uint32_t)top_k;
-  const uint32_t vn32 = (uint32_t)vn;  // below 2^26
   __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
   __shared__ uint32_t s_e[kFinishList];
   __shared__ uint32_t s_f[kFinishFull];
@@ -222,14 +285,44 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
   __shared__ uint32_t s_wtot[kFinishThreads / 64];
   __shared__ uint32_t s_mm[2 * (kFinishThreads / 64)];
   __shared__ uint32_t s_out[3];
+  __shared__ uint32_t s_bits[SUBSET ? kSubFastCap / 32 : 1];  // chosen list positions
+
+  // vn: the row's entries (chunks below valid_n, or list positions).
+  int64_t vn;
+  if (SUBSET) {
+    const int64_t n64 = n_subset ? (int64_t)n_subset[b] : (int64_t)cap;
+    vn = n64 < 0 ? 0 : (n64 > cap ? cap : n64);
+    if (top_k == 0 || vn == 0) {
+      if (t == 0) n_out[b] = 0;
+      return;
+    }
+  } else {
+    vn = row_valid(valid_n, b, N);
+    if (top_k == 0 || (int64_t)top_k >= vn) return;  // the scan wrote the whole mask
+  }
+  uint8_t* mrow = mask + (SUBSET ? 0 : (size_t)b * N);
+  const float* row = scores + (size_t)b * N;
+  const uint32_t* krow = keys + (SUBSET ? (size_t)b * kSubFastCap : 0);
+  uint32_t K = (uint32_t)top_k;
+  const uint32_t vn32 = (uint32_t)vn;  // below 2^26
+  const __amdgpu_buffer_rsrc_t rr = SUBSET ? buffer(krow, vn * 4) : buffer(row, vn * 4);
+  // The key of entry n (loads past vn give key 0 / score 0, never used).
+  auto key_of = [&](uint32_t n) -> uint32_t {
+    const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b32(rr, n != kNone ? 4u * n : kOutOfRange, 0, 0);
+    return SUBSET ? raw : order_key(__uint_as_float(raw));
+  };
+  auto emit = [&](uint32_t n) {
+    if (SUBSET) atomicOr(&s_bits[n >> 5], 1u << (n & 31));
+    else mrow[n] = 1;
+  };
 
   // Tile words: thread t holds tiles 512 (j / 2) + 2 t + j % 2 (16-byte
   // loads through a descriptor over the row's slot, a multiple of 16 bytes:
   // zeros past it); their maxima are counted in the row's histogram.
   const int s = tile_shift(vn, top_k);
-  const int lt = 4 + s;  // log2 of the tile's chunks
+  const int lt = 4 + s;  // log2 of the tile's entries
   const uint32_t nt = (uint32_t)((vn + (1 << lt) - 1) >> lt);
-  const int64_t tstride = tile_info_stride(N);
+  const int64_t tstride = SUBSET ? kSubFastCap / kSub : tile_info_stride(N);
   const uint2* irow = tile_info + (size_t)b * tstride;
   const __amdgpu_buffer_rsrc_t ir = buffer(irow, tstride * 8);
   constexpr int kRegTiles = 2 * kFinishRegPairs;
@@ -244,18 +337,39 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
   auto tile_of = [&](int j) { return (uint32_t)(2 * kFinishThreads * (j >> 1) + 2 * t + (j & 1)); };
   constexpr uint32_t kBlockTiles = (uint32_t)kRegTiles * kFinishThreads;
   clear_bins<kFinishThreads>(h);
+  if (SUBSET)
+    for (int i = t; i < kSubFastCap / 32; i += kFinishThreads) s_bits[i] = 0u;
   __syncthreads();
+  uint32_t counted = 0;  // entries with a key in this thread's tiles
 #pragma unroll
   for (int j = 0; j < kRegTiles; ++j)
-    if (tile_of(j) < nt) atomicAdd(&h[tw_bin1(info[j])], 1u);
-  for (uint32_t i = kBlockTiles + t; i < nt; i += kFinishThreads) atomicAdd(&h[tw_bin1(irow[i])], 1u);
+    if (tile_of(j) < nt) {
+      atomicAdd(&h[tw_bin1(info[j])], 1u);
+      counted += tw_count(info[j]);
+    }
+  for (uint32_t i = kBlockTiles + t; i < nt; i += kFinishThreads) {
+    const uint2 w = irow[i];
+    atomicAdd(&h[tw_bin1(w)], 1u);
+    counted += tw_count(w);
+  }
   __syncthreads();
+  if (SUBSET) {
+    // The chosen number: K, or every entry with a key when there are fewer.
+    uint32_t n_keyed;
+    (void)block_excl_scan(counted, s_wtot, &n_keyed);
+    if (K >= n_keyed) {
+      for (uint32_t n = t; n < vn32; n += kFinishThreads)
+        if (key_of(n) != 0) emit(n);
+      K = n_keyed;
+      goto write_out;
+    }
+  }
+  {
   int c = 0;
   if (K <= nt) {
     block_find<kFinishThreads>(h, K, s_wtot, s_out, true);
     c = (int)s_out[0];
   }
-
   // The listed chunks of each tile whose maximum is in bin c or above: its
   // largest one or two (s_e), or, when its third largest is in bin c or
   // above too, the whole tile (s_f).  Each thread first stages its tiles'
@@ -338,9 +452,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
       const uint32_t y = x - ne;
       return (s_f[y >> lt] << lt) + (y & ((1u << lt) - 1));
     };
-    // The candidates: listed chunks in bin c or above, with their keys.  A
-    // descriptor over the row's valid scores gives 0 past them.
-    const __amdgpu_buffer_rsrc_t rr = buffer(row, vn * 4);
+    // The candidates: listed entries with a key in bin c or above.
     auto final_select = [&](auto each) {
       // Bins of the keys between the smallest and the largest candidate:
       // (key - kmin) >> sh < kSelBins.
@@ -381,7 +493,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
       uint32_t pos = block_excl_scan(mine, s_wtot, &in_c2);
       each([&](uint2 e) {
         const uint32_t bn = (e.x - kmin) >> sh;
-        if (bn > c2) mrow[e.y] = 1;
+        if (bn > c2) emit(e.y);
         if (bn == c2) {
           if (pos < (uint32_t)kFinishThreads) s_r[pos] = e;
           ++pos;
@@ -396,7 +508,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
             const uint2 o = s_r[j];
             rank += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
           }
-          if (rank < need) mrow[me.y] = 1;
+          if (rank < need) emit(me.y);
         }
       } else {
         auto in_bin = [&](auto f) {
@@ -407,61 +519,57 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
         uint32_t T, last;
         radix_select<kFinishThreads>(in_bin, need, index_bits(vn), h, s_wtot, s_out, &T, &last);
         in_bin([&](uint2 e) {
-          if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
+          if (e.x > T || (e.x == T && e.y <= last)) emit(e.y);
         });
       }
     };
     if (total <= (uint32_t)(kFinishThreads * kFinishRegEntries)) {
       // Each thread holds its listed chunks in registers.
       uint32_t n[kFinishRegEntries];
-      float e[kFinishRegEntries];
+      uint32_t e[kFinishRegEntries];
 #pragma unroll
       for (int r = 0; r < kFinishRegEntries; ++r) {
         const uint32_t x = t + r * kFinishThreads;
         n[r] = x < total ? entry(x) : kNone;
       }
 #pragma unroll
-      for (int r = 0; r < kFinishRegEntries; ++r)
-        e[r] = __builtin_bit_cast(float,
-                                  __builtin_amdgcn_raw_buffer_load_b32(rr, n[r] != kNone ? 4u * n[r] : kOutOfRange, 0, 0));
+      for (int r = 0; r < kFinishRegEntries; ++r) e[r] = key_of(n[r]);
       uint2 cand[kFinishRegEntries];
       bool ok[kFinishRegEntries];
 #pragma unroll
       for (int r = 0; r < kFinishRegEntries; ++r) {
-        ok[r] = n[r] < vn32 && bin_at_least(e[r], c);
-        cand[r] = make_uint2(order_key(e[r]), n[r]);
+        ok[r] = n[r] < vn32 && e[r] != 0 && key_at_least(e[r], c);
+        cand[r] = make_uint2(e[r], n[r]);
       }
       final_select([&](auto f) {
 #pragma unroll
         for (int r = 0; r < kFinishRegEntries; ++r)
           if (ok[r]) f(cand[r]);
       });
-      return;
+      goto write_out;
     }
     // More listed chunks: the candidates go to LDS first.
     uint32_t nc = 0;
     for (uint32_t base = 0; base < total; base += kFinishThreads * 4) {
       uint32_t n[4];
-      float e[4];
+      uint32_t e[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t x = base + t + r * kFinishThreads;
         n[r] = x < total ? entry(x) : kNone;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        e[r] = __builtin_bit_cast(float,
-                                  __builtin_amdgcn_raw_buffer_load_b32(rr, n[r] != kNone ? 4u * n[r] : kOutOfRange, 0, 0));
+      for (int r = 0; r < 4; ++r) e[r] = key_of(n[r]);
       uint32_t okb = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (n[r] < vn32 && bin_at_least(e[r], c)) okb |= 1u << r;
+        if (n[r] < vn32 && e[r] != 0 && key_at_least(e[r], c)) okb |= 1u << r;
       uint32_t tot;
       uint32_t pos = nc + block_excl_scan(__popc(okb), s_wtot, &tot);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (okb & (1u << r)) {
-          if (pos < (uint32_t)kFinishCand) s_c[pos] = make_uint2(order_key(e[r]), n[r]);
+          if (pos < (uint32_t)kFinishCand) s_c[pos] = make_uint2(e[r], n[r]);
           ++pos;
         }
       nc += tot;
@@ -471,19 +579,53 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const float
       final_select([&](auto f) {
         for (uint32_t i = t; i < nc; i += kFinishThreads) f(s_c[i]);
       });
-      return;
+      goto write_out;
     }
   }
-  // Too many equal or nearly equal scores for LDS: exact selection over the
-  // whole row (nothing has been set yet).
-  auto each = [&](auto f) {
-    for (int64_t n = t; n < vn; n += kFinishThreads) f(make_uint2(order_key(row[n]), (uint32_t)n));
-  };
-  uint32_t T, last;
-  radix_select<kFinishThreads>(each, K, index_bits(vn), h, s_wtot, s_out, &T, &last);
-  each([&](uint2 e) {
-    if (e.x > T || (e.x == T && e.y <= last)) mrow[e.y] = 1;
-  });
+  // Too many equal or nearly equal keys for LDS: exact selection over all
+  // the row's entries (nothing has been chosen yet).
+  {
+    auto each = [&](auto f) {
+      for (uint32_t n = t; n < vn32; n += kFinishThreads) {
+        const uint32_t k = key_of(n);
+        if (!SUBSET || k != 0) f(make_uint2(k, n));
+      }
+    };
+    uint32_t T, last;
+    radix_select<kFinishThreads>(each, K, index_bits(vn), h, s_wtot, s_out, &T, &last);
+    each([&](uint2 e) {
+      if (e.x > T || (e.x == T && e.y <= last)) emit(e.y);
+    });
+  }
+  }
+write_out:
+  if (SUBSET) {
+    // The chosen positions in list order: thread t holds bitmap words 4 t ..
+    // 4 t + 3; a scan of their counts gives each one's place in out.
+    __syncthreads();
+    uint32_t w4[4], cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int wi = 4 * t + q;
+      w4[q] = wi < kSubFastCap / 32 ? s_bits[wi] : 0u;
+      cnt += __popc(w4[q]);
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan(cnt, s_wtot, &tot);
+    const int32_t* srow = subset + (size_t)b * cap;
+    int32_t* orow = out + (size_t)b * top_k;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t bits = w4[q];
+      while (bits) {
+        const uint32_t p = 32u * (4 * t + q) + __builtin_ctz(bits);
+        bits &= bits - 1;
+        if (pos < (uint32_t)top_k) orow[pos] = srow[p];
+        ++pos;
+      }
+    }
+    if (t == 0) n_out[b] = (int32_t)K;
+  }
 }
 
 // Threshold mask: 16 chunks per thread, one 16-byte store when the run is
@@ -519,8 +661,22 @@ hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, i
   const unsigned slices = (unsigned)((N + kScanSlice - 1) / kScanSlice);
   hipLaunchKernelGGL(topk_scan_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, valid_n, top_k,
                      ws.tile_info, mask);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k,
-                     (const uint2*)ws.tile_info, mask);
+  hipLaunchKernelGGL(topk_finish_kernel<false>, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k,
+                     (const uint2*)ws.tile_info, mask, (const uint32_t*)nullptr, (const int32_t*)nullptr,
+                     (const int32_t*)nullptr, 0, (int32_t*)nullptr, (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk_subset_fast(const Workspace& ws, const float* scores, int B, int64_t N,
+                                          const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
+                                          int32_t* out, int32_t* n_out, hipStream_t stream) {
+  const unsigned slices = (unsigned)((cap + kSubScanSlice - 1) / kSubScanSlice);
+  if (slices > 0)
+    hipLaunchKernelGGL(subset_scan_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, subset, n_subset,
+                       cap, top_k, ws.sub_keys, ws.sub_tiles);
+  hipLaunchKernelGGL(topk_finish_kernel<true>, dim3(B), dim3(kFinishThreads), 0, stream, scores, N,
+                     (const int32_t*)nullptr, top_k, (const uint2*)ws.sub_tiles, (uint8_t*)nullptr,
+                     (const uint32_t*)ws.sub_keys, subset, n_subset, cap, out, n_out);
   return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@ __device__ __forceinline__ bool in_range(int32_t i, int64_t N) { return i >= 0 &
 // per row, kSubLdsRounds x 1024 keys then the validity bitmap (32 words per
 // round), in the workspace's staging rows.
 constexpr size_t kSubPreRow = (size_t)kSubLdsRounds * kSubThreads + (size_t)kSubLdsRounds * 2 * kSubWaves;
-static_assert(kSubPreRow == kSubStageRowWords, "staging row size");
+static_assert(kSubPreRow <= kSubStageRowWords, "staging row size");
 
 // grid = (rounds, B), 256 threads: round r of row b, positions r 1024 + 256 u
 // + t (u = 0..3).  Writes each position's key and the round's bitmap words.
@@ -374,6 +374,8 @@ hipError_t init_select_topk_subset() {
 hipError_t launch_select_topk_subset(const Workspace& ws, const float* scores, int B, int64_t N,
                                      const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                      int32_t* out, int32_t* n_out, hipStream_t stream) {
+  if (cap <= kSubFastCap) return launch_select_topk_subset_fast(ws, scores, B, N, subset, n_subset, cap, top_k, out,
+                                                                 n_out, stream);
   if (cap <= kSubLdsRounds * kSubThreads) {
     uint32_t* pre = ws.sub_stage;
     if (B > 0 && cap > 0) {

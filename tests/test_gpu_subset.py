@@ -67,8 +67,8 @@ def check(retr, scores, subset, n_sub, top_k, with_count=True):
     (3, 1000, 17, "sorted", 0),
     (5, 70000, 5000, "sorted", 3),
     (5, 50000, 3000, "shuffled", 2),
-    (2, 262144, 32768, "sorted", 0),     # keys held in LDS
-    (2, 262144, 65536, "sorted", 5),     # keys gathered again in every pass
+    (2, 262144, 32768, "sorted", 0),     # the longest list of the tile scan + finish path
+    (2, 262144, 65536, "sorted", 5),     # longer lists: keys gathered again in every pass
     (3, 4096, 4096, "sorted", 0),
 ])
 def test_random_subsets_exact(retr, B, N, cap, order, bad):
@@ -80,9 +80,10 @@ def test_random_subsets_exact(retr, B, N, cap, order, bad):
 
 @pytest.mark.parametrize("levels,k", [(4, 512), (64, 512), (100000, 7000), (3, 20000)])
 def test_sampled_cutoff_paths(retr, levels, k):
-    """Long lists held in LDS take the sampled cut-off; heavy ties at the
-    cut-off (few distinct scores) overflow it and fall back to the whole
-    list.  Both must give the exact result."""
+    """Lists of up to 32768 entries take the tile scan + finish; heavy ties
+    at the cut-off (few distinct scores) overflow its candidate lists and
+    fall back to a radix selection over the whole list.  Both must give the
+    exact result."""
     rng = np.random.default_rng(levels + k)
     B, N, cap = 3, 262144, 32768
     scores = (rng.integers(0, levels, (B, N)) / levels).astype(np.float32)
@@ -92,9 +93,8 @@ def test_sampled_cutoff_paths(retr, levels, k):
 
 
 def test_small_context_gathers_in_the_selecting_block():
-    """A context whose workspace cannot stage the gathered keys (small
-    max_n) gathers them in the selecting block instead; lists longer than N
-    (padded with out-of-range entries) still take the sampled cut-off."""
+    """A small context (max_n 8192) with lists longer than N, padded with
+    out-of-range entries, in list order and shuffled."""
     import sparse_attention_chunk_amd as fm
     r = fm.FlashMemoryRetriever(fm.weights_to_device(synth.make_weights()), max_batch=4, max_n=8192)
     try:
