@@ -47,9 +47,9 @@ PEAK_F16_TFLOPS = 2500.0               # MI355X dense f16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0               # MI355X dense fp8 MFMA
 CSRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc")
-# Everything the score kernel's code and launch shape come from: a change to
+# The score kernel's code and the constants it is built from: a change to
 # any of them voids the committed counter summary.
-SCORE_SRCS = [os.path.join(CSRC, f) for f in ("fm_score.hip", "fm_score_common.h", "fm_internal.h", "fm_api.hip")]
+SCORE_SRCS = [os.path.join(CSRC, f) for f in ("fm_score.hip", "fm_score_common.h", "fm_internal.h")]
 QUERY_WEIGHT_BYTES = 3 * (1024 * 4096 + 1024 + 8192 * 1024 + 64 * 4096) * 4   # fp32 weights of the query branch
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_b30_n262144_pmc.txt")
 
