@@ -210,15 +210,23 @@ __device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], cons
   }
 }
 
-// Head reduction, sigmoid, ensemble and store of one tile.  wh = w / 2,
-// ub[l] = 2^-b_l.
-// With the threshold mask folded in (THR), also writes the mask of the tile
-// before (its scores in e_pend) and leaves this tile's scores in e_pend.
-template <bool MEAN, bool PER_LAYER, bool THR>
+// Head reduction, sigmoid, ensemble and store of one tile, in the phase
+// P = (tile + 1) mod 8.  wh = w / 2, ub[l] = 2^-b_l.
+//
+// Scores only (no per-layer output): tile_rows of the tile goes to
+// x[tile mod 4], and the phase that finishes the last tile of an aligned
+// group of four (P = 4 and 0) reduces, stores and, with the threshold mask
+// folded in (THR), keeps the group's scores in e_pend; the next phase writes
+// their mask (so it does not wait on this phase's chain).
+//
+// With per-layer scores: every tile is stored on its own, and with THR the
+// mask of the tile before (its scores in e_pend) is written first.
+template <bool MEAN, bool PER_LAYER, bool THR, int P>
 __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
                                             const f32x4 (&wh)[kLayers][4], const float (&ub)[kLayers], float s,
-                                            int tile, float& e_pend) {
-  if (THR) threshold_tile(cx, e_pend, tile - 1);
+                                            int tile, float& e_pend, float (&x)[4]) {
+  if (THR && PER_LAYER) threshold_tile(cx, e_pend, tile - 1);
+  if (THR && !PER_LAYER && (P == 1 || P == 5)) threshold_group(cx, e_pend, tile - 4);
   float t[kLayers];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -231,8 +239,17 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
     // add the three parts of the linear term, group 3 holds zero there.
     t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  const float e = store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
-  if (THR) e_pend = e;
+  if constexpr (PER_LAYER) {
+    const float e = store_tile<MEAN, true>(cx, t, fabsf(s), tile);
+    if (THR) e_pend = e;
+  } else {
+    x[(P + 7) & 3] = tile_rows<MEAN>(t, fabsf(s));
+    if (P == 0 || P == 4) {
+      const float e = group_scores<MEAN>(cx, x);
+      store_group(cx, e, tile - 3);
+      if (THR) e_pend = e;
+    }
+  }
 }
 
 // Instruction order of one phase for the scheduler: the fp8 MFMA (32
@@ -337,7 +354,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   f16x8 kf[2][4];
   f32x4 acc[2][kLayers][4];
   f32x4 lin[2];
-  float e_pend = 0.f;  // scores of the tile whose threshold mask is still to be written
+  float e_pend = 0.f;  // scores of the tile or group whose threshold mask is still to be written
+  float x[4] = {0.f, 0.f, 0.f, 0.f};  // tile_rows of the open group's tiles
 
   // Phase of tile i, P = i mod 8 (compile-time, so every register index is
   // static): MFMAs of tile i; finish tile i-1 (its scale still in its ring
@@ -346,8 +364,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 #define FM_PHASE(P, I)                                                                                \
   {                                                                                                   \
     mfma_tile(qf, qlin, ring[(P) & 7], kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                     \
-    finish_tile<MEAN, PER_LAYER, THR>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,             \
-                                            ring[((P) + 7) & 7].s, (I) - 1, e_pend);                  \
+    finish_tile<MEAN, PER_LAYER, THR, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,          \
+                                         ring[((P) + 7) & 7].s, (I) - 1, e_pend, x);                  \
     decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
     interleave_phase();                                                                               \
@@ -374,8 +392,16 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
     FM_PHASE(0, i + 7)
     i += 8;
   } while (i < tiles);
-  finish_tile<MEAN, PER_LAYER, THR>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, e_pend);  // tile i - 1 = 0 mod 8
-  if (THR) threshold_tile(cx, e_pend, i - 1);
+  // Tile i - 1 (0 mod 8); with scores only, it opens a group whose other
+  // tiles are past the run (their stale rows in x go to dropped slots).
+  finish_tile<MEAN, PER_LAYER, THR, 1>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, e_pend, x);
+  if constexpr (PER_LAYER) {
+    if (THR) threshold_tile(cx, e_pend, i - 1);
+  } else {
+    const float e = group_scores<MEAN>(cx, x);
+    store_group(cx, e, i - 1);
+    if (THR) threshold_group(cx, e, i - 1);
+  }
 #undef FM_PHASE
 }
 

@@ -54,19 +54,39 @@ __device__ __forceinline__ float sum4rows(float v) {
   swap16(v, w);
   return v + w;
 }
-// max(a, b) as the median of (a, b, +inf): one instruction, with no
-// quieting of the lane-swapped operands (NaN scores are not ordered).
-__device__ __forceinline__ float max2(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, __builtin_huge_valf());
+// max(a, b) as the median of (a, b, pinf) with pinf = +inf held in a
+// register the compiler cannot see into: one instruction.  (With a literal
+// +inf the compiler rewrites the median as a maximum and quiets both
+// operands first, two more instructions; the scores are never NaN.)
+__device__ __forceinline__ float max2(float a, float b, float pinf) {
+  return __builtin_amdgcn_fmed3f(a, b, pinf);
 }
-__device__ __forceinline__ float max4rows(float v) {
+__device__ __forceinline__ float max4rows(float v, float pinf) {
   float w = v;
   swap32(v, w);
-  v = max2(v, w);
+  v = max2(v, w, pinf);
   w = v;
   swap16(v, w);
-  return max2(v, w);
+  return max2(v, w, pinf);
 }
+
+// Sum (SUM) or maximum over the four 16-lane rows of four tiles at once:
+// lane row g of the result holds the reduction of x_k with k = kGroupTile[g]
+// (rows 1 and 2 trade places), each lane's column c staying chunk c.  Two
+// 32-lane swaps pair rows {0, 2} and {1, 3} of x0 with x1 and of x2 with x3,
+// one 16-lane swap then pairs the halves: 3 swaps and 3 operations for four
+// tiles, where one tile alone takes 2 swaps, 2 moves and 2 operations.  The
+// sums associate as sum4rows' do, (r0 + r2) + (r1 + r3).
+template <bool SUM>
+__device__ __forceinline__ float reduce4(float x0, float x1, float x2, float x3, float pinf) {
+  swap32(x0, x1);
+  swap32(x2, x3);
+  float a = SUM ? x0 + x1 : max2(x0, x1, pinf);
+  float b = SUM ? x2 + x3 : max2(x2, x3, pinf);
+  swap16(a, b);
+  return SUM ? a + b : max2(a, b, pinf);
+}
+constexpr int kGroupTile[4] = {0, 2, 1, 3};
 
 // The three layers' logits of every chunk from the lanes' partial sums:
 // u[l] is lane group g's part of layer l for the lane's chunk (l % 16).
@@ -118,6 +138,13 @@ struct Ctx {
   uint32_t lane_mask_off;                // 4 l in lanes l = 0..3 (one word of 4 mask bytes each), out of range elsewhere
   uint32_t nib_shift;                    // 4 (l % 4): lane l's four chunks in the tile's compare mask
   float threshold;
+  // Four-tile groups (scores only): lane l stores chunk c of tile
+  // kGroupTile[g] of the group, i.e. group chunk 16 kGroupTile[g] + c; the
+  // group's mask goes out as 16 words from lanes 0..15.
+  uint32_t lane_grp_off;                 // 4 (16 kGroupTile[g] + c)
+  int32_t grp_chunk;                     // 16 kGroupTile[g] + c
+  uint32_t lane_grp_mask_off;            // 4 c in lane row 0, out of range elsewhere
+  float pinf;                            // +inf, opaque to the compiler (max2)
 };
 
 // Buffer views of one pipeline run: chunks [start, start + count) of row b.
@@ -148,6 +175,14 @@ __device__ __forceinline__ Ctx make_ctx(const uint8_t* comp_k, int B, int64_t N,
     cx.mask_words = (int32_t)(words < row_words ? words : row_words);
   }
   cx.threshold = 0.f;
+  cx.grp_chunk = 16 * kGroupTile[cx.g] + cx.c;
+  cx.lane_grp_off = (uint32_t)(4 * cx.grp_chunk);
+  cx.lane_grp_mask_off = cx.g == 0 ? (uint32_t)(4 * cx.c) : kDropOffset;
+  {
+    float inf = __builtin_huge_valf();
+    asm volatile("" : "+s"(inf));
+    cx.pinf = inf;
+  }
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
     cx.lane_pl_off[l] = cx.g == kLayerRow[l] ? (uint32_t)(cx.c * 4) : kDropOffset;
@@ -203,7 +238,7 @@ __device__ __forceinline__ float store_tile(const Ctx& cx, const float (&u)[kLay
     // Row 3 holds 0 for the mean (its sigmoid, 1/2, is taken back out of
     // the sum) and layer 2 again for the max.
     const float sl = sigmoid(as * layer_totals(u, MEAN));
-    e = MEAN ? (sum4rows(sl) - 0.5f) * (1.0f / 3.0f) : max4rows(sl);
+    e = MEAN ? (sum4rows(sl) - 0.5f) * (1.0f / 3.0f) : max4rows(sl, cx.pinf);
     if (PER_LAYER) {
 #pragma unroll
       for (int l = 0; l < kLayers; ++l)
@@ -211,10 +246,45 @@ __device__ __forceinline__ float store_tile(const Ctx& cx, const float (&u)[kLay
                                               cx.lane_pl_off[l], 0, 0);
     }
   } else {
-    e = sigmoid(as * max4rows(layer_totals(u, false)));
+    e = sigmoid(as * max4rows(layer_totals(u, false), cx.pinf));
   }
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), tile_rsrc(cx.out, cx.out_bytes, to), cx.lane_out_off, 0, 0);
   return e;
+}
+
+// Four-tile groups of the scores-only outputs (the maximum and mean
+// ensembles without per-layer scores).  Per tile, tile_rows gives each lane
+// row's layer total times |s|, or for the mean its sigmoid (lane row 3 holds
+// layer 2 again for the maximum, 0 for the mean); per group, group_scores
+// reduces the rows of the four tiles together and takes one sigmoid for the
+// maximum (|s| >= 0, so max_l |s| T_l = |s| max_l T_l, rounding included).
+template <bool MEAN>
+__device__ __forceinline__ float tile_rows(const float (&u)[kLayers], float as) {
+  const float x = as * layer_totals(u, MEAN);
+  return MEAN ? sigmoid(x) : x;
+}
+template <bool MEAN>
+__device__ __forceinline__ float group_scores(const Ctx& cx, const float (&x)[4]) {
+  const float r = reduce4<MEAN>(x[0], x[1], x[2], x[3], cx.pinf);
+  return MEAN ? (r - 0.5f) * (1.0f / 3.0f) : sigmoid(r);
+}
+// Scores of the group of tiles tile0 .. tile0 + 3: one 256-byte store.
+__device__ __forceinline__ void store_group(const Ctx& cx, float e, int tile0) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), tile_rsrc(cx.out, cx.out_bytes, tile0 * (kTile * 4)),
+                                        cx.lane_grp_off, 0, 0);
+}
+// Threshold mask of the group of tiles tile0 .. tile0 + 3 (64 bytes, 16
+// words from lanes 0..15); a group before the run's first tile (tile0 < 0)
+// writes nothing.  Ballot bit 16 g + c is group chunk 16 kGroupTile[g] + c:
+// trading the middle two 16-bit fields puts the bits in chunk order, and
+// lane c spreads bits 4c .. 4c + 3 to the bytes of its word.
+__device__ __forceinline__ void threshold_group(const Ctx& cx, float e, int tile0) {
+  const int32_t n0 = tile0 * kTile;
+  uint64_t keep = __ballot(e > cx.threshold && n0 + cx.grp_chunk < cx.count);
+  keep = (keep & 0xffff00000000ffffull) | ((keep >> 16) & 0xffff0000ull) | ((keep << 16) & 0xffff00000000ull);
+  const uint32_t nib = (uint32_t)(keep >> (4 * cx.c)) & 0xfu;
+  const uint32_t word = (nib * 0x204081u) & 0x01010101u;  // bit k -> byte k (a 24-bit multiply)
+  __builtin_amdgcn_raw_buffer_store_b32(word, tile_rsrc(cx.mask, cx.mask_words, n0), cx.lane_grp_mask_off, 0, 0);
 }
 
 // The persistent grid's work split: the valid tiles of all rows, in
