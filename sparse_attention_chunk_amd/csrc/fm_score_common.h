@@ -199,11 +199,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
                                            kBufferWord3);
 }
 
+// Records of tile `tile` (>= 0) of the run.  The descriptor spans the whole
+// run and the tile's byte offset goes in the scalar offset: on gfx950 a lane
+// is in range when vector offset + scalar offset < size (checked on the GPU
+// with in-bounds loads), so lanes past the run's end read zeros exactly as
+// with a descriptor starting at the tile, and per tile only the offset
+// changes (one scalar add, no new base address).
 __device__ __forceinline__ void load_tile(const Ctx& cx, int tile, RawTile& t) {
-  const __amdgpu_buffer_rsrc_t r = tile_rsrc(cx.rec, cx.rec_bytes, tile * kTileBytes);
-  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off, 0, 0));
-  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off + 16, 0, 0));
-  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, cx.lane_scale_off, 0, 0));
+  const int32_t from = tile * kTileBytes;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cx.rec, 0, cx.rec_bytes, kBufferWord3);
+  t.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off, from, 0));
+  t.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, cx.lane_rec_off + 16, from, 0));
+  t.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, cx.lane_scale_off, from, 0));
 }
 
 // Threshold mode folded into the score pass: the tile's 16 mask bytes,
@@ -268,10 +275,13 @@ __device__ __forceinline__ float group_scores(const Ctx& cx, const float (&x)[4]
   const float r = reduce4<MEAN>(x[0], x[1], x[2], x[3], cx.pinf);
   return MEAN ? (r - 0.5f) * (1.0f / 3.0f) : sigmoid(r);
 }
-// Scores of the group of tiles tile0 .. tile0 + 3: one 256-byte store.
+// Scores of the group of tiles tile0 .. tile0 + 3 (tile0 >= 0): one
+// 256-byte store, addressed like load_tile's records (the run's descriptor,
+// the group's offset in the scalar offset; stores past the run are dropped).
 __device__ __forceinline__ void store_group(const Ctx& cx, float e, int tile0) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), tile_rsrc(cx.out, cx.out_bytes, tile0 * (kTile * 4)),
-                                        cx.lane_grp_off, 0, 0);
+  const int32_t from = tile0 * (kTile * 4);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cx.out, 0, cx.out_bytes, kBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), r, cx.lane_grp_off, from, 0);
 }
 // Threshold mask of the group of tiles tile0 .. tile0 + 3 (64 bytes, 16
 // words from lanes 0..15); a group before the run's first tile (tile0 < 0)
@@ -280,11 +290,15 @@ __device__ __forceinline__ void store_group(const Ctx& cx, float e, int tile0) {
 // lane c spreads bits 4c .. 4c + 3 to the bytes of its word.
 __device__ __forceinline__ void threshold_group(const Ctx& cx, float e, int tile0) {
   const int32_t n0 = tile0 * kTile;
+  // The run's mask descriptor with the group's offset in the scalar offset
+  // (as in load_tile); empty for a group before the run.
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cx.mask, 0, n0 < 0 ? 0 : cx.mask_words, kBufferWord3);
   uint64_t keep = __ballot(e > cx.threshold && n0 + cx.grp_chunk < cx.count);
   keep = (keep & 0xffff00000000ffffull) | ((keep >> 16) & 0xffff0000ull) | ((keep << 16) & 0xffff00000000ull);
   const uint32_t nib = (uint32_t)(keep >> (4 * cx.c)) & 0xfu;
   const uint32_t word = (nib * 0x204081u) & 0x01010101u;  // bit k -> byte k (a 24-bit multiply)
-  __builtin_amdgcn_raw_buffer_store_b32(word, tile_rsrc(cx.mask, cx.mask_words, n0), cx.lane_grp_mask_off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(word, r, cx.lane_grp_mask_off, n0 < 0 ? 0 : n0, 0);
 }
 
 // The persistent grid's work split: the valid tiles of all rows, in

@@ -202,12 +202,15 @@ __device__ __forceinline__ void mfma_tile8(const i32x8 (&qh)[kLayers][4], const 
     for (int mt = 0; mt < 4; ++mt) acc[l][mt] = mfma8(ql[l][mt], k, acc[l][mt]);
 }
 
-// Head reduction, sigmoid, ensemble and store of one tile.  wv = w 2^-a / 2
-// of this lane's heads; ub[l] = 2^-b_l.
-template <bool MEAN, bool PER_LAYER>
+// Head reduction, sigmoid, ensemble and store of one tile, in the phase
+// P = (tile + 1) mod 8.  wv = w 2^-a / 2 of this lane's heads; ub[l] =
+// 2^-b_l.  Scores only: in four-tile groups, as in the f16 kernel (the
+// phases P = 4 and 0 reduce and store the group); with per-layer scores,
+// every tile on its own.
+template <bool MEAN, bool PER_LAYER, int P>
 __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
                                              const f32x4 (&wv)[kLayers][4], const float (&ub)[kLayers], float s,
-                                             int tile) {
+                                             int tile, float (&x)[4]) {
   float t[kLayers];
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
@@ -220,7 +223,12 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
     // add the three parts of the linear term, group 3 holds zero there.
     t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
-  (void)store_tile<MEAN, PER_LAYER>(cx, t, fabsf(s), tile);
+  if constexpr (PER_LAYER) {
+    (void)store_tile<MEAN, true>(cx, t, fabsf(s), tile);
+  } else {
+    x[(P + 7) & 3] = tile_rows<MEAN>(t, fabsf(s));
+    if (P == 0 || P == 4) store_group(cx, group_scores<MEAN>(cx, x), tile - 3);
+  }
 }
 
 // Instruction order of one phase: every MFMA followed by up to four
@@ -306,6 +314,7 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
 
   f32x4 acc[2][kLayers][4];
   f32x4 lin[2];
+  float x[4] = {0.f, 0.f, 0.f, 0.f};  // tile_rows of the open group's tiles
 
   // Phase of tile i, P = i mod 8: MFMAs of tile i from its ring slot; finish
   // tile i-1 (its scale still in its slot); request tile i+6 into the slot of
@@ -313,8 +322,8 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
 #define FM_PHASE8(P, I)                                                                                   \
   {                                                                                                       \
     mfma_tile8(qh, ql, qlin, tile_codes(ring[(P) & 7]), acc[(P) & 1], lin[(P) & 1]);                      \
-    finish_tile8<MEAN, PER_LAYER>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub, ring[((P) + 7) & 7].s, \
-                                  (I) - 1);                                                               \
+    finish_tile8<MEAN, PER_LAYER, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,                 \
+                                     ring[((P) + 7) & 7].s, (I) - 1, x);                                  \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                     \
     interleave_phase8();                                                                                  \
   }
@@ -336,7 +345,10 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
     FM_PHASE8(0, i + 7)
     i += 8;
   } while (i < tiles);
-  finish_tile8<MEAN, PER_LAYER>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1);
+  // Tile i - 1 (0 mod 8); with scores only, it opens a group whose other
+  // tiles are past the run.
+  finish_tile8<MEAN, PER_LAYER, 1>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, x);
+  if constexpr (!PER_LAYER) store_group(cx, group_scores<MEAN>(cx, x), i - 1);
 #undef FM_PHASE8
 }
 
