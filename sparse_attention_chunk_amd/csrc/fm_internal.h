@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "fm.h"
+#include "fm_index.h"
 
 namespace fm {
 
@@ -68,10 +69,9 @@ constexpr int kSubFastCap = 32768;
 constexpr int kResSlice = 4096;
 
 // Top-K selection: the scan kernel writes a 64-bit word per tile of 16 or
-// more chunks (histogram bins and positions of its largest scores); rows of
-// tile words are ceil(N / 16) rounded up to a multiple of 2 long (16-byte
-// aligned rows).
-inline __host__ __device__ int64_t tile_info_stride(int64_t N) { return ((N + 15) / 16 + 1) & ~(int64_t)1; }
+// more chunks (histogram bins and positions of its largest scores), in rows
+// of tile_info_stride(N) words (fm_index.h).
+using idx::tile_info_stride;
 
 struct Workspace {
   // Weights packed at context creation: each row scaled by a power of two

@@ -468,14 +468,9 @@ __global__ __launch_bounds__(1024) void score_plan_kernel(const int32_t* __restr
   const int64_t total = s_pre[B];
   for (int r = t; r <= B; r += 1024) row_tiles[r] = s_pre[r];
   for (int g = t; g < waves; g += 1024) {
-    const int64_t first = (int64_t)g * total / waves;
-    int lo = 0, hi = B - 1;  // largest row with s_pre[row] <= first
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= first) lo = mid;
-      else hi = mid - 1;
-    }
-    wave_row[g] = lo;
+    int64_t first, end;
+    idx::wave_share(g, waves, total, &first, &end);
+    wave_row[g] = idx::plan_row_of(s_pre, B, first);
   }
 }
 

@@ -19,16 +19,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kTile = 16;                        // chunks per MFMA column tile
+constexpr int kTile = idx::kTile;                // chunks per MFMA column tile
 constexpr int kTileBytes = kTile * kRecord;      // 2112
-constexpr int64_t kMaxSegTiles = 1 << 16;        // tiles per pipeline run: buffer offsets stay below 2^31
 constexpr int kRing = 8;                         // register ring of record tiles
 constexpr int kAhead = 6;                        // tile i + 6 is requested in the phase of tile i
-
-// An offset past every buffer of one pipeline run (they hold at most
-// 16 kMaxSegTiles + 8 tiles of records): the store is dropped by the range
-// check, with no branch.
+// A lane offset past every buffer of one pipeline run: the access is
+// dropped by the range check, with no branch.
 constexpr uint32_t kDropOffset = 0x40000000u;
+// A run of at most idx::kMaxSegTiles tiles addresses tiles below
+// kMaxSegTiles + 16 (the loop's rounding up to 8 m + 1 tiles, kAhead tiles
+// requested ahead, the last group of four), so every tile offset (the
+// scalar offset of a load or store) stays below 2^28: a run's buffers are
+// smaller than kDropOffset, and kDropOffset plus a tile offset does not
+// wrap around 2^32.
+static_assert((idx::kMaxSegTiles + 16) * (int64_t)kTileBytes < (1 << 28), "tile offsets reach 2^28");
 
 // Cross-lane moves.  permlane32_swap(x, y) swaps lanes 32..63 of x with
 // lanes 0..31 of y; permlane16_swap(x, y) swaps the odd 16-lane rows of x
@@ -165,15 +169,9 @@ __device__ __forceinline__ Ctx make_ctx(const uint8_t* comp_k, int B, int64_t N,
   cx.mask = nullptr;
   cx.lane_mask_off = lane < 4 ? (uint32_t)(4 * lane) : kDropOffset;
   cx.nib_shift = 4u * (uint32_t)(lane & 3);
-  {
-    // Words up to the run's last chunk rounded up to a word, but never past
-    // the row's last whole word (bytes beyond a row's valid chunks are zero
-    // in the mask, so a word may cover them; the row's last N % 4 bytes are
-    // written by a separate kernel after the pass).
-    const int64_t words = (count + 3) & ~(int64_t)3;
-    const int64_t row_words = (N - start) & ~(int64_t)3;
-    cx.mask_words = (int32_t)(words < row_words ? words : row_words);
-  }
+  // Bytes beyond a row's valid chunks are zero in the mask, so a word may
+  // cover them.
+  cx.mask_words = (int32_t)idx::run_mask_words(start, count, N);
   cx.threshold = 0.f;
   cx.grp_chunk = 16 * kGroupTile[cx.g] + cx.c;
   cx.lane_grp_off = (uint32_t)(4 * cx.grp_chunk);
@@ -301,54 +299,16 @@ __device__ __forceinline__ void threshold_group(const Ctx& cx, float e, int tile
   __builtin_amdgcn_raw_buffer_store_b32(word, r, cx.lane_grp_mask_off, n0 < 0 ? 0 : n0, 0);
 }
 
-// The persistent grid's work split: the valid tiles of all rows, in
-// row-major order, are cut into equal contiguous shares, one per wave (4
-// waves per block): with row_tiles (prefix of the rows' valid tile counts,
-// from the plan kernel) when rows are ragged, else every row has
-// ceil(N / 16) tiles.  A share may end in the next row (or, for short rows,
-// several rows later): each row's part is its own pipeline run,
-// run(b, start, count), at most kMaxSegTiles tiles long.
+// The persistent grid's work split (idx::walk_runs): wave 4 blockIdx.x +
+// (threadIdx.x / 64) of 4 gridDim.x waves scores its share of the tile list,
+// one pipeline run per row it touches.
 template <class Run>
 __device__ __forceinline__ void walk_share(int B, int64_t N, const int32_t* __restrict__ valid_n,
                                            const int64_t* __restrict__ row_tiles,
                                            const int32_t* __restrict__ wave_row, int64_t total_tiles, Run&& run) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps descriptors scalar
-  const int64_t waves = 4 * (int64_t)gridDim.x;
-  const int64_t gw = 4 * (int64_t)blockIdx.x + wave;
-  const int64_t total = row_tiles ? row_tiles[B] : total_tiles;
-  int64_t t = gw * total / waves;
-  const int64_t t_end = (gw + 1) * total / waves;
-  if (t >= t_end) return;
-  const int64_t row_full = (N + kTile - 1) / kTile;
-  int b;
-  int64_t first;  // list index of row b's first tile
-  if (row_tiles) {
-    b = wave_row[gw];
-    first = row_tiles[b];
-  } else {
-    b = (int)(t / row_full);
-    first = (int64_t)b * row_full;
-  }
-  while (t < t_end) {
-    const int64_t last = row_tiles ? row_tiles[b + 1] : first + row_full;
-    int64_t run_end = t_end < last ? t_end : last;
-    if (run_end - t > kMaxSegTiles) run_end = t + kMaxSegTiles;
-    if (run_end > t) {
-      int64_t vn = N;
-      if (valid_n) {
-        const int64_t v = valid_n[b];
-        vn = v < 0 ? 0 : (v > N ? N : v);
-      }
-      const int64_t start = (t - first) * kTile;
-      const int64_t end = run_end - first == last - first ? vn : (run_end - first) * kTile;
-      run(b, start, end - start);
-    }
-    t = run_end;
-    if (t >= last) {
-      ++b;
-      first = last;
-    }
-  }
+  idx::walk_runs(4 * (int64_t)blockIdx.x + wave, 4 * (int64_t)gridDim.x, B, N, valid_n, row_tiles, wave_row,
+                 total_tiles, run);
 }
 
 }  // namespace score

@@ -77,10 +77,8 @@ __device__ __forceinline__ bool key_at_least(uint32_t k, int c) {
 
 // log2 of the tile's kSub-chunk parts in a row of vn chunks (0..2): the
 // largest leaving at least 4 K tiles.
-__device__ __forceinline__ int tile_shift(int64_t vn, int32_t k) {
-  const int64_t need = 4 * (int64_t)k;
-  return (vn >> 6) >= need ? 2 : ((vn >> 5) >= need ? 1 : 0);
-}
+using idx::tile_shift;
+static_assert(kSub == idx::kSelSub, "scan part size");
 
 // Tile word: x bits 0-10 the largest key's bin, 11-16 its position in the
 // tile, 17-27 the second largest's bin; y bits 0-5 the second largest's
@@ -185,8 +183,8 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(const float* __
       for (int j = 0; j < kSub && n0 + j < vn; ++j) top3_take(a, order_key(row[n0 + j]), p0 + j);
     }
     const uint2 word = tile_word(a, s);
-    const int64_t tile = g >> s;
-    if (p0 == 0 && (tile << (4 + s)) < vn) tile_info[(size_t)b * tile_info_stride(N) + tile] = word;
+    const int64_t tile = idx::scan_tile_written(g, s, vn);
+    if (tile >= 0) tile_info[(size_t)b * tile_info_stride(N) + tile] = word;
   }
   if (n0 >= N) return;
   const uint8_t keep = keep_all ? 1 : 0;
@@ -321,7 +319,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   // zeros past it); their maxima are counted in the row's histogram.
   const int s = tile_shift(vn, top_k);
   const int lt = 4 + s;  // log2 of the tile's entries
-  const uint32_t nt = (uint32_t)((vn + (1 << lt) - 1) >> lt);
+  const uint32_t nt = (uint32_t)idx::finish_tiles(vn, s);
   const int64_t tstride = SUBSET ? kSubFastCap / kSub : tile_info_stride(N);
   const uint2* irow = tile_info + (size_t)b * tstride;
   const __amdgpu_buffer_rsrc_t ir = buffer(irow, tstride * 8);
