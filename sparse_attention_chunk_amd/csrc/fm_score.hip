@@ -52,16 +52,19 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 // of its A holds part k of u_l = 2^b_l v_l, v_l = 1/2 sum_h w_{l,h} q_{l,h}
 // (q already rounded to f16, the sum in fp32), with 2^b_l putting the
 // largest |u_l| in [128, 256): part 0 = e4m3(u), part 1 = e4m3(u - part 0),
-// part 2 = e4m3 of what remains.  Other rows are zero.  The MFMA output
-// then holds, in lane group k, part k of layer r's term in element r; the
-// parts share the scale 2^-b_l, so the cross-group sum adds them.
+// part 2 = e4m3 of what remains.  Other rows are zero.  The A operand's
+// block scales (E8M0, one per row and 32-wide block, from the lane holding
+// the block; code 127 is 1, checked on the GPU) undo 2^b_l: the rows of
+// layer l carry code 127 - b_l.  The MFMA output then holds, in lane group
+// k, part k of layer r's term in element r, already times 2^-b_l, and the
+// cross-group sum adds the parts.
 //
 // Packed row: 48 head fragments (64 lanes x 16 bytes), the linear fragment
-// (64 lanes x 32 bytes) at byte kQLinOffset, and the three 2^-b_l at byte
-// kQScaleOffset.
+// (64 lanes x 32 bytes) at byte kQLinOffset, and each lane's A block-scale
+// code (one int32 per lane) at byte kQScaleOffset.
 constexpr int kQLinOffset = kQHeadFrags * 64 * 16;
 constexpr int kQScaleOffset = kQLinOffset + 64 * 32;
-static_assert(kQScaleOffset + 16 <= kQFrags * 64 * 16, "packed query row too small");
+static_assert(kQScaleOffset + 64 * 4 <= kQFrags * 64 * 16, "packed query row too small");
 
 // 2^a with m 2^a in [128, 256) (m > 0); 0 for m = 0.
 __device__ __forceinline__ int part_exponent(float m) {
@@ -147,7 +150,15 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q
       word |= __shfl_xor(word, 2);
       if ((t & 3) == 0) lin8[k][t >> 2] = word;
     }
-    if (t == 0) ((float*)(row + kQScaleOffset))[layer] = ldexpf(1.0f, -bl);
+    // Block-scale codes of this layer's rows (rows 4k + layer, k = 0..2, in
+    // all four lane groups); the layer-0 block also writes code 127 (scale
+    // 1) for the zero rows.  2^-b_l below 2^-127 (|u_l| below 2^-119) is
+    // clamped to 2^-127.
+    const int r16 = t & 15;
+    const bool mine = r16 < 12 && (r16 & 3) == layer;
+    const bool zero_row = r16 >= 12 || (r16 & 3) == 3;
+    const int code = 127 - bl < 0 ? 0 : (127 - bl > 254 ? 254 : 127 - bl);
+    if (t < 64 && (mine || (layer == 0 && zero_row))) ((int32_t*)(row + kQScaleOffset))[t] = mine ? code : 127;
   }
   __syncthreads();
   uint4* lin_out = (uint4*)(row + kQLinOffset);
@@ -191,11 +202,13 @@ __device__ __forceinline__ i32x8 tile_codes(const RawTile& t) {
 // The 49 MFMAs of one tile: the linear term first (fp8, from the stored
 // codes), then the 48 head MFMAs in k-step order, so no MFMA waits on the
 // one before it.
-__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const i32x8& qlin, const RawTile& raw,
-                                          const f16x8 (&kf)[4], f32x4 (&acc)[kLayers][4], f32x4& lin) {
+__device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], const i32x8& qlin, int32_t qsc,
+                                          const RawTile& raw, const f16x8 (&kf)[4], f32x4 (&acc)[kLayers][4],
+                                          f32x4& lin) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  // Format code 0 (e4m3) for both operands; no block scales.
-  lin = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qlin, tile_codes(raw), zero, 0, 0, 0, 0, 0, 0);
+  // Format code 0 (e4m3) for both operands; A block scales qsc (2^-b_l),
+  // B unscaled (code 127).
+  lin = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qlin, tile_codes(raw), zero, 0, 0, 0, qsc, 0, 127);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
@@ -211,7 +224,7 @@ __device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], cons
 }
 
 // Head reduction, sigmoid, ensemble and store of one tile, in the phase
-// P = (tile + 1) mod 8.  wh = w / 2, ub[l] = 2^-b_l.
+// P = (tile + 1) mod 8.  wh = w / 2; lin is already times 2^-b_l.
 //
 // Scores only (no per-layer output): tile_rows of the tile goes to
 // x[tile mod 4], and the phase that finishes the last tile of an aligned
@@ -223,11 +236,12 @@ __device__ __forceinline__ void mfma_tile(const f16x8 (&qf)[kLayers][4][4], cons
 // mask of the tile before (its scores in e_pend) is written first.
 template <bool MEAN, bool PER_LAYER, bool THR, int P>
 __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
-                                            const f32x4 (&wh)[kLayers][4], const float (&ub)[kLayers], float s,
-                                            int tile, float& e_pend, float (&x)[4]) {
+                                            const f32x4 (&wh)[kLayers][4], float s, int tile, float& e_pend,
+                                            float (&x)[4]) {
   if (THR && PER_LAYER) threshold_tile(cx, e_pend, tile - 1);
   if (THR && !PER_LAYER && (P == 1 || P == 5)) threshold_group(cx, e_pend, tile - 4);
   float t[kLayers];
+  const float sg = __builtin_copysignf(1.0f, s);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
     float p = 0.f;
@@ -237,8 +251,12 @@ __device__ __forceinline__ void finish_tile(const Ctx& cx, const f32x4 (&acc)[kL
       for (int r = 0; r < 4; ++r) p = fmaf(fabsf(acc[l][mt][r]), wh[l][mt][r], p);
     // (s 2^-b lin + |s| p) / |s| = sign(s) 2^-b lin + p: lane groups 0..2
     // add the three parts of the linear term, group 3 holds zero there.
-    t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
+    t[l] = fmaf(sg, lin[l], p);
   }
+  // The linear term's fourth element is never read; keeping it live until
+  // here stops its register being reused right after the MFMA that writes
+  // it (a write-after-write wait on the 32-cycle MFMA).
+  asm volatile("" ::"v"(lin[3]));
   if constexpr (PER_LAYER) {
     const float e = store_tile<MEAN, true>(cx, t, fabsf(s), tile);
     if (THR) e_pend = e;
@@ -298,7 +316,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   f16x8 qf[kLayers][4][4];
   i32x8 qlin;
   f32x4 wv[kLayers][4];  // w / 2 of the heads this lane's accumulators hold: 16 mt + 4 g + r
-  float ub[kLayers];     // 2^-b_l of the linear term
+  int32_t qsc;           // the linear fragment's A block-scale code (2^-b_l)
   {
     const f16x8* qrow = qpack + (size_t)b * kQFrags * 64;
     const f16x8* qp = qrow + lane;
@@ -309,9 +327,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 #pragma unroll
         for (int t = 0; t < 4; ++t) qf[l][mt][t] = qp[((l * 4 + mt) * 4 + t) * 64];
     qlin = *((const i32x8*)((const uint8_t*)qrow + kQLinOffset) + lane);
-    const float* usc = (const float*)((const uint8_t*)qrow + kQScaleOffset);
-#pragma unroll
-    for (int l = 0; l < kLayers; ++l) ub[l] = usc[l];
+    qsc = ((const int32_t*)((const uint8_t*)qrow + kQScaleOffset))[lane];
 #pragma unroll
     for (int l = 0; l < kLayers; ++l)
 #pragma unroll
@@ -346,8 +362,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
       wv[l][mt] = 0.5f * wv[l][mt];
       asm volatile("" : "+v"(wv[l][mt]));
     }
-#pragma unroll
-  for (int l = 0; l < kLayers; ++l) asm volatile("" : "+v"(ub[l]));
+  asm volatile("" : "+v"(qsc));
 
   const int tiles = (int)((count + kTile - 1) / kTile);
 
@@ -363,8 +378,8 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   // into the slot of tile i-2, finished in the previous phase.
 #define FM_PHASE(P, I)                                                                                \
   {                                                                                                   \
-    mfma_tile(qf, qlin, ring[(P) & 7], kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                     \
-    finish_tile<MEAN, PER_LAYER, THR, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,          \
+    mfma_tile(qf, qlin, qsc, ring[(P) & 7], kf[(P) & 1], acc[(P) & 1], lin[(P) & 1]);                \
+    finish_tile<MEAN, PER_LAYER, THR, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv,              \
                                          ring[((P) + 7) & 7].s, (I) - 1, e_pend, x);                  \
     decode_tile(ring[((P) + 1) & 7], kf[((P) + 1) & 1]);                                              \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                 \
@@ -373,7 +388,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
 
   // Tile 0 (nothing to finish yet).
   decode_tile(ring[0], kf[0]);
-  mfma_tile(qf, qlin, ring[0], kf[0], acc[0], lin[0]);
+  mfma_tile(qf, qlin, qsc, ring[0], kf[0], acc[0], lin[0]);
   decode_tile(ring[1], kf[1]);
   load_tile(cx, kAhead, ring[kAhead]);
 
@@ -394,7 +409,7 @@ __device__ __forceinline__ void score_run(const f16x8* __restrict__ qpack, const
   } while (i < tiles);
   // Tile i - 1 (0 mod 8); with scores only, it opens a group whose other
   // tiles are past the run (their stale rows in x go to dropped slots).
-  finish_tile<MEAN, PER_LAYER, THR, 1>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, e_pend, x);
+  finish_tile<MEAN, PER_LAYER, THR, 1>(cx, acc[0], lin[0], wv, ring[0].s, i - 1, e_pend, x);
   if constexpr (PER_LAYER) {
     if (THR) threshold_tile(cx, e_pend, i - 1);
   } else {

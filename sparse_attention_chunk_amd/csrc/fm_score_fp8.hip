@@ -223,6 +223,7 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
     // add the three parts of the linear term, group 3 holds zero there.
     t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
   }
+  asm volatile("" ::"v"(lin[3]));  // keeps the unread element's register from reuse (as in the f16 kernel)
   if constexpr (PER_LAYER) {
     (void)store_tile<MEAN, true>(cx, t, fabsf(s), tile);
   } else {
