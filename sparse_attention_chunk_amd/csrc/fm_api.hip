@@ -195,7 +195,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kCosSin] = sizeof(float) * mb * kRopeDim;
   sizes[kQPack] = (size_t)16 * kQFrags * 64 * mb;        // f16x8 per lane
   sizes[kQPack8] = (size_t)32 * kQ8Frags * 64 * mb;      // 32 e4m3 bytes per lane
-  sizes[kW8] = sizeof(float) * kLayers * kW8Stride * mb;
+  sizes[kW8] = sizeof(float) * kW8Row * mb;
   sizes[kRowTiles] = sizeof(int64_t) * (mb + 1);
   sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
   sizes[kSubStage] = sizeof(uint32_t) * mb * kSubStageRowWords;

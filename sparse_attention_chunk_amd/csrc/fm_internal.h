@@ -40,17 +40,18 @@ inline int proj1_splits(int) { return kHidden / kSliceK; }
 // fragments (3 layers x 4 head tiles x 4 k-steps) of 64 lanes x 8 halves,
 // then one fp8 fragment (64 lanes x 32 bytes) of the per-layer weighted
 // query sums in three e4m3 parts and their three power-of-two scales; a
-// row takes kQFrags 1 KB units.
+// row takes kQFrags 1 KB units (the last holds the fp8 fragment's block-scale
+// codes).
 constexpr int kQHeadFrags = kLayers * 4 * 4;
 constexpr int kQFrags = kQHeadFrags + 3;
 // fp8 score path: per request row 24 fragments of 64 lanes x 32 e4m3 bytes
 // (3 layers x 4 head tiles x {hi, lo} parts), then one fragment of the
-// per-layer weighted query sums in three parts; per (row, layer) the halved
-// head weights with each head's query scale folded in, then the layer's
-// linear-term scale (kW8Stride floats).
+// per-layer weighted query sums in three parts; per row (kW8Row floats) the
+// halved head weights of each layer with each head's query scale folded in,
+// then the linear fragment's 64 per-lane block-scale codes (int32).
 constexpr int kQ8HeadFrags = kLayers * 4 * 2;
 constexpr int kQ8Frags = kQ8HeadFrags + 1;
-constexpr int kW8Stride = kHeads + 4;
+constexpr int kW8Row = kLayers * kHeads + 64;
 // The score kernel runs one block of 4 waves per compute unit; each wave
 // takes an equal share of the row-major list of 16-chunk tiles.
 constexpr int kMaxScoreBlocks = 1024;
@@ -90,7 +91,7 @@ struct Workspace {
   float* rope_cs = nullptr;      // [max_batch][kRopeDim / 2][2]: cos, sin of position * freq
   void* qpack = nullptr;         // [max_batch][kQFrags][64][8] fp16
   void* qpack8 = nullptr;        // [max_batch][kQ8Frags][64][32] e4m3
-  float* w8 = nullptr;           // [max_batch][3][kW8Stride]
+  float* w8 = nullptr;           // [max_batch][kW8Row]
   int64_t* row_tiles = nullptr;  // [max_batch + 1]: first tile of each row in the list of valid tiles
   int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
   int score_blocks = 0;          // compute units of the device

@@ -43,6 +43,12 @@ __device__ __forceinline__ f32x4 mfma8(const i32x8& a, const i32x8& b, const f32
   // Format codes 0 (e4m3) for both operands; no block scales.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// The linear term: A block scales sa (E8M0 code per row and 32-wide block,
+// supplied by the lane holding the block; 127 is 1), B unscaled.
+__device__ __forceinline__ f32x4 mfma8_scaled(const i32x8& a, int32_t sa, const i32x8& b) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, sa, 0, 127);
+}
 
 // Four floats -> four e4m3 bytes (round to nearest even), and back.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
@@ -68,9 +74,10 @@ __device__ __forceinline__ int part_exponent(float m) {
 // One block per (row, layer), 256 threads: thread t owns head t / 4, dims
 // 32 (t % 4) .. + 31, i.e. lane (head % 16) + 16 (t % 4) of the head tile's
 // two fragments.  Writes the hi and lo fragments, the scaled half weights
-// w8[row][layer][h] = w_h 2^-a_h / 2, then the linear-term rows of this layer
-// and w8[row][layer][64] = 2^-b.  The layer-0 block also writes the zero rows
-// of the linear-term fragment.
+// w8[row][layer 64 + h] = w_h 2^-a_h / 2, then the linear-term rows of this
+// layer and their block-scale codes 127 - b (2^-b) at w8[row][192 + lane].
+// The layer-0 block also writes the zero rows of the linear-term fragment
+// and their codes (127).
 __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ q, const float* __restrict__ w, int B,
                                                       uint4* __restrict__ qpack8, float* __restrict__ w8) {
   __shared__ float qs[kHeads][kHeadDim + 4];  // the dequantised query hi + lo
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ 
     out[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     out[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
   }
-  if (g == 0) w8[((size_t)b * kLayers + layer) * kW8Stride + h] = ldexpf(0.5f * wl[h], -a);
+  if (g == 0) w8[(size_t)b * kW8Row + layer * kHeads + h] = ldexpf(0.5f * wl[h], -a);
   __syncthreads();
 
   // v_d = 1/2 sum_h w_h q_hd over the dequantised parts, in two head halves.
@@ -161,7 +168,14 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ 
       word |= __shfl_xor(word, 2);
       if ((t & 3) == 0) lin8[k][t >> 2] = word;
     }
-    if (t == 0) w8[((size_t)b * kLayers + layer) * kW8Stride + kHeads] = ldexpf(1.0f, -bl);
+    // Block-scale codes of this layer's rows (4k + layer, k = 0..2; 2^-b
+    // below 2^-127 clamped to 2^-127), code 127 for the zero rows (layer 0).
+    const int r16 = t & 15;
+    const bool mine = r16 < 12 && (r16 & 3) == layer;
+    const bool zero_row = r16 >= 12 || (r16 & 3) == 3;
+    const int code = 127 - bl < 0 ? 0 : (127 - bl > 254 ? 254 : 127 - bl);
+    if (t < 64 && (mine || (layer == 0 && zero_row)))
+      ((int32_t*)(w8 + (size_t)b * kW8Row + kLayers * kHeads))[t] = mine ? code : 127;
   }
   __syncthreads();
   uint4* lin_out = qpack8 + ((size_t)b * kQ8Frags * 64 + (size_t)kQ8HeadFrags * 64) * 2;
@@ -189,13 +203,14 @@ __device__ __forceinline__ i32x8 tile_codes(const RawTile& t) {
 // The 25 MFMAs of one tile: the hi parts of every head tile first, then the
 // linear term, then the lo parts, so no MFMA waits on the one before it.
 __device__ __forceinline__ void mfma_tile8(const i32x8 (&qh)[kLayers][4], const i32x8 (&ql)[kLayers][4],
-                                           const i32x8& qlin, const i32x8& k, f32x4 (&acc)[kLayers][4], f32x4& lin) {
+                                           const i32x8& qlin, int32_t qsc, const i32x8& k, f32x4 (&acc)[kLayers][4],
+                                           f32x4& lin) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[l][mt] = mfma8(qh[l][mt], k, zero);
-  lin = mfma8(qlin, k, zero);
+  lin = mfma8_scaled(qlin, qsc, k);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l)
 #pragma unroll
@@ -203,15 +218,15 @@ __device__ __forceinline__ void mfma_tile8(const i32x8 (&qh)[kLayers][4], const 
 }
 
 // Head reduction, sigmoid, ensemble and store of one tile, in the phase
-// P = (tile + 1) mod 8.  wv = w 2^-a / 2 of this lane's heads; ub[l] =
-// 2^-b_l.  Scores only: in four-tile groups, as in the f16 kernel (the
+// P = (tile + 1) mod 8.  wv = w 2^-a / 2 of this lane's heads; lin is
+// already times 2^-b_l (the MFMA's block scales).  Scores only: in four-tile groups, as in the f16 kernel (the
 // phases P = 4 and 0 reduce and store the group); with per-layer scores,
 // every tile on its own.
 template <bool MEAN, bool PER_LAYER, int P>
 __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[kLayers][4], const f32x4& lin,
-                                             const f32x4 (&wv)[kLayers][4], const float (&ub)[kLayers], float s,
-                                             int tile, float (&x)[4]) {
+                                             const f32x4 (&wv)[kLayers][4], float s, int tile, float (&x)[4]) {
   float t[kLayers];
+  const float sg = __builtin_copysignf(1.0f, s);
 #pragma unroll
   for (int l = 0; l < kLayers; ++l) {
     float p = 0.f;
@@ -221,7 +236,7 @@ __device__ __forceinline__ void finish_tile8(const Ctx& cx, const f32x4 (&acc)[k
       for (int r = 0; r < 4; ++r) p = fmaf(fabsf(acc[l][mt][r]), wv[l][mt][r], p);
     // (s 2^-b lin + |s| p) / |s| = sign(s) 2^-b lin + p: lane groups 0..2
     // add the three parts of the linear term, group 3 holds zero there.
-    t[l] = fmaf(__builtin_copysignf(ub[l], s), lin[l], p);
+    t[l] = fmaf(sg, lin[l], p);
   }
   asm volatile("" ::"v"(lin[3]));  // keeps the unread element's register from reuse (as in the f16 kernel)
   if constexpr (PER_LAYER) {
@@ -265,7 +280,7 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
   i32x8 qh[kLayers][4], ql[kLayers][4];
   i32x8 qlin;
   f32x4 wv[kLayers][4];
-  float ub[kLayers];
+  int32_t qsc;  // the linear fragment's A block-scale code (2^-b_l)
   {
     const i32x8* qp = qpack8 + (size_t)b * kQ8Frags * 64 + lane;
 #pragma unroll
@@ -276,13 +291,12 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
         ql[l][mt] = qp[((l * 4 + mt) * 2 + 1) * 64];
       }
     qlin = qp[kQ8HeadFrags * 64];
-    const float* wb = w8 + (size_t)b * kLayers * kW8Stride;
+    const float* wb = w8 + (size_t)b * kW8Row;
 #pragma unroll
-    for (int l = 0; l < kLayers; ++l) {
+    for (int l = 0; l < kLayers; ++l)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) wv[l][mt] = *(const f32x4*)(wb + l * kW8Stride + 16 * mt + 4 * cx.g);
-      ub[l] = wb[l * kW8Stride + kHeads];
-    }
+      for (int mt = 0; mt < 4; ++mt) wv[l][mt] = *(const f32x4*)(wb + l * kHeads + 16 * mt + 4 * cx.g);
+    qsc = ((const int32_t*)(wb + kLayers * kHeads))[lane];
   }
   // The first records are requested after the queries and weights, one tile
   // at a time in tile order: the waits before the loop then cover only the
@@ -308,8 +322,8 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
   for (int l = 0; l < kLayers; ++l) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+v"(wv[l][mt]));
-    asm volatile("" : "+v"(ub[l]));
   }
+  asm volatile("" : "+v"(qsc));
 
   const int tiles = (int)((count + kTile - 1) / kTile);
 
@@ -322,14 +336,14 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
   // tile i-2, finished in the previous phase.
 #define FM_PHASE8(P, I)                                                                                   \
   {                                                                                                       \
-    mfma_tile8(qh, ql, qlin, tile_codes(ring[(P) & 7]), acc[(P) & 1], lin[(P) & 1]);                      \
-    finish_tile8<MEAN, PER_LAYER, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv, ub,                 \
+    mfma_tile8(qh, ql, qlin, qsc, tile_codes(ring[(P) & 7]), acc[(P) & 1], lin[(P) & 1]);                      \
+    finish_tile8<MEAN, PER_LAYER, P>(cx, acc[((P) + 1) & 1], lin[((P) + 1) & 1], wv,                     \
                                      ring[((P) + 7) & 7].s, (I) - 1, x);                                  \
     load_tile(cx, (I) + kAhead, ring[((P) + 6) & 7]);                                                     \
     interleave_phase8();                                                                                  \
   }
 
-  mfma_tile8(qh, ql, qlin, tile_codes(ring[0]), acc[0], lin[0]);
+  mfma_tile8(qh, ql, qlin, qsc, tile_codes(ring[0]), acc[0], lin[0]);
   load_tile(cx, kAhead, ring[kAhead]);
 
   // Tiles 1 .. 8 m, eight per iteration, branch-free (tiles past the last
@@ -348,7 +362,7 @@ __device__ __forceinline__ void score_run8(const i32x8* __restrict__ qpack8, con
   } while (i < tiles);
   // Tile i - 1 (0 mod 8); with scores only, it opens a group whose other
   // tiles are past the run.
-  finish_tile8<MEAN, PER_LAYER, 1>(cx, acc[0], lin[0], wv, ub, ring[0].s, i - 1, x);
+  finish_tile8<MEAN, PER_LAYER, 1>(cx, acc[0], lin[0], wv, ring[0].s, i - 1, x);
   if constexpr (!PER_LAYER) store_group(cx, group_scores<MEAN>(cx, x), i - 1);
 #undef FM_PHASE8
 }
