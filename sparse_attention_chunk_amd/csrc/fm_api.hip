@@ -179,7 +179,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   }
   enum {
     kW1, kW1Inv, kW2, kW2Inv, kGain, kPart1, kAHatHi, kAHatLo, kAHatInv, kFreq, kCosSin, kQPack, kQPack8, kW8, kRowTiles, kWaveRow,
-    kSubStage, kSubKeys, kSubTiles, kResCount, kResBits, kTileInfo, kNumBuffers
+    kSubKeys, kSubTiles, kResCount, kResBits, kTileInfo, kNumBuffers
   };
   size_t sizes[kNumBuffers];
   sizes[kW1] = (size_t)4 * kLayers * kProj1Out * kHidden;  // two f16 parts per weight
@@ -198,7 +198,6 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   sizes[kW8] = sizeof(float) * kW8Row * mb;
   sizes[kRowTiles] = sizeof(int64_t) * (mb + 1);
   sizes[kWaveRow] = sizeof(int32_t) * 4 * (size_t)cus;
-  sizes[kSubStage] = sizeof(uint32_t) * mb * kSubStageRowWords;
   sizes[kSubKeys] = sizeof(uint32_t) * mb * kSubFastCap;
   sizes[kSubTiles] = sizeof(uint2) * mb * (kSubFastCap / 16);
   sizes[kResCount] = 3 * sizeof(uint32_t) * mb * (size_t)((max_n + kResSlice - 1) / kResSlice);
@@ -240,7 +239,6 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   ctx->ws.row_tiles = (int64_t*)(p + offs[kRowTiles]);
   ctx->ws.wave_row = (int32_t*)(p + offs[kWaveRow]);
   ctx->ws.score_blocks = cus;
-  ctx->ws.sub_stage = (uint32_t*)(p + offs[kSubStage]);
   ctx->ws.sub_keys = (uint32_t*)(p + offs[kSubKeys]);
   ctx->ws.sub_tiles = (uint2*)(p + offs[kSubTiles]);
   ctx->ws.res_count = (uint32_t*)(p + offs[kResCount]);
@@ -250,7 +248,6 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* weights, int32_t max
   double freq[kRopeDim / 2];
   rope_frequencies(*cfg, freq);
   e = hipMemcpy(ctx->ws.rope_freq, freq, sizeof(freq), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = init_select_topk_subset();
   if (e == hipSuccess) e = launch_pack_weights(*weights, ctx->ws, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {

@@ -59,11 +59,9 @@ constexpr int kMaxScoreBlocks = 1024;
 // Histogram bins of the exact selections.
 constexpr int kSelBins = 2048;
 
-// Subset top-K: words staged per row for a list's gathered keys (32 rounds
-// of 1024 keys, then 32 validity words per round) on the long-list path;
-// lists of up to kSubFastCap entries take the scan + finish path, with the
-// keys and tile words in their own buffers.
-constexpr size_t kSubStageRowWords = 32 * 1024 + 32 * 32;
+// Subset top-K: lists of up to kSubFastCap entries take the scan + finish
+// path, with their keys and tile words in workspace buffers; longer lists
+// are selected by one block per row that gathers the keys in every pass.
 constexpr int kSubFastCap = 32768;
 
 // Resident-set compaction: a block covers kResSlice chunks of one row.
@@ -95,7 +93,6 @@ struct Workspace {
   int64_t* row_tiles = nullptr;  // [max_batch + 1]: first tile of each row in the list of valid tiles
   int32_t* wave_row = nullptr;   // [4 * score_blocks]: row holding each wave's first tile
   int score_blocks = 0;          // compute units of the device
-  uint32_t* sub_stage = nullptr; // [max_batch][kSubStageRowWords]: the subset top-K's gathered keys
   uint32_t* sub_keys = nullptr;  // [max_batch][kSubFastCap]: keys of the list positions (scan + finish path)
   uint2* sub_tiles = nullptr;    // [max_batch][kSubFastCap / 16]: their tile words
   uint32_t* res_count = nullptr; // [max_batch][ceil(max_n / kResSlice)][3]: set sizes per slice
@@ -134,9 +131,8 @@ hipError_t launch_score_threshold(const Workspace& ws, const float* q, const flo
                                   int64_t N, const int32_t* valid_n, int mode, float threshold, float* scores,
                                   uint8_t* mask, float* per_layer, hipStream_t stream);
 
-// Subset top-K: init raises the LDS limit of the in-LDS variant (once, at
-// context creation).
-hipError_t init_select_topk_subset();
+// Subset top-K: the scan + finish path (cap <= kSubFastCap) and the entry
+// that picks it or the long-list path.
 hipError_t launch_select_topk_subset_fast(const Workspace& ws, const float* scores, int B, int64_t N,
                                           const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                           int32_t* out, int32_t* n_out, hipStream_t stream);

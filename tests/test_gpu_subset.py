@@ -79,7 +79,7 @@ def test_random_subsets_exact(retr, B, N, cap, order, bad):
 
 
 @pytest.mark.parametrize("levels,k", [(4, 512), (64, 512), (100000, 7000), (3, 20000)])
-def test_sampled_cutoff_paths(retr, levels, k):
+def test_heavy_ties_fall_back_to_whole_list_selection(retr, levels, k):
     """Lists of up to 32768 entries take the tile scan + finish; heavy ties
     at the cut-off (few distinct scores) overflow its candidate lists and
     fall back to a radix selection over the whole list.  Both must give the
@@ -92,7 +92,7 @@ def test_sampled_cutoff_paths(retr, levels, k):
     check(retr, scores, subset, n_sub, k)
 
 
-def test_small_context_gathers_in_the_selecting_block():
+def test_small_context_lists_longer_than_the_row():
     """A small context (max_n 8192) with lists longer than N, padded with
     out-of-range entries, in list order and shuffled."""
     import sparse_attention_chunk_amd as fm
