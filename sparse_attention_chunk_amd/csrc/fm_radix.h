@@ -126,11 +126,7 @@ __device__ __forceinline__ void clear_bins(uint32_t* h) {
 // into a few bins of the first pass and serialise its LDS atomics.  The
 // index passes cover the low idx_bits bits and run only when some key equal
 // to T is left out.
-//
-// Without WITH_INDEX (a cut-off, not a selection) at most two digit passes
-// run and T is the lowest key of the bin reached: a lower bound of the k-th
-// largest key, so at least k keys are >= T.
-template <int THREADS, bool WITH_INDEX = true, typename Each>
+template <int THREADS, typename Each>
 __device__ void radix_select(Each each, uint32_t k, int idx_bits, uint32_t* h, uint32_t* s_wtot, uint32_t* s_out,
                              uint32_t* T_out, uint32_t* last_out) {
   __shared__ uint32_t s_mm[3 * (THREADS / 64)];
@@ -166,11 +162,9 @@ __device__ void radix_select(Each each, uint32_t k, int idx_bits, uint32_t* h, u
   uint64_t prefix = (uint64_t)kmax >> lo;
   uint32_t n_eq = cnt;  // keys equal to the prefix so far
   int buf = 0;
-  int passes = 0;
   clear_bins<THREADS>(h);
   __syncthreads();
-  while (lo > 0 && (WITH_INDEX || passes < 2)) {
-    ++passes;
+  while (lo > 0) {
     const int w = lo >= 11 ? 11 : lo;
     const int shift = lo - w;
     const int nb = 1 << w;
@@ -186,10 +180,6 @@ __device__ void radix_select(Each each, uint32_t k, int idx_bits, uint32_t* h, u
     n_eq = s_out[2];
     lo = shift;
     buf ^= 1;
-  }
-  if (!WITH_INDEX) {
-    *T_out = (uint32_t)(prefix << lo);  // lowest key of the bin reached
-    return;
   }
   const uint32_t T = (uint32_t)prefix;  // k = keys equal to T still to keep (>= 1)
   *T_out = T;
