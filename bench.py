@@ -49,7 +49,7 @@ PEAK_FP8_TFLOPS = 5000.0               # MI355X dense fp8 MFMA
 CSRC = os.path.join(ROOT, "sparse_attention_chunk_amd", "csrc")
 # The score kernel's code and the constants it is built from: a change to
 # any of them voids the committed counter summary.
-SCORE_SRCS = [os.path.join(CSRC, f) for f in ("fm_score.hip", "fm_score_common.h", "fm_internal.h")]
+SCORE_SRCS = [os.path.join(CSRC, f) for f in ("fm_score.hip", "fm_score_common.h", "fm_internal.h", "fm_index.h")]
 QUERY_WEIGHT_BYTES = 3 * (1024 * 4096 + 1024 + 8192 * 1024 + 64 * 4096) * 4   # fp32 weights of the query branch
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_b30_n262144_pmc.txt")
 
@@ -59,8 +59,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # The chip takes a few tens of steps after idle to reach its steady clock
-    # under this load: five warmup steps time the ramp (about 415 us per step
-    # instead of 370 us).
+    # under this load (five warmup steps alone would time that ramp); the
+    # settle phase after the warmup covers it whatever W is.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--settle-seconds", type=float, default=1.5,
                     help="untimed back-to-back steps after the warmup until this much load has run")

@@ -42,7 +42,7 @@ def test_traffic_summary_tied_to_the_score_source(tmp_path):
 
 def test_source_digest_covers_the_shared_score_headers():
     names = [os.path.basename(p) for p in bench.SCORE_SRCS]
-    assert {"fm_score.hip", "fm_score_common.h", "fm_internal.h"} <= set(names)
+    assert {"fm_score.hip", "fm_score_common.h", "fm_internal.h", "fm_index.h"} <= set(names)
 
 
 def test_cpu_baseline_reports_the_oracle():
