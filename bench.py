@@ -72,12 +72,22 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank lines (a comment edit does
+    not change the compiled kernel, so it does not void the counters)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest() -> str:
-    """SHA-256 over the score kernel's sources, in a fixed order."""
+    """SHA-256 over the score kernel's sources (code only), in a fixed order."""
     h = hashlib.sha256()
     for path in SCORE_SRCS:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -1,8 +1,9 @@
 // Parts shared by the two score kernels (the f16-MFMA path in fm_score.hip
 // and the fp8-MFMA path in fm_score_fp8.hip): record tiles and their loads,
 // the per-lane buffer views of one pipeline run, the cross-lane head sum, the
-// ensemble and store of a tile's scores, and the walk of a wave's share of
-// the tile list.
+// ensemble and store of a tile's scores (per tile, or per group of four
+// tiles), the threshold mask, and the walk of a wave's share of the tile
+// list.
 //
 // Both paths put the keys in the MFMA's B operand: lane l holds chunk l % 16
 // of a 16-chunk tile and the 32 code bytes at dims 32 (l / 16) .. + 31, and
@@ -121,10 +122,11 @@ struct RawTile {
 
 // One pipeline run's buffers: base addresses and byte counts of this
 // run's records and outputs (wave-uniform), and the lane's offsets within a
-// tile.  Each tile's buffer descriptors start at the tile (scalar
-// arithmetic) and end at the run's end, so the per-lane offsets stay fixed
-// and the range checks make reads past the run return 0 and drop writes
-// past it.
+// tile.  Record loads and group stores use one descriptor over the run with
+// the tile's offset in the scalar offset; per-tile stores use a descriptor
+// starting at the tile (tile_rsrc).  Either way the per-lane offsets stay
+// fixed and the range checks make reads past the run return 0 and drop
+// writes past it.
 struct Ctx {
   const uint8_t* rec;                    // records of this run's chunks
   float* out;                            // their scores

@@ -124,3 +124,11 @@ def test_timing_event_brackets_the_same_work_as_torch_events():
     t_hip, t_torch = a.elapsed_time(b), ta.elapsed_time(tb)
     assert 0.8 * t_torch < t_hip <= 1.05 * t_torch + 0.01, (t_hip, t_torch)
     assert float(x[-1]) == 2.0
+
+
+def test_source_digest_ignores_comments_not_code():
+    """A comment edit leaves the compiled kernel, and so the counters, as they
+    were; a code edit voids them."""
+    base = "int a = 1;  // one\n/* block\n comment */\nint b = 2;\n"
+    assert bench._code_only(base) == bench._code_only("int a = 1;  // uno\n\nint b = 2;  /* two */\n")
+    assert bench._code_only(base) != bench._code_only("int a = 1;\nint b = 3;\n")
