@@ -132,7 +132,12 @@ fm_status fm_prepare_query(fm_ctx* ctx, const float* hidden, const int64_t* posi
 
 /* Per-layer score and ensemble ("Architecture" score line, "Joint checkpoint
  * + ensemble").
- *   q, w      device fp32, as written by fm_prepare_query
+ *   q, w      device fp32, as written by fm_prepare_query; q is rounded once
+ *             to f16 for the MFMA, so its entries must stay within the f16
+ *             range (|q| <= 65504), and that rounding moves each logit by
+ *             about 2^-11 of its size: the score tolerance holds for q of the
+ *             prepared queries' size (order one, a normalised transform of
+ *             RMS-normalised projections)
  *   comp_k    device uint8 [B][N][132] ("compressed_k format"): bytes 0..127
  *             are OCP float8 e4m3fn codes, bytes 128..131 a little-endian
  *             fp32 scale; k = decode(code) * scale

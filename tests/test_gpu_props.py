@@ -1,7 +1,8 @@
 """GPU properties and edge cases through the C ABI: determinism, chunk
-permutation, row independence, ties, zero and negative-scale records,
-ragged and degenerate sizes, and the selection kernels on constructed
-scores (compared exactly with the oracle's selection of the same scores)."""
+permutation, row independence, ties, zero and negative-scale records, tiny
+and large (f16-exact) query magnitudes, ragged and degenerate sizes, and the
+selection kernels on constructed scores (compared exactly with the oracle's
+selection of the same scores)."""
 
 import numpy as np
 import pytest
@@ -153,6 +154,43 @@ def test_negative_and_mixed_scales(retr, qw):
     per_ref, ens_ref = oracle_scores(ck, q[:, :1], w[:, :1], [1000], "max")
     e = max(max_score_err(s, ens_ref), max_score_err(p, per_ref))
     report("negative scales", max_abs=e)
+    assert e <= SCORE_TOL
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_tiny_queries(retr, qw, fp8):
+    """Queries scaled by 2^-20: most f16 query entries fall in the subnormal
+    range and the linear term's block scale is far from 1.  Scores stay
+    within the tolerance of the oracle's on the same queries (near 1/2,
+    with nothing flushed to NaN or infinity)."""
+    q, w = qw
+    qs = q[:, :2] * 2.0 ** -20
+    ck = records(3000, 11, rows=2)
+    s, p = retr.score(dev(qs.astype(np.float32)), dev(w[:, :2].astype(np.float32)), dev(ck), None, "max",
+                      per_layer=True, fp8=fp8)
+    per_ref, ens_ref = oracle_scores(ck, qs, w[:, :2], [3000, 3000], "max")
+    e = max(max_score_err(host(s), ens_ref), max_score_err(host(p), per_ref))
+    report(f"q x 2^-20 ({'fp8' if fp8 else 'f16'})", max_abs=e)
+    assert e <= SCORE_TOL
+
+
+def test_large_f16_exact_queries(retr, qw):
+    """Queries 256 times their usual size (most sigmoids saturate) but exactly
+    representable in f16, so the kernel's one rounding of q is exact and
+    what remains (the exact decode, fp32 products and sums, the linear term's
+    three e4m3 parts, the sigmoid) must stay within the tolerance of the
+    oracle on the same queries.  (With unrepresentable queries at this size,
+    the rounding of q to f16 alone moves scores by up to about 2.4e-2: the
+    score error of the f16 path grows with the size of the logits, and the
+    2e-3 bound holds at the prepared queries' size.)"""
+    q, w = qw
+    qs = q[:, :2].astype(np.float16).astype(np.float64) * 2.0 ** 8
+    ck = records(3000, 12, rows=2)
+    s, p = retr.score(dev(qs.astype(np.float32)), dev(w[:, :2].astype(np.float32)), dev(ck), None, "max",
+                      per_layer=True)
+    per_ref, ens_ref = oracle_scores(ck, qs, w[:, :2], [3000, 3000], "max")
+    e = max(max_score_err(host(s), ens_ref), max_score_err(host(p), per_ref))
+    report("q x 2^8, f16-exact", max_abs=e)
     assert e <= SCORE_TOL
 
 
