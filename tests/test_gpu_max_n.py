@@ -10,7 +10,9 @@ random sign, scales of either sign with magnitude in [0.02, 0.2).  Scores
 sampled chunks: the first and last ones, those on both sides of the 2^32-byte
 record offset and of wave-share edges, and random ones.  The top-K and
 threshold masks are compared exactly with the oracle's selection of the
-GPU's own scores over the whole row."""
+GPU's own scores over the whole row, and so are the next rows' passes at
+this length: the resident set and recall delta between two masks, and the
+top-K within a resident list."""
 
 import numpy as np
 import pytest
@@ -95,3 +97,31 @@ def test_max_n_threshold_in_the_score_pass(big):
     e = max_score_err(s_h[idx], ens_ref)
     report(f"N = 2^26, mean + threshold, {len(idx)} sampled chunks", max_abs=e, kept=int(own.sum()))
     assert e <= SCORE_TOL
+
+
+def test_max_n_resident_delta(big):
+    """Resident set and recall delta between two top-4096 masks of the row
+    (the max and the mean ensemble's), against the oracle's lists."""
+    r, ck, qd, wd, q, w = big
+    cur = r.keep_topk(r.score(qd, wd, ck, None, "max"), 4096)
+    prev = r.keep_topk(r.score(qd, wd, ck, None, "mean"), 4096)
+    res, ent, lea = r.resident_delta(cur, prev, cap=8192)
+    ref = oracle.resident_delta(cur[0].cpu().numpy(), prev[0].cpu().numpy())
+    for got, want, name in zip((res[0], ent[0], lea[0]), ref, ("resident", "entering", "leaving")):
+        assert np.array_equal(got.cpu().numpy().astype(np.int64), want), name
+    report("N = 2^26, resident delta", resident=len(ref[0]), entering=len(ref[1]), leaving=len(ref[2]))
+
+
+def test_max_n_subset_topk(big):
+    """Top-512 of the mean-ensemble scores within the max ensemble's top-32768
+    chunks (the scan + finish path's longest list), against the oracle."""
+    r, ck, qd, wd, q, w = big
+    s_max = r.score(qd, wd, ck, None, "max")
+    s_mean = r.score(qd, wd, ck, None, "mean")
+    (res,), _, _ = r.resident_delta(r.keep_topk(s_max, 32768), None, cap=32768)
+    subset = res.reshape(1, -1).contiguous()
+    out, n_out = r.topk_in_subset(s_mean, subset, 512)
+    torch.cuda.synchronize()
+    want = oracle.select_topk_subset(s_mean[0].cpu().numpy(), subset[0].cpu().numpy(), 512)
+    assert int(n_out[0]) == len(want) == 512
+    assert np.array_equal(out[0].cpu().numpy().astype(np.int64), want)
