@@ -695,14 +695,18 @@ def _rocm_version() -> str:
 
 
 def _cpu_model() -> str:
+    """The host's CPU model name as /proc/cpuinfo gives it (a virtual machine
+    may report only the family) and the logical CPUs this process may use."""
+    model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                    model = line.split(":", 1)[1].strip()
+                    break
     except OSError:
         pass
-    return "unknown"
+    return f"{model}, {len(os.sched_getaffinity(0))} logical CPUs available"
 
 
 def main(argv=None):
