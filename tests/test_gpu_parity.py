@@ -88,6 +88,24 @@ def test_prepare_query_parity_yarn(retr_yarn, weights_np, rows):
     assert dq <= Q_TOL and dw <= W_TOL
 
 
+@pytest.mark.parametrize("yarn", [False, True])
+def test_prepare_query_large_positions(retr, retr_yarn, weights_np, yarn):
+    """Positions at the int32 and uint32 edges and past them: the angle in
+    double, its reduction to one turn and the float rotation keep q within
+    tolerance (the double product position x frequency itself moves by at
+    most a few times position x 2^-53 rad between two correct computations:
+    about 1e-6 at 2^32)."""
+    wl = synth.WORKLOADS[4 if yarn else 3]
+    pos = np.array([0, 1, 65535, 65536, 1 << 24, (1 << 31) - 1, 1 << 31, (1 << 32) + 5], np.int64)
+    hidden = synth.make_hidden(wl)[:len(pos)]
+    q_ref, w_ref = oracle.prepare_query(weights_np, hidden, pos, oracle_config(wl))
+    q, w = (retr_yarn if yarn else retr).prepare_query(dev(hidden), dev(pos))
+    dq = np.abs(host(q) - q_ref).max()
+    dw = np.abs(host(w) - w_ref).max()
+    report(f"prepare_query positions up to 2^32 + 5 ({'yarn' if yarn else 'no yarn'})", max_abs_q=dq, max_abs_w=dw)
+    assert dq <= Q_TOL and dw <= W_TOL
+
+
 # --------------------------------------------------------------------------- score from oracle queries
 
 @pytest.mark.parametrize("mode", ["max", "mean"])
