@@ -106,6 +106,31 @@ def test_prepare_query_large_positions(retr, retr_yarn, weights_np, yarn):
     assert dq <= Q_TOL and dw <= W_TOL
 
 
+def test_prepare_query_hidden_magnitudes(retr, weights_np):
+    """Hidden rows the activation split must handle: all zero, alternate
+    128-wide chunks zero, a single non-zero entry, fp32 subnormal entries,
+    and whole rows scaled by 2^-30 and 2^12 (RMSNorm's eps then dominates or
+    vanishes).  q is compared absolutely; w, which is not normalised,
+    relative to the row's scale."""
+    wl = synth.WORKLOADS[3]
+    base = synth.make_hidden(wl)[:6].astype(np.float64)
+    rows = [np.zeros(4096), base[0].copy(), np.zeros(4096), base[2] * 1e-41, base[3] * 2.0 ** -30, base[4] * 2.0 ** 12]
+    rows[1].reshape(32, 128)[::2] = 0.0
+    rows[2][1234] = 3.5
+    hidden = np.stack(rows).astype(np.float32)
+    scale = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 2.0 ** 12])
+    pos = synth.make_positions(wl)[:6]
+    q_ref, w_ref = oracle.prepare_query(weights_np, hidden.astype(np.float64), pos, oracle_config(wl))
+    q, w = retr.prepare_query(dev(hidden), dev(pos))
+    q_h, w_h = host(q), host(w)
+    assert np.all(np.isfinite(q_h)) and np.all(np.isfinite(w_h))
+    assert not np.any(q_h[:, 0]) and not np.any(w_h[:, 0])   # zero row: q = 0, w = 0 exactly
+    dq = np.abs(q_h - q_ref).max()
+    dw = (np.abs(w_h - w_ref) / scale[None, :, None]).max()
+    report("prepare_query hidden magnitudes", max_abs_q=dq, max_w_err_over_scale=dw)
+    assert dq <= Q_TOL and dw <= W_TOL
+
+
 # --------------------------------------------------------------------------- score from oracle queries
 
 @pytest.mark.parametrize("mode", ["max", "mean"])
