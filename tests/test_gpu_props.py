@@ -1,6 +1,7 @@
 """GPU properties and edge cases through the C ABI: determinism, chunk
-permutation, row independence, ties, zero and negative-scale records, tiny
-and large (f16-exact) query magnitudes, ragged and degenerate sizes, and the
+permutation, row independence, ties, zero and negative-scale records,
+records at the ends of the format (saturating scores), tiny and large
+(f16-exact) query magnitudes, ragged and degenerate sizes, and the
 selection kernels on constructed scores (compared exactly with the oracle's
 selection of the same scores)."""
 
@@ -192,6 +193,46 @@ def test_large_f16_exact_queries(retr, qw):
     e = max(max_score_err(host(s), ens_ref), max_score_err(host(p), per_ref))
     report("q x 2^8, f16-exact", max_abs=e)
     assert e <= SCORE_TOL
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_extreme_codes_and_saturating_scales(retr, qw, fp8):
+    """Records at the ends of the format: every code +-448 (the largest
+    e4m3fn magnitude) or the smallest subnormal (2^-9), and scales from
+    1e-30 up to 3e38, where |s| times a logit overflows to +-inf and the
+    sigmoid must give exactly 0 or 1 (never NaN).  Scores against the oracle;
+    the top-K among the many exact ties at 0 and 1 goes to the lowest
+    indices."""
+    q, w = qw
+    rng = np.random.default_rng(31)
+    n = 16 * 40
+    ck = records(n, 32)[0]
+    kinds = rng.integers(0, 6, n)
+    for c in range(n):
+        kind = kinds[c]
+        if kind == 0:
+            ck[c, :128] = 0x7E                                       # +448
+        elif kind == 1:
+            ck[c, :128] = 0xFE                                       # -448
+        elif kind == 2:
+            ck[c, :128] = np.where(rng.integers(0, 2, 128) == 1, 0x01, 0x81)   # +-2^-9
+        scale = [1.0, 1.0, 1e-30, 1e36, -3e38, 1e30][kind] * (1 + rng.uniform())
+        ck[c, 128:] = np.frombuffer(np.float32(min(scale, 3.4e38) if scale > 0 else max(scale, -3.4e38)).tobytes(),
+                                    np.uint8)
+    ck = ck[None]
+    qs, ws = q[:, :1], w[:, :1]
+    s, p = retr.score(dev(qs.astype(np.float32)), dev(ws.astype(np.float32)), dev(ck), None, "max",
+                      per_layer=True, fp8=fp8)
+    s_h, p_h = host(s), host(p)
+    assert np.all(np.isfinite(s_h)) and np.all(np.isfinite(p_h))
+    per_ref, ens_ref = oracle_scores(ck, qs, ws, [n], "max")
+    e = max(max_score_err(s_h, ens_ref), max_score_err(p_h, per_ref))
+    sat = int(np.sum((s_h == 0.0) | (s_h == 1.0)))
+    report(f"extreme codes and scales ({'fp8' if fp8 else 'f16'})", max_abs=e, saturated=sat)
+    assert e <= SCORE_TOL
+    for k in (7, 200):
+        m = host(retr.keep_topk(s, k))
+        assert np.array_equal(m[0].astype(np.uint8), oracle.select_topk(s_h[0].astype(np.float64), n, k))
 
 
 def test_identical_records_tie_to_lowest_index(retr, qw):
