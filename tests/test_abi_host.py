@@ -107,3 +107,26 @@ def test_binding_loads_torch_before_libfm():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-500:]
     assert out.stdout.strip().endswith("True")
+
+
+def test_plain_c_caller_builds_and_runs(tmp_path):
+    """include/fm.h compiles as strict C99 and a C program linked against
+    libfm.so gets the defaults and the host-side argument checks
+    (tests/abi_c/abi_check.c)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    pkg = os.path.join(ROOT, "sparse_attention_chunk_amd")
+    if not os.path.exists(os.path.join(pkg, "libfm.so")):
+        pytest.skip("libfm.so is not built")
+    exe = str(tmp_path / "abi_check")
+    build = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                            "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_c", "abi_check.c"),
+                            "-L", pkg, "-l:libfm.so", "-Wl,-rpath," + pkg, "-o", exe],
+                           capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0, (run.stdout + run.stderr)[-3000:]
+    assert run.stdout.strip() == "ok"
