@@ -370,52 +370,41 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   }
   // The listed chunks of each tile whose maximum is in bin c or above: its
   // largest one or two (s_e), or, when its third largest is in bin c or
-  // above too, the whole tile (s_f).  Each thread first stages its tiles'
-  // entries in LDS (slot k of thread t at k 256 + t, in the space of s_c):
-  // (chunk, second chunk or kNone), or (tile | 2^31, kNone) for a whole
-  // tile.  One scan then places both lists (counts in the low and high 16
-  // bits).
-  uint2* s_stage = s_c;
+  // above too, the whole tile (s_f).  Each thread classifies its register
+  // tiles without branches (2 bits each: 0 none, 1 the largest chunk, 2 the
+  // largest two, 3 the whole tile) and counts its entries; one scan places
+  // both lists (counts in the low and high 16 bits), and a second pass over
+  // the same registers writes the thread's entries in tile order.
   uint32_t ne = 0, nf = 0;
   {
-    uint32_t cnt = 0, nloc = 0;
+    uint32_t cnt = 0, kinds = 0;
 #pragma unroll
     for (int j = 0; j < kRegTiles; ++j) {
       const uint2 w = info[j];
-      const uint32_t tile = tile_of(j);
-      if (tile < nt && tw_bin1(w) >= c) {
-        const uint32_t first = tile << lt;
-        uint2 st;
-        if (tw_bin2(w) < c) {
-          st = make_uint2(first + tw_pos1(w), kNone);
-          cnt += 1u;
-        } else if (tw_bin3(w) < c) {
-          st = make_uint2(first + tw_pos1(w), first + tw_pos2(w));
-          cnt += 2u;
-        } else {
-          st = make_uint2(tile | 0x80000000u, kNone);
-          cnt += 0x10000u;
-        }
-        s_stage[nloc * kFinishThreads + t] = st;
-        ++nloc;
-      }
+      const bool q = tile_of(j) < nt && tw_bin1(w) >= c;
+      const uint32_t k = !q ? 0u : (tw_bin2(w) < c ? 1u : (tw_bin3(w) < c ? 2u : 3u));
+      kinds |= k << (2 * j);
+      cnt += k == 3u ? 0x10000u : k;
     }
     uint32_t tot;
     const uint32_t pos = block_excl_scan(cnt, s_wtot, &tot);
     ne = tot & 0xffffu;
     nf = tot >> 16;
     uint32_t pe = pos & 0xffffu, pf = pos >> 16;
-    for (uint32_t k = 0; k < nloc; ++k) {
-      const uint2 st = s_stage[k * kFinishThreads + t];
-      if (st.x & 0x80000000u) {
-        if (pf < (uint32_t)kFinishFull) s_f[pf] = st.x & 0x7fffffffu;
-        ++pf;
-      } else {
-        if (pe < (uint32_t)kFinishList) s_e[pe] = st.x;
-        ++pe;
-        if (st.y != kNone) {
-          if (pe < (uint32_t)kFinishList) s_e[pe] = st.y;
-          ++pe;
+#pragma unroll
+    for (int j = 0; j < kRegTiles; ++j) {
+      const uint32_t k = (kinds >> (2 * j)) & 3u;
+      if (k != 0u) {
+        const uint2 w = info[j];
+        const uint32_t tile = tile_of(j);
+        const uint32_t first = tile << lt;
+        if (k == 3u) {
+          if (pf < (uint32_t)kFinishFull) s_f[pf] = tile;
+          ++pf;
+        } else {
+          if (pe < (uint32_t)kFinishList) s_e[pe] = first + tw_pos1(w);
+          if (k == 2u && pe + 1 < (uint32_t)kFinishList) s_e[pe + 1] = first + tw_pos2(w);
+          pe += k;
         }
       }
     }
