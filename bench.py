@@ -22,7 +22,10 @@ fraction of a second of load after idle), then the K timed steps run.
 `configs` times the other four seeded workloads (B=1 N=4096; B=8 N=65536
 planted; B=32 N=131072 mean/threshold; B=60 N=131072 ragged YaRN top-1024)
 the same way, each with its own oracle baseline; the headline `value` is
-the B=30 N=262144 workload.
+the B=30 N=262144 workload.  `mfma_ceiling` times a dense f16 GEMM through
+torch.matmul (ROCm's BLAS) after a second of back-to-back calls: what a
+vendor-tuned MFMA kernel sustains on the same chip at its power limit, set
+beside the score kernel's rate.
 """
 
 from __future__ import annotations
@@ -67,6 +70,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the dense f16 GEMM that gives the chip's sustained MFMA rate for comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args(argv)
@@ -694,6 +699,38 @@ def _rocm_version() -> str:
         return "unknown"
 
 
+def gemm_ceiling_leg(seconds: float = 1.0, n: int = 8192, calls: int = 30):
+    """What a vendor-tuned MFMA kernel sustains on this chip under the same
+    conditions: a dense f16 GEMM (n x n x n, fp32 accumulation) through
+    torch.matmul, i.e. ROCm's BLAS.  The calls run back to back for `seconds`
+    first, so that the chip has reached the clock its power limit allows,
+    then `calls` more are timed between two synchronisations.  A context
+    for the roofline fraction, not a part of the scoring pass."""
+    import torch
+
+    a = torch.randn(n, n, device="cuda", dtype=torch.float16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.float16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.float16)
+    t0 = time.perf_counter()
+    settle = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        settle += 10
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / calls
+    del a, b, c
+    torch.cuda.empty_cache()
+    tflops = 2.0 * n ** 3 / dt / 1e12
+    return {"what": f"dense f16 GEMM {n}x{n}x{n} (fp32 accumulation) through torch.matmul (ROCm BLAS), "
+                    f"timed after {settle} back-to-back calls",
+            "us_per_call": dt * 1e6, "tflops": tflops, "frac_of_peak": tflops / PEAK_F16_TFLOPS}
+
+
 def _cpu_model() -> str:
     """The host's CPU model name as /proc/cpuinfo gives it (a virtual machine
     may report only the family) and the logical CPUs this process may use."""
@@ -827,6 +864,11 @@ def main(argv=None):
         for cid in (1, 2, 3, 4):
             print(f"# workload {cid}: {synth.WORKLOADS[cid].name}", file=sys.stderr, flush=True)
             configs[synth.WORKLOADS[cid].name] = config_leg(cid, weights, args.steps, 0.5, config_inputs)
+    ceiling = None
+    if not args.no_gemm_ceiling:
+        print("# dense f16 GEMM ceiling", file=sys.stderr, flush=True)
+        ceiling = gemm_ceiling_leg()
+        ceiling["score_kernel_frac_of_it"] = achieved / ceiling["tflops"]
     print("# cpu baseline", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, leg_inputs, config_inputs)
     cpu_model = cpu.pop("_cpu_model") if cpu else None
@@ -857,6 +899,7 @@ def main(argv=None):
             "hbm_algorithmic_gbs": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9,
             "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9 / PEAK_HBM_GBS,
         },
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "breakdown_steps": f"HIP events on {len(timed)} of the {args.steps} timed steps (every {EVENT_STRIDE}th)",
         "breakdown_us": {"prepare_query": float(prep.mean() * 1e6), "score": t_score * 1e6,
