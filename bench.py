@@ -22,10 +22,10 @@ fraction of a second of load after idle), then the K timed steps run.
 `configs` times the other four seeded workloads (B=1 N=4096; B=8 N=65536
 planted; B=32 N=131072 mean/threshold; B=60 N=131072 ragged YaRN top-1024)
 the same way, each with its own oracle baseline; the headline `value` is
-the B=30 N=262144 workload.  `mfma_ceiling` times a dense f16 GEMM through
-torch.matmul (ROCm's BLAS) after a second of back-to-back calls: what a
-vendor-tuned MFMA kernel sustains on the same chip at its power limit, set
-beside the score kernel's rate.
+the B=30 N=262144 workload.  `mfma_ceiling` times dense f16 and bf16
+GEMMs through torch.matmul (ROCm's BLAS) after a second of back-to-back
+calls each: what a vendor-tuned MFMA kernel sustains on the same chip at
+its power limit, set beside the score kernel's rate.
 """
 
 from __future__ import annotations
@@ -701,34 +701,39 @@ def _rocm_version() -> str:
 
 def gemm_ceiling_leg(seconds: float = 1.0, n: int = 8192, calls: int = 30):
     """What a vendor-tuned MFMA kernel sustains on this chip under the same
-    conditions: a dense f16 GEMM (n x n x n, fp32 accumulation) through
-    torch.matmul, i.e. ROCm's BLAS.  The calls run back to back for `seconds`
-    first, so that the chip has reached the clock its power limit allows,
-    then `calls` more are timed between two synchronisations.  A context
-    for the roofline fraction, not a part of the scoring pass."""
+    conditions: a dense 16-bit GEMM (n x n x n, fp32 accumulation) through
+    torch.matmul, i.e. ROCm's BLAS, in f16 and in bf16 (whose library kernels
+    are the faster here).  For each type the calls run back to back for
+    `seconds` first, so that the chip has reached the clock its power limit
+    allows, then `calls` more are timed between two synchronisations.
+    `tflops` is the faster type's.  A context for the roofline fraction, not
+    a part of the scoring pass."""
     import torch
 
-    a = torch.randn(n, n, device="cuda", dtype=torch.float16)
-    b = torch.randn(n, n, device="cuda", dtype=torch.float16)
-    c = torch.empty(n, n, device="cuda", dtype=torch.float16)
-    t0 = time.perf_counter()
-    settle = 0
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(10):
+    res = {}
+    for name, dt_ in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        a = torch.randn(n, n, device="cuda", dtype=dt_)
+        b = torch.randn(n, n, device="cuda", dtype=dt_)
+        c = torch.empty(n, n, device="cuda", dtype=dt_)
+        t0 = time.perf_counter()
+        settle = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+            settle += 10
+        t0 = time.perf_counter()
+        for _ in range(calls):
             torch.matmul(a, b, out=c)
         torch.cuda.synchronize()
-        settle += 10
-    t0 = time.perf_counter()
-    for _ in range(calls):
-        torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / calls
-    del a, b, c
-    torch.cuda.empty_cache()
-    tflops = 2.0 * n ** 3 / dt / 1e12
-    return {"what": f"dense f16 GEMM {n}x{n}x{n} (fp32 accumulation) through torch.matmul (ROCm BLAS), "
-                    f"timed after {settle} back-to-back calls",
-            "us_per_call": dt * 1e6, "tflops": tflops, "frac_of_peak": tflops / PEAK_F16_TFLOPS}
+        dt = (time.perf_counter() - t0) / calls
+        del a, b, c
+        torch.cuda.empty_cache()
+        res[name] = {"us_per_call": dt * 1e6, "tflops": 2.0 * n ** 3 / dt / 1e12, "settle_calls": settle}
+    best = max(res.values(), key=lambda r: r["tflops"])["tflops"]
+    return {"what": f"dense {n}x{n}x{n} GEMM (fp32 accumulation) through torch.matmul (ROCm BLAS), f16 and bf16, "
+                    f"each timed after a second of back-to-back calls",
+            **res, "tflops": best, "frac_of_peak": best / PEAK_F16_TFLOPS}
 
 
 def _cpu_model() -> str:
@@ -866,7 +871,7 @@ def main(argv=None):
             configs[synth.WORKLOADS[cid].name] = config_leg(cid, weights, args.steps, 0.5, config_inputs)
     ceiling = None
     if not args.no_gemm_ceiling:
-        print("# dense f16 GEMM ceiling", file=sys.stderr, flush=True)
+        print("# dense 16-bit GEMM ceiling", file=sys.stderr, flush=True)
         ceiling = gemm_ceiling_leg()
         ceiling["score_kernel_frac_of_it"] = achieved / ceiling["tflops"]
     print("# cpu baseline", file=sys.stderr, flush=True)
