@@ -9,8 +9,10 @@ workload (a 1M-token context at 4x compression, concurrency 30), synthetic
 seeded inputs already resident in HBM.  Prints one JSON line.
 
 `roofline` describes the score kernel (the dominant one, MFMA-bound at
-49152 flop per chunk); its duration comes from HIP events around each
-fm_score call on the stream the kernels run on.  `traffic` is read from the
+49152 flop per chunk); its duration comes from HIP events that libfm
+records around the score kernel's own launch (fm_set_score_events), on
+the stream the kernels run on; the whole fm_score call (query packing +
+score kernel) is timed by events around it as well.  `traffic` is read from the
 committed rocprofv3 counter summary when that summary was taken on the
 current score-kernel source, else null.  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on this host, and under
@@ -70,6 +72,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed step leg")
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the dense f16 GEMM that gives the chip's sustained MFMA rate for comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -263,6 +266,47 @@ def settle(step, stream, min_s: float, block: int = 50):
             break
     return {"steps": steps, "seconds": time.perf_counter() - t0, "first_block_us_per_step": per_block[0] * 1e6,
             "last_block_us_per_step": per_block[-1] * 1e6}
+
+
+def graph_step_leg(body, outputs, steps: int, settle_s: float) -> dict:
+    """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: after settle_s seconds of replays, `steps` replays back to
+    back, timed by host wall-clock between synchronisations and by two HIP
+    events.  body(stream_handle) enqueues one step; `outputs` are the
+    tensors it writes, whose eager values the last replay must equal bit
+    for bit."""
+    import torch
+
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        body(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    settled = settle(g.replay, stream, settle_s)
+    ev = [TimingEvent() for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(steps):
+        g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev_s = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    same = all(torch.equal(a, b) for a, b in zip(eager, outputs))
+    del g
+    return {"us_per_step": wall * 1e6, "us_per_step_events": ev_s * 1e6, "replays": steps,
+            "matches_eager": bool(same), "settle": settled,
+            "note": "prepare + score + top-K captured once as a HIP graph and replayed; wall-clock between "
+                    "synchronisations like the headline"}
 
 
 def _parity(ref: dict, gpu_scores, gpu_mask, valid_n: int, top_k, threshold, band: float = 2e-3) -> dict:
@@ -802,8 +846,10 @@ def main(argv=None):
         L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, sh)
         if ev is not None:
             ev[1].record(stream)
+            L.fm_set_score_events(r.ctx, ev[4].ev, ev[5].ev)  # the score kernel's launch alone
         L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, sh)
         if ev is not None:
+            L.fm_set_score_events(r.ctx, None, None)
             ev[2].record(stream)
         L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, sh)
         if ev is not None:
@@ -841,7 +887,7 @@ def main(argv=None):
     # Per-phase HIP events on every EVENT_STRIDE-th timed step: each record
     # still costs the stream about 1 us, so recording four on every step would
     # slow the loop being timed by about 1%.
-    events = [[TimingEvent() for _ in range(4)] if i % EVENT_STRIDE == 0 else None
+    events = [[TimingEvent() for _ in range(6)] if i % EVENT_STRIDE == 0 else None
               for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -854,12 +900,22 @@ def main(argv=None):
     prep = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
     score = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
     sel = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e-3
+    kern = np.array([e[4].elapsed_time(e[5]) for e in timed]) * 1e-3
     s_step = wall / args.steps
     chunks = B * N
     t_score = float(score.mean())
-    achieved = FLOP_PER_CHUNK * chunks / t_score / 1e12
+    t_kern = float(kern.mean())
+    achieved = FLOP_PER_CHUNK * chunks / t_kern / 1e12
     traffic = read_traffic(chunks)
     leg_inputs["headline"] = (scores.cpu().numpy(), mask.cpu().numpy())
+
+    def step_body(h):
+        L.fm_prepare_query(r.ctx, hidden, pos, B, q, w, h)
+        L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, h)
+        L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, h)
+
+    graph = None if args.no_graph else graph_step_leg(step_body, (q, w, scores, mask), args.steps,
+                                                      args.settle_seconds)
     r.close()
     del comp_k
     torch.cuda.empty_cache()
@@ -894,21 +950,26 @@ def main(argv=None):
         "config": {"workload": wl.name, "batch": B, "n_chunks": N, "layers": 3, "heads": 64, "head_dim": 128,
                    "q_lora_rank": 1024, "hidden": 4096, "ensemble": "max", "top_k": TOP_K, "positions": 4 * N},
         "roofline": {
-            "kernel": "score_kernel (fm_score: q pack + fused 3-layer score)",
+            "kernel": "score_kernel (fused 3-layer score and max ensemble), its launch alone",
+            "us_per_launch": t_kern * 1e6,
+            "fm_score_call_us": t_score * 1e6,
+            "fm_score_call_frac": FLOP_PER_CHUNK * chunks / t_score / 1e12 / PEAK_F16_TFLOPS,
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_F16_TFLOPS,
             "traffic": traffic,
-            "hbm_algorithmic_gbs": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9,
-            "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t_score / 1e9 / PEAK_HBM_GBS,
+            "hbm_algorithmic_gbs": SCORE_BYTES_PER_CHUNK * chunks / t_kern / 1e9,
+            "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t_kern / 1e9 / PEAK_HBM_GBS,
         },
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "breakdown_steps": f"HIP events on {len(timed)} of the {args.steps} timed steps (every {EVENT_STRIDE}th)",
         "breakdown_us": {"prepare_query": float(prep.mean() * 1e6), "score": t_score * 1e6,
                          "select_topk": float(sel.mean() * 1e6),
+                         "score_kernel": t_kern * 1e6,
+                         "score_kernel_median": float(np.median(kern) * 1e6),
                          "prepare_query_median": float(np.median(prep) * 1e6),
                          "score_median": float(np.median(score) * 1e6),
                          "select_topk_median": float(np.median(sel) * 1e6),
@@ -919,6 +980,7 @@ def main(argv=None):
         "score_select_chunks_per_s": chunks / (t_score + float(sel.mean())),
         "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
                       "mask_logits": masking},
+        "graph_step": graph,
         "workload_variants": variants,
         "settle": dict(settled, note="untimed back-to-back steps after the warmup, before the timed steps"),
         "clocks": clocks.summary(),

@@ -261,6 +261,19 @@ fm_status fm_resident_delta(fm_ctx* ctx, const uint8_t* prev_mask, const uint8_t
 fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, int32_t R, int64_t N,
                          const uint8_t* mask, void* stream);
 
+/* Timing hook for the score kernel alone (not a step of the pass: for
+ * measuring the dominant kernel against its roofline).  With two events
+ * set, every later fm_score, fm_score_threshold and fm_score_fp8 on ctx
+ * records `before` on its stream right before the score kernel's launch
+ * (after the query packing and the ragged-row planning) and `after` right
+ * after it, so hipEventElapsedTime(before, after) is that launch's
+ * duration.
+ *   before, after  hipEvent_t of the context's device, created and owned
+ *                  by the caller, valid while set; both NULL clears them
+ * One NULL and one not gives FM_EINVAL.  A failing record makes the score
+ * call return FM_EHIP (after its launches were enqueued). */
+fm_status fm_set_score_events(fm_ctx* ctx, void* before, void* after);
+
 /* Message of the last failing call on this thread ("" if none); valid until
  * the next fm_* call on this thread. */
 const char* fm_last_error(void);

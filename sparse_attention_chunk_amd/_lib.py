@@ -36,7 +36,7 @@ STATUS_NAMES = {FM_OK: "FM_OK", FM_EINVAL: "FM_EINVAL", FM_EUNSUPPORTED: "FM_EUN
 # Exported symbols, in header order.
 EXPORTS = ("fm_config_default", "fm_create", "fm_destroy", "fm_prepare_query", "fm_score", "fm_score_threshold",
            "fm_score_fp8", "fm_select_topk", "fm_select_topk_static", "fm_select_topk_subset", "fm_select_threshold", "fm_resident_delta",
-           "fm_mask_logits", "fm_last_error")
+           "fm_mask_logits", "fm_set_score_events", "fm_last_error")
 
 
 class FmConfig(ctypes.Structure):
@@ -102,6 +102,8 @@ def _load() -> ctypes.CDLL:
     lib.fm_mask_logits.restype = ctypes.c_int
     lib.fm_resident_delta.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.fm_resident_delta.restype = ctypes.c_int
+    lib.fm_set_score_events.argtypes = [vp, vp, vp]
+    lib.fm_set_score_events.restype = ctypes.c_int
     lib.fm_last_error.argtypes = []
     lib.fm_last_error.restype = ctypes.c_char_p
     return lib
@@ -193,6 +195,11 @@ def fm_select_threshold(ctx, scores, B, N, valid_n, threshold, mask, stream=None
 def fm_mask_logits(ctx, logits, dtype, B, R, N, mask, stream=None) -> None:
     s = current_stream() if stream is None else stream
     check(LIB.fm_mask_logits(ctx, ptr(logits), dtype, B, R, N, ptr(mask), s), "fm_mask_logits")
+
+
+def fm_set_score_events(ctx, before, after) -> None:
+    """before/after: hipEvent_t handles (ints or ctypes.c_void_p), or both None."""
+    check(LIB.fm_set_score_events(ctx, before, after), "fm_set_score_events")
 
 
 def fm_resident_delta(ctx, prev_mask, mask, B, N, cap, resident, n_resident, entering=None, n_entering=None,

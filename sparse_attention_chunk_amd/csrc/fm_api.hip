@@ -333,6 +333,17 @@ fm_status fm_score_threshold(fm_ctx* ctx, const float* q, const float* w, const 
   return FM_OK;
 }
 
+fm_status fm_set_score_events(fm_ctx* ctx, void* before, void* after) {
+  clear_err();
+  fm_status st = check_ctx(ctx);
+  if (st != FM_OK) return st;
+  if ((before == nullptr) != (after == nullptr))
+    return fail(FM_EINVAL, "fm_set_score_events takes two events or none");
+  ctx->ws.score_ev[0] = (hipEvent_t)before;
+  ctx->ws.score_ev[1] = (hipEvent_t)after;
+  return FM_OK;
+}
+
 fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N, const int32_t* valid_n,
                          int32_t top_k, uint8_t* mask, void* stream) {
   clear_err();

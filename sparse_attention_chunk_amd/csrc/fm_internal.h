@@ -99,7 +99,16 @@ struct Workspace {
   unsigned long long* res_bits = nullptr;  // [max_batch][ceil(max_n / kResSlice) * 256]: per 16 chunks, the
                                            //   three sets' bits (16 each), from the count pass
   uint2* tile_info = nullptr;    // [max_batch][tile_info_stride(max_n)]: per tile, for the top-K finish
+  // Caller's timing events (fm_set_score_events), recorded on the call's
+  // stream right before and right after the score kernel's own launch; null
+  // when unset.
+  hipEvent_t score_ev[2] = {nullptr, nullptr};
 };
+
+// Records the workspace's score events around one launch (when set).
+inline void record_score_event(const Workspace& ws, int which, hipStream_t stream) {
+  if (ws.score_ev[which]) (void)hipEventRecord(ws.score_ev[which], stream);
+}
 
 // Launchers.  Shapes are validated by the caller; each returns the launch
 // status (hipGetLastError after the launches).

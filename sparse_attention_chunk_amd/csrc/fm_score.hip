@@ -563,9 +563,11 @@ hipError_t launch_score_sel(const Workspace& ws, const float* q, const float* w,
   const bool mean = mode == FM_ENSEMBLE_MEAN;
   auto kern = mean ? (per_layer ? score_kernel<true, true, THR> : score_kernel<true, false, THR>)
                    : (per_layer ? score_kernel<false, true, THR> : score_kernel<false, false, THR>);
+  record_score_event(ws, 0, stream);
   hipLaunchKernelGGL(kern, dim3(ws.score_blocks), dim3(256), 0, stream, (const f16x8*)qpack, w, comp_k, B, N,
                      valid_n, row_tiles, (const int32_t*)ws.wave_row, total_tiles, scores, per_layer, mask,
                      threshold);
+  record_score_event(ws, 1, stream);
   if (THR && (N & 3))
     hipLaunchKernelGGL(threshold_edge_kernel, dim3(B), dim3(64), 0, stream, (const float*)scores, valid_n, N,
                        threshold, mask);

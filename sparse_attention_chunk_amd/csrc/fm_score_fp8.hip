@@ -395,8 +395,10 @@ hipError_t launch_score_fp8(const Workspace& ws, const float* q, const float* w,
   const bool mean = mode == FM_ENSEMBLE_MEAN;
   auto kern = mean ? (per_layer ? score8_kernel<true, true> : score8_kernel<true, false>)
                    : (per_layer ? score8_kernel<false, true> : score8_kernel<false, false>);
+  record_score_event(ws, 0, stream);
   hipLaunchKernelGGL(kern, dim3(ws.score_blocks), dim3(256), 0, stream, (const i32x8*)ws.qpack8, (const float*)ws.w8,
                      comp_k, B, N, valid_n, row_tiles, (const int32_t*)ws.wave_row, total_tiles, scores, per_layer);
+  record_score_event(ws, 1, stream);
   return hipGetLastError();
 }
 

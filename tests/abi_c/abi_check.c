@@ -55,6 +55,7 @@ int main(void) {
   EXPECT(fm_select_topk_subset(NULL, NULL, 1, 1, NULL, NULL, 1, 1, NULL, NULL, NULL) == FM_EINVAL);
   EXPECT(fm_resident_delta(NULL, NULL, NULL, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == FM_EINVAL);
   EXPECT(fm_mask_logits(NULL, NULL, FM_DTYPE_BF16, 1, 1, 1, NULL, NULL) == FM_EINVAL);
+  EXPECT(fm_set_score_events(NULL, NULL, NULL) == FM_EINVAL && has_message());
   fm_destroy(NULL);
 
   EXPECT(fm_select_topk_static(NULL, 70000, 16, NULL, 1, NULL, NULL) == FM_EINVAL && has_message());

@@ -106,3 +106,51 @@ def test_package_imported_before_torch_creates_a_context():
             "r.close(); print('ok')" % root)
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-800:]
+
+
+def test_score_events_time_the_score_kernel_alone(env):
+    """fm_set_score_events: the events bracket the score kernel's launch
+    inside fm_score, fm_score_threshold and fm_score_fp8 (so they span less
+    than the whole call), and clearing them leaves later calls alone."""
+    r, L = env
+    lib, ctx = L.LIB, r.ctx
+    B, N = 4, 1000
+    rng = np.random.default_rng(11)
+    q = torch.from_numpy(rng.standard_normal((3, B, 64, 128)).astype(np.float32) * 0.1).cuda()
+    w = torch.from_numpy(rng.standard_normal((3, B, 64)).astype(np.float32) * 0.01).cuda()
+    ck = torch.from_numpy(rng.integers(0, 0x7f, (B, N, 132), dtype=np.uint8)).cuda()
+    scores = torch.empty((B, N), device="cuda")
+    mask = torch.empty((B, N), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    P = L.ptr
+    assert lib.fm_set_score_events(ctx, None, None) == L.FM_OK
+    call = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kern = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in kern:
+        e.record(stream)  # creates the event
+    torch.cuda.synchronize()
+    assert lib.fm_set_score_events(ctx, kern[0].cuda_event, None) == L.FM_EINVAL
+    assert lib.fm_set_score_events(None, kern[0].cuda_event, kern[1].cuda_event) == L.FM_EINVAL
+    assert lib.fm_set_score_events(ctx, kern[0].cuda_event, kern[1].cuda_event) == L.FM_OK
+    try:
+        calls = [
+            lambda: lib.fm_score(ctx, P(q), P(w), P(ck), B, N, None, 0, P(scores), None, s),
+            lambda: lib.fm_score_threshold(ctx, P(q), P(w), P(ck), B, N, None, 0, 0.5, P(scores), P(mask), None, s),
+            lambda: lib.fm_score_fp8(ctx, P(q), P(w), P(ck), B, N, None, 0, P(scores), None, s),
+        ]
+        for c in calls:
+            call[0].record(stream)
+            assert c() == L.FM_OK
+            call[1].record(stream)
+            torch.cuda.synchronize()
+            t_kern = kern[0].elapsed_time(kern[1])
+            t_call = call[0].elapsed_time(call[1])
+            assert 0.0 < t_kern <= t_call
+    finally:
+        assert lib.fm_set_score_events(ctx, None, None) == L.FM_OK
+    # Cleared: a later call records nothing, so the pair keeps its last span.
+    before = kern[0].elapsed_time(kern[1])
+    assert lib.fm_score(ctx, P(q), P(w), P(ck), B, N, None, 0, P(scores), None, s) == L.FM_OK
+    torch.cuda.synchronize()
+    assert kern[0].elapsed_time(kern[1]) == before
