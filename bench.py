@@ -73,6 +73,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed step leg")
+    ap.add_argument("--no-pipelined", action="store_true", help="skip the two-stream pipelined leg")
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the dense f16 GEMM that gives the chip's sustained MFMA rate for comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -307,6 +308,54 @@ def graph_step_leg(body, outputs, steps: int, settle_s: float) -> dict:
             "matches_eager": bool(same), "settle": settled,
             "note": "prepare + score + top-K captured once as a HIP graph and replayed; wall-clock between "
                     "synchronisations like the headline"}
+
+
+def pipelined_leg(L, ctx_a, ctx_b, hidden, pos, q, w, comp_k, B, N, ref_scores, ref_mask, steps: int,
+                  settle_s: float) -> dict:
+    """Consecutive passes pipelined over two streams: the query preparation
+    and the score of pass i run on the current stream with context ctx_a,
+    its top-K on a second stream with context ctx_b (each context serves one
+    stream), so pass i's selection runs while pass i+1's preparation does.
+    Scores and masks are double-buffered; pass i's score waits for the
+    selection that last read its buffer (pass i-2).  Every pass does the
+    whole path.  Timed by host wall-clock between device synchronisations
+    over `steps` passes, after settle_s seconds of passes; the last pass's
+    scores and mask must equal the sequential step's (ref_*) bit for bit."""
+    import torch
+
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()
+    scores = [torch.empty((B, N), device="cuda") for _ in range(2)]
+    masks = [torch.empty((B, N), dtype=torch.bool, device="cuda") for _ in range(2)]
+    ev_score = [torch.cuda.Event() for _ in range(2)]
+    ev_sel = [torch.cuda.Event() for _ in range(2)]
+    for e in ev_sel:
+        e.record(sa)
+    state = {"i": 0}
+
+    def one():
+        b = state["i"] & 1
+        L.fm_prepare_query(ctx_a, hidden, pos, B, q, w, sa.cuda_stream)
+        sa.wait_event(ev_sel[b])
+        L.fm_score(ctx_a, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores[b], None, sa.cuda_stream)
+        ev_score[b].record(sa)
+        sb.wait_event(ev_score[b])
+        L.fm_select_topk(ctx_b, scores[b], B, N, None, TOP_K, masks[b], sb.cuda_stream)
+        ev_sel[b].record(sb)
+        state["i"] += 1
+
+    settled = settle(one, sa, settle_s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    last = (state["i"] - 1) & 1
+    same = bool(torch.equal(scores[last], ref_scores) and torch.equal(masks[last], ref_mask))
+    return {"us_per_step": wall * 1e6, "steps": steps, "matches_sequential": same, "settle": settled,
+            "note": "pass i's top-K on a second stream (own context) while pass i+1's query preparation runs; "
+                    "scores and masks double-buffered"}
 
 
 def _parity(ref: dict, gpu_scores, gpu_mask, valid_n: int, top_k, threshold, band: float = 2e-3) -> dict:
@@ -916,6 +965,12 @@ def main(argv=None):
 
     graph = None if args.no_graph else graph_step_leg(step_body, (q, w, scores, mask), args.steps,
                                                       args.settle_seconds)
+    pipelined = None
+    if not args.no_pipelined:
+        r_sel = fm.FlashMemoryRetriever(weights, max_batch=B, max_n=N)
+        pipelined = pipelined_leg(L, r.ctx, r_sel.ctx, hidden, pos, q, w, comp_k, B, N, scores, mask, args.steps,
+                                  args.settle_seconds)
+        r_sel.close()
     r.close()
     del comp_k
     torch.cuda.empty_cache()
@@ -981,6 +1036,7 @@ def main(argv=None):
         "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
                       "mask_logits": masking},
         "graph_step": graph,
+        "pipelined_step": pipelined,
         "workload_variants": variants,
         "settle": dict(settled, note="untimed back-to-back steps after the warmup, before the timed steps"),
         "clocks": clocks.summary(),
