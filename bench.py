@@ -269,6 +269,21 @@ def settle(step, stream, min_s: float, block: int = 50):
             "last_block_us_per_step": per_block[-1] * 1e6}
 
 
+def _frac_at_clock(achieved_tflops: float, clocks: dict):
+    """The score kernel's rate against the f16 MFMA peak scaled to the mean
+    GFX clock the firmware reported during the settle phase (the published
+    2.5 PF assumes 2.4 GHz), or None without clock samples."""
+    try:
+        mhz = float(clocks["current_gfxclk"]["mean"])
+    except (KeyError, TypeError, ValueError):
+        return None
+    if not mhz > 0:
+        return None
+    peak = PEAK_F16_TFLOPS * mhz / 2400.0
+    return {"gfxclk_mhz": mhz, "peak_tflops_at_clock": peak, "frac": achieved_tflops / peak,
+            "note": "mean of the firmware's current_gfxclk samples over the settle phase"}
+
+
 def graph_step_leg(body, outputs, steps: int, settle_s: float) -> dict:
     """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
     replayed: after settle_s seconds of replays, `steps` replays back to
@@ -1019,6 +1034,7 @@ def main(argv=None):
             "hbm_frac": SCORE_BYTES_PER_CHUNK * chunks / t_kern / 1e9 / PEAK_HBM_GBS,
         },
         "mfma_ceiling": ceiling,
+        "frac_at_sampled_clock": _frac_at_clock(achieved, clocks.summary()),
         "cpu_baseline": cpu,
         "breakdown_steps": f"HIP events on {len(timed)} of the {args.steps} timed steps (every {EVENT_STRIDE}th)",
         "breakdown_us": {"prepare_query": float(prep.mean() * 1e6), "score": t_score * 1e6,
