@@ -270,8 +270,10 @@ fm_status fm_mask_logits(fm_ctx* ctx, void* logits, fm_dtype dtype, int32_t B, i
  * duration.
  *   before, after  hipEvent_t of the context's device, created and owned
  *                  by the caller, valid while set; both NULL clears them
- * One NULL and one not gives FM_EINVAL.  A failing record makes the score
- * call return FM_EHIP (after its launches were enqueued). */
+ * A score call that enqueues nothing (B == 0 or N == 0, or an argument
+ * error) records nothing, so the events keep their last timestamps.  One
+ * NULL and one not gives FM_EINVAL.  A failing record makes the score call
+ * return FM_EHIP (after its launches were enqueued). */
 fm_status fm_set_score_events(fm_ctx* ctx, void* before, void* after);
 
 /* Message of the last failing call on this thread ("" if none); valid until
