@@ -442,9 +442,8 @@ __global__ __launch_bounds__(256, 1) void score_kernel(const f16x8* __restrict__
 // Plan for ragged rows (one block of 1024 threads): row_tiles[b] = sum of
 // ceil(valid_n / 16) over the rows before b (row_tiles[B] = all tiles), and
 // for each wave the row holding its first tile.
-__global__ __launch_bounds__(1024) void score_plan_kernel(const int32_t* __restrict__ valid_n, int B, int64_t N,
-                                                          int waves, int64_t* __restrict__ row_tiles,
-                                                          int32_t* __restrict__ wave_row) {
+__device__ __forceinline__ void plan_rows(const int32_t* __restrict__ valid_n, int B, int64_t N, int waves,
+                                          int64_t* __restrict__ row_tiles, int32_t* __restrict__ wave_row) {
   __shared__ int64_t s_pre[4096 + 1];
   __shared__ int64_t s_wsum[16];
   const int t = threadIdx.x;
@@ -489,17 +488,26 @@ __global__ __launch_bounds__(1024) void score_plan_kernel(const int32_t* __restr
   }
 }
 
-// -inf for the chunks of each row at or beyond its valid_n
-// (and, with the selection folded in, a zero mask byte).
+// Ragged rows, one launch before the score kernel (block = 1024 threads,
+// grid = (tail_blocks + 1, B)): the last column's block of row 0 runs the
+// plan (the other rows' blocks of that column have nothing to do); the
+// other blocks write -inf for the chunks of row blockIdx.y at or beyond its
+// valid_n (and, with the selection folded in, a zero mask byte).
 template <bool PER_LAYER>
-__global__ __launch_bounds__(256) void score_tail_kernel(const int32_t* __restrict__ valid_n, int B, int64_t N,
-                                                         float* __restrict__ scores, float* __restrict__ per_layer,
-                                                         uint8_t* __restrict__ mask) {
+__global__ __launch_bounds__(1024) void score_ragged_kernel(const int32_t* __restrict__ valid_n, int B, int64_t N,
+                                                            int waves, int64_t* __restrict__ row_tiles,
+                                                            int32_t* __restrict__ wave_row, float* __restrict__ scores,
+                                                            float* __restrict__ per_layer, uint8_t* __restrict__ mask) {
+  const int tail_blocks = (int)gridDim.x - 1;
+  if ((int)blockIdx.x == tail_blocks) {
+    if (blockIdx.y == 0) plan_rows(valid_n, B, N, waves, row_tiles, wave_row);
+    return;
+  }
   const int b = blockIdx.y;
   const int64_t v = valid_n[b];
   const int64_t vn = v < 0 ? 0 : (v > N ? N : v);
   const float ninf = -__builtin_huge_valf();
-  for (int64_t n = vn + (int64_t)blockIdx.x * 256 + threadIdx.x; n < N; n += (int64_t)gridDim.x * 256) {
+  for (int64_t n = vn + (int64_t)blockIdx.x * 1024 + threadIdx.x; n < N; n += (int64_t)tail_blocks * 1024) {
     scores[(size_t)b * N + n] = ninf;
     if (PER_LAYER)
       for (int l = 0; l < kLayers; ++l) per_layer[((size_t)l * B + b) * N + n] = ninf;
@@ -535,16 +543,11 @@ hipError_t plan_and_tail(const Workspace& ws, const int32_t* valid_n, int B, int
   *total_tiles = (int64_t)B * ((N + kTile - 1) / kTile);
   *row_tiles = nullptr;
   if (valid_n) {
-    hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(1024), 0, stream, valid_n, B, N, 4 * ws.score_blocks,
-                       ws.row_tiles, ws.wave_row);
     *row_tiles = ws.row_tiles;
-    const unsigned gx = (unsigned)std::min<int64_t>((N + 255) / 256, 64);
-    if (per_layer)
-      hipLaunchKernelGGL(score_tail_kernel<true>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores, per_layer,
-                         mask);
-    else
-      hipLaunchKernelGGL(score_tail_kernel<false>, dim3(gx, B), dim3(256), 0, stream, valid_n, B, N, scores,
-                         per_layer, mask);
+    const unsigned gx = (unsigned)std::min<int64_t>((N + 1023) / 1024, 16);  // tail blocks per row
+    auto kern = per_layer ? score_ragged_kernel<true> : score_ragged_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(gx + 1, B), dim3(1024), 0, stream, valid_n, B, N, 4 * ws.score_blocks,
+                       ws.row_tiles, ws.wave_row, scores, per_layer, mask);
   }
   return hipGetLastError();
 }
