@@ -87,11 +87,13 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q
   __shared__ float red[2][kHeadDim];
   __shared__ float vmax[2];
   __shared__ __attribute__((aligned(16))) uint32_t lin8[3][kHeadDim / 4];  // [part][dims / 4]
+  __shared__ float w_s[kHeads];  // the row's head weights, loaded with q (not in the sum's loop)
   const int b = blockIdx.x / kLayers;
   const int layer = blockIdx.x % kLayers;
   const int t = threadIdx.x;
   const float* qb = q + ((size_t)layer * B + b) * kHeads * kHeadDim;
   f16x8* out = qpack + (size_t)b * kQFrags * 64;
+  const float wt = t < kHeads ? w[((size_t)layer * B + b) * kHeads + t] : 0.f;
   float4 v[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -113,13 +115,13 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const float* __restrict__ q
     out[(layer * 16 + f) * 64 + lane] = h;
     *(f16x8*)&qs[head][d0] = h;
   }
+  if (t < kHeads) w_s[t] = wt;
   __syncthreads();
   {
     const int d = t & (kHeadDim - 1), half = t >> 7;
-    const float* wb = w + ((size_t)layer * B + b) * kHeads + 32 * half;
     float acc = 0.f;
 #pragma unroll 8
-    for (int h = 0; h < 32; ++h) acc = fmaf(wb[h], (float)qs[32 * half + h][d], acc);
+    for (int h = 0; h < 32; ++h) acc = fmaf(w_s[32 * half + h], (float)qs[32 * half + h][d], acc);
     red[half][d] = acc;
   }
   __syncthreads();

@@ -84,12 +84,13 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ 
   __shared__ float red[2][kHeadDim];
   __shared__ float wmax[2];
   __shared__ __attribute__((aligned(16))) uint32_t lin8[3][kHeadDim / 4];  // [part][dims / 4]
+  __shared__ float w_s[kHeads];  // the row's head weights, loaded with q (not in the sum's loop)
   const int b = blockIdx.x / kLayers;
   const int layer = blockIdx.x % kLayers;
   const int t = threadIdx.x;
   const int h = t >> 2, g = t & 3;
   const float* qh = q + (((size_t)layer * B + b) * kHeads + h) * kHeadDim + 32 * g;
-  const float* wl = w + ((size_t)layer * B + b) * kHeads;
+  const float wh = w[((size_t)layer * B + b) * kHeads + h];
   float v[32];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -130,7 +131,10 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ 
     out[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     out[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
   }
-  if (g == 0) w8[(size_t)b * kW8Row + layer * kHeads + h] = ldexpf(0.5f * wl[h], -a);
+  if (g == 0) {
+    w8[(size_t)b * kW8Row + layer * kHeads + h] = ldexpf(0.5f * wh, -a);
+    w_s[h] = wh;
+  }
   __syncthreads();
 
   // v_d = 1/2 sum_h w_h q_hd over the dequantised parts, in two head halves.
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(const float* __restrict__ 
     const int d = t & (kHeadDim - 1), half = t >> 7;
     float acc = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) acc = fmaf(wl[32 * half + k], qs[32 * half + k][d], acc);
+    for (int k = 0; k < 32; ++k) acc = fmaf(w_s[32 * half + k], qs[32 * half + k][d], acc);
     red[half][d] = acc;
   }
   __syncthreads();
