@@ -326,16 +326,19 @@ def graph_step_leg(body, outputs, steps: int, settle_s: float) -> dict:
 
 
 def pipelined_leg(L, ctx_a, ctx_b, hidden, pos, q, w, comp_k, B, N, ref_scores, ref_mask, steps: int,
-                  settle_s: float) -> dict:
+                  settle_s: float, beside: str = "prepare") -> dict:
     """Consecutive passes pipelined over two streams: the query preparation
     and the score of pass i run on the current stream with context ctx_a,
     its top-K on a second stream with context ctx_b (each context serves one
-    stream), so pass i's selection runs while pass i+1's preparation does.
-    Scores and masks are double-buffered; pass i's score waits for the
-    selection that last read its buffer (pass i-2).  Every pass does the
-    whole path.  Timed by host wall-clock between device synchronisations
-    over `steps` passes, after settle_s seconds of passes; the last pass's
-    scores and mask must equal the sequential step's (ref_*) bit for bit."""
+    stream).  beside="prepare": pass i's top-K starts when its score ends,
+    beside pass i+1's query preparation; beside="score": it starts when pass
+    i+1's preparation ends, beside pass i+1's score kernel (whose waves leave
+    room on each SIMD for a selection wave).  Scores and masks are
+    double-buffered; pass i's score waits for the selection that last read
+    its buffer (pass i-2).  Every pass does the whole path.  Timed by host
+    wall-clock between device synchronisations over `steps` passes, after
+    settle_s seconds of passes; the last pass's scores and mask must equal
+    the sequential step's (ref_*) bit for bit."""
     import torch
 
     sa = torch.cuda.current_stream()
@@ -344,33 +347,56 @@ def pipelined_leg(L, ctx_a, ctx_b, hidden, pos, q, w, comp_k, B, N, ref_scores, 
     masks = [torch.empty((B, N), dtype=torch.bool, device="cuda") for _ in range(2)]
     ev_score = [torch.cuda.Event() for _ in range(2)]
     ev_sel = [torch.cuda.Event() for _ in range(2)]
+    ev_prep = torch.cuda.Event()
     for e in ev_sel:
         e.record(sa)
-    state = {"i": 0}
+    state = {"i": 0, "pending": None}
+
+    def select(b, after):
+        sb.wait_event(after)
+        L.fm_select_topk(ctx_b, scores[b], B, N, None, TOP_K, masks[b], sb.cuda_stream)
+        ev_sel[b].record(sb)
 
     def one():
         b = state["i"] & 1
         L.fm_prepare_query(ctx_a, hidden, pos, B, q, w, sa.cuda_stream)
+        if beside == "score" and state["pending"] is not None:
+            ev_prep.record(sa)
+            select(state["pending"], ev_prep)
+            state["pending"] = None
         sa.wait_event(ev_sel[b])
         L.fm_score(ctx_a, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores[b], None, sa.cuda_stream)
         ev_score[b].record(sa)
-        sb.wait_event(ev_score[b])
-        L.fm_select_topk(ctx_b, scores[b], B, N, None, TOP_K, masks[b], sb.cuda_stream)
-        ev_sel[b].record(sb)
+        if beside == "score":
+            state["pending"] = b
+        else:
+            select(b, ev_score[b])
         state["i"] += 1
 
-    settled = settle(one, sa, settle_s)
+    def drain():
+        if state["pending"] is not None:
+            select(state["pending"], ev_score[state["pending"]])
+            state["pending"] = None
+
+    def block_step():
+        one()
+
+    settled = settle(block_step, sa, settle_s)
+    drain()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         one()
+    drain()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     last = (state["i"] - 1) & 1
     same = bool(torch.equal(scores[last], ref_scores) and torch.equal(masks[last], ref_mask))
     return {"us_per_step": wall * 1e6, "steps": steps, "matches_sequential": same, "settle": settled,
-            "note": "pass i's top-K on a second stream (own context) while pass i+1's query preparation runs; "
-                    "scores and masks double-buffered"}
+            "beside": beside,
+            "note": f"pass i's top-K on a second stream (own context) beside pass i+1's "
+                    f"{'query preparation' if beside == 'prepare' else 'score kernel'}; scores and masks "
+                    "double-buffered"}
 
 
 def _parity(ref: dict, gpu_scores, gpu_mask, valid_n: int, top_k, threshold, band: float = 2e-3) -> dict:
@@ -990,8 +1016,9 @@ def main(argv=None):
     pipelined = None
     if not args.no_pipelined:
         r_sel = fm.FlashMemoryRetriever(weights, max_batch=B, max_n=N)
-        pipelined = pipelined_leg(L, r.ctx, r_sel.ctx, hidden, pos, q, w, comp_k, B, N, scores, mask, args.steps,
-                                  args.settle_seconds)
+        pipelined = {beside: pipelined_leg(L, r.ctx, r_sel.ctx, hidden, pos, q, w, comp_k, B, N, scores, mask,
+                                           args.steps, args.settle_seconds, beside)
+                     for beside in ("prepare", "score")}
         r_sel.close()
     r.close()
     del comp_k
