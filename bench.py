@@ -1011,14 +1011,23 @@ def main(argv=None):
         L.fm_score(r.ctx, q, w, comp_k, B, N, None, L.FM_ENSEMBLE_MAX, scores, None, h)
         L.fm_select_topk(r.ctx, scores, B, N, None, TOP_K, mask, h)
 
-    graph = None if args.no_graph else graph_step_leg(step_body, (q, w, scores, mask), args.steps,
-                                                      args.settle_seconds)
+    # Supplementary legs after the headline's figures are taken: a failure is
+    # reported in their field (the headline line is still printed).
+    graph = None
+    if not args.no_graph:
+        try:
+            graph = graph_step_leg(step_body, (q, w, scores, mask), args.steps, args.settle_seconds)
+        except Exception as exc:  # noqa: BLE001
+            graph = {"error": f"{type(exc).__name__}: {exc}"}
     pipelined = None
     if not args.no_pipelined:
         r_sel = fm.FlashMemoryRetriever(weights, max_batch=B, max_n=N)
-        pipelined = {beside: pipelined_leg(L, r.ctx, r_sel.ctx, hidden, pos, q, w, comp_k, B, N, scores, mask,
-                                           args.steps, args.settle_seconds, beside)
-                     for beside in ("prepare", "score")}
+        try:
+            pipelined = {beside: pipelined_leg(L, r.ctx, r_sel.ctx, hidden, pos, q, w, comp_k, B, N, scores, mask,
+                                               args.steps, args.settle_seconds, beside)
+                         for beside in ("prepare", "score")}
+        except Exception as exc:  # noqa: BLE001
+            pipelined = {"error": f"{type(exc).__name__}: {exc}"}
         r_sel.close()
     r.close()
     del comp_k
