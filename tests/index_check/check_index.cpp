@@ -55,7 +55,7 @@ void check_score_walk(const Shape& sh, int waves) {
   const int64_t N = sh.N;
   const bool ragged = !sh.valid.empty();
   const int32_t* vptr = ragged ? sh.valid.data() : nullptr;
-  // The ragged plan's outputs (the plan kernel forms the same prefix with a
+  // The ragged plan's outputs (the ragged launch's plan block forms the same prefix with a
   // parallel scan): each row's first list index and each wave's first row.
   std::vector<int64_t> pre(B + 1);
   std::vector<int32_t> wave_row(waves);
