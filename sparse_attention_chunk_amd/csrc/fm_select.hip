@@ -25,7 +25,9 @@
 //      ranked (key descending, index ascending) for the rest.
 // When the listed chunks or the candidates overflow LDS (many equal or
 // nearly equal scores), the finish selects exactly over the whole row with
-// radix passes instead, so the result is always the exact top-K.
+// radix passes instead, so the result is always the exact top-K.  Rows of
+// at most kShortRow chunks skip the scan: one launch selects each row with
+// those radix passes directly.
 #include "fm_radix.h"
 
 namespace fm {
@@ -615,6 +617,45 @@ write_out:
   }
 }
 
+// Top-K of short rows (N <= kShortRow) in one launch instead of scan +
+// finish: one block per row selects exactly over the row's keys (every
+// radix pass re-reads the row's scores, at most kShortRow x 4 bytes, from
+// the cache) and then writes each mask byte of the row once.  The same
+// chunks as the two-kernel path: keys above the K-th key T, and of those
+// equal to T the ones up to `last` (ties to the lowest indices).
+constexpr int64_t kShortRow = 8192;
+__global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float* __restrict__ scores, int64_t N,
+                                                                    const int32_t* __restrict__ valid_n,
+                                                                    int32_t top_k, uint8_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
+  __shared__ uint32_t s_wtot[kFinishThreads / 64];
+  __shared__ uint32_t s_out[3];
+  const int b = blockIdx.x;
+  const uint32_t t = threadIdx.x;
+  const int64_t vn = row_valid(valid_n, b, N);
+  const float* row = scores + (size_t)b * N;
+  uint8_t* mrow = mask + (size_t)b * N;
+  const uint32_t n_all = (uint32_t)N, vn32 = (uint32_t)vn;  // N <= kShortRow
+  if (top_k == 0 || (int64_t)top_k >= vn) {  // uniform over the block: nothing or every valid chunk
+    const uint8_t keep = top_k > 0 ? 1 : 0;
+    for (uint32_t n = t; n < n_all; n += kFinishThreads) mrow[n] = n < vn32 ? keep : 0;
+    return;
+  }
+  auto each = [&](auto f) {
+    for (uint32_t n = t; n < vn32; n += kFinishThreads) f(make_uint2(order_key(row[n]), n));
+  };
+  uint32_t T, last;
+  radix_select<kFinishThreads>(each, (uint32_t)top_k, index_bits(vn), h, s_wtot, s_out, &T, &last);
+  for (uint32_t n = t; n < n_all; n += kFinishThreads) {
+    uint8_t keep = 0;
+    if (n < vn32) {
+      const uint32_t k = order_key(row[n]);
+      keep = (k > T || (k == T && n <= last)) ? 1 : 0;
+    }
+    mrow[n] = keep;
+  }
+}
+
 // Threshold mask: 16 chunks per thread, one 16-byte store when the run is
 // whole and aligned.  grid = (ceil(N / kScanSlice), B), block = kScanThreads.
 __global__ __launch_bounds__(kScanThreads) void threshold_kernel(const float* __restrict__ scores, int64_t N,
@@ -645,6 +686,10 @@ __global__ __launch_bounds__(kScanThreads) void threshold_kernel(const float* __
 
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream) {
+  if (N <= kShortRow) {
+    hipLaunchKernelGGL(topk_short_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k, mask);
+    return hipGetLastError();
+  }
   const unsigned slices = (unsigned)((N + kScanSlice - 1) / kScanSlice);
   hipLaunchKernelGGL(topk_scan_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, valid_n, top_k,
                      ws.tile_info, mask);

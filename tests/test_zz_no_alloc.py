@@ -1,7 +1,8 @@
 """fm_select_topk_static (no context, no allocation: its scratch is a static
 device array) through the C ABI, against fm_select_topk on the same scores:
 masks identical, on two calls in a row, the second smaller than the first
-(the scratch keeps the first call's contents)."""
+(the scratch keeps the first call's contents), then on rows short enough
+for the one-launch path."""
 
 import numpy as np
 import pytest
@@ -39,14 +40,22 @@ def test_static_topk_matches_the_context_call_twice_second_smaller():
         s1 = _scores(30, 262144, 1, ties=False)
         a, b = _both(r.ctx, s1, None, 512)
         assert torch.equal(a, b) and int(b.sum()) == 30 * 512
-        # 2: smaller, ragged, heavy ties, N not a multiple of 16
-        s2 = _scores(4, 5003, 2, ties=True)
-        vn = torch.tensor([5003, 4000, 17, 0], dtype=torch.int32, device="cuda")
+        # 2: smaller, ragged, heavy ties, N not a multiple of 16 (rows longer
+        # than 8192 chunks: the scan + finish path on the static scratch)
+        s2 = _scores(4, 20003, 2, ties=True)
+        vn = torch.tensor([20003, 16000, 17, 0], dtype=torch.int32, device="cuda")
         for k in (1, 17, 600):
             a, b = _both(r.ctx, s2, vn, k)
             assert torch.equal(a, b), k
             counts = b.sum(dim=1).cpu().numpy()
-            assert list(counts) == [min(k, 5003), min(k, 4000), min(k, 17), 0]
+            assert list(counts) == [min(k, 20003), min(k, 16000), min(k, 17), 0]
+        # 3: short rows (one launch, no scratch needed)
+        s3 = _scores(4, 5003, 3, ties=True)
+        vn3 = torch.tensor([5003, 4000, 17, 0], dtype=torch.int32, device="cuda")
+        for k in (1, 600):
+            a, b = _both(r.ctx, s3, vn3, k)
+            assert torch.equal(a, b), k
+            assert list(b.sum(dim=1).cpu().numpy()) == [min(k, 5003), min(k, 4000), min(k, 17), 0]
         # oversize: rejected, nothing launched
         big = torch.empty((65, 16), device="cuda")
         with pytest.raises(_lib.FmError) as e:
