@@ -149,6 +149,17 @@ def test_score_events_time_the_score_kernel_alone(env):
             assert 0.0 < t_kern <= t_call
     finally:
         assert lib.fm_set_score_events(ctx, None, None) == L.FM_OK
+    # Ragged rows: the plan and -inf tail launch runs before the events.
+    vn = torch.tensor([1000, 517, 3, 0], dtype=torch.int32, device="cuda")
+    assert lib.fm_set_score_events(ctx, kern[0].cuda_event, kern[1].cuda_event) == L.FM_OK
+    try:
+        call[0].record(stream)
+        assert lib.fm_score(ctx, P(q), P(w), P(ck), B, N, P(vn), 0, P(scores), None, s) == L.FM_OK
+        call[1].record(stream)
+        torch.cuda.synchronize()
+        assert 0.0 < kern[0].elapsed_time(kern[1]) <= call[0].elapsed_time(call[1])
+    finally:
+        assert lib.fm_set_score_events(ctx, None, None) == L.FM_OK
     # Cleared: a later call records nothing, so the pair keeps its last span.
     before = kern[0].elapsed_time(kern[1])
     assert lib.fm_score(ctx, P(q), P(w), P(ck), B, N, None, 0, P(scores), None, s) == L.FM_OK

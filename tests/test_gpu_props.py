@@ -358,10 +358,11 @@ def test_topk_rows_beyond_the_register_tiles(weights_np):
         r.close()
 
 
-@pytest.mark.parametrize("n,k", [(5003, 17), (77, 5), (40000, 512), (3, 1)])
+@pytest.mark.parametrize("n,k", [(5003, 17), (77, 5), (40000, 512), (3, 1), (8192, 512), (8193, 512)])
 def test_topk_and_threshold_write_every_byte(retr, n, k):
     """Masks filled with ones beforehand: every byte of the [B][N] mask is
-    written (N odd, ragged rows, rows kept whole and empty)."""
+    written (N odd, ragged rows, rows kept whole and empty), on both sides of
+    the row length (8192) up to which top-K takes one launch per row."""
     from sparse_attention_chunk_amd import _lib as L
     rng = np.random.default_rng(n)
     B = 5
