@@ -194,7 +194,9 @@ fm_status fm_select_topk(fm_ctx* ctx, const float* scores, int32_t B, int64_t N,
  * to even) must not exceed 8 MiB (B = 30, N = 262144 needs 3.75 MiB), else
  * FM_EINVAL.  B in [0, 65535], N in [0, 2^26].  Every call on a GPU shares
  * that GPU's scratch: calls that overlap on one GPU (other streams, other
- * threads) race; the first call on a device looks the array's address up. */
+ * threads) race; the first call on a device looks the array's address up.
+ * Rows of at most 8192 chunks are selected in one launch that uses no
+ * scratch (the size limit still applies). */
 fm_status fm_select_topk_static(const float* scores, int32_t B, int64_t N, const int32_t* valid_n, int32_t top_k,
                                 uint8_t* mask, void* stream);
 
