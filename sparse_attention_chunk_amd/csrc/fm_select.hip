@@ -618,12 +618,14 @@ write_out:
 }
 
 // Top-K of short rows (N <= kShortRow) in one launch instead of scan +
-// finish: one block per row selects exactly over the row's keys (every
-// radix pass re-reads the row's scores, at most kShortRow x 4 bytes, from
-// the cache) and then writes each mask byte of the row once.  The same
-// chunks as the two-kernel path: keys above the K-th key T, and of those
-// equal to T the ones up to `last` (ties to the lowest indices).
+// finish: one block per row loads the row's keys into registers once (all
+// loads in flight together), selects exactly over them with radix passes and
+// then writes each mask byte of the row once.  The same chunks as the
+// two-kernel path: keys above the K-th key T, and of those equal to T the
+// ones up to `last` (ties to the lowest indices).
 constexpr int64_t kShortRow = 8192;
+constexpr int kShortPer = (int)(kShortRow / kFinishThreads);  // keys per thread
+static_assert(kShortRow % kFinishThreads == 0, "short rows split evenly over the block");
 __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float* __restrict__ scores, int64_t N,
                                                                     const int32_t* __restrict__ valid_n,
                                                                     int32_t top_k, uint8_t* __restrict__ mask) {
@@ -641,18 +643,29 @@ __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float*
     for (uint32_t n = t; n < n_all; n += kFinishThreads) mrow[n] = n < vn32 ? keep : 0;
     return;
   }
+  // Entry j of thread t is chunk t + j kFinishThreads.
+  uint32_t keys[kShortPer];
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const uint32_t n = t + (uint32_t)j * kFinishThreads;
+    keys[j] = n < vn32 ? order_key(row[n]) : 0u;
+  }
   auto each = [&](auto f) {
-    for (uint32_t n = t; n < vn32; n += kFinishThreads) f(make_uint2(order_key(row[n]), n));
+#pragma unroll
+    for (int j = 0; j < kShortPer; ++j) {
+      const uint32_t n = t + (uint32_t)j * kFinishThreads;
+      if (n < vn32) f(make_uint2(keys[j], n));
+    }
   };
   uint32_t T, last;
   radix_select<kFinishThreads>(each, (uint32_t)top_k, index_bits(vn), h, s_wtot, s_out, &T, &last);
-  for (uint32_t n = t; n < n_all; n += kFinishThreads) {
-    uint8_t keep = 0;
-    if (n < vn32) {
-      const uint32_t k = order_key(row[n]);
-      keep = (k > T || (k == T && n <= last)) ? 1 : 0;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const uint32_t n = t + (uint32_t)j * kFinishThreads;
+    if (n < n_all) {
+      const uint32_t k = keys[j];
+      mrow[n] = (n < vn32 && (k > T || (k == T && n <= last))) ? 1 : 0;
     }
-    mrow[n] = keep;
   }
 }
 
