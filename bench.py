@@ -640,15 +640,17 @@ def score_fp8_leg(L, r, q, w, comp_k, scores, B, N, sh, stream, steps):
             "rates_from": "the score kernel's launch alone (events libfm records around it); 'us' is the whole call"}
 
 
-def subset_topk_leg(L, r, scores, B, N, sh, stream, steps, leg_inputs, resident_k=32768):
+def subset_topk_leg(L, r, scores, B, N, sh, stream, steps, leg_inputs, resident_k=32768, key="subset_topk"):
     """fm_select_topk_subset: a decode step's top-512 within each row's
-    resident set.  The resident set is this pass's top-32768 chunks per row
-    (12.5% of N, the share of the compressed cache the model card keeps on
-    the GPU); the step's scores are seeded uniform stand-ins (the pages do
-    not define the step's score function).  HIP-event time per call on the
-    launch stream; bytes = the list and the gathered scores (4 B each per
-    entry) plus the chosen indices.  Host copies of the step's scores and the
-    lists go into leg_inputs for the CPU baseline."""
+    resident set.  The resident set is this pass's top-`resident_k` chunks per
+    row (32768 = 12.5% of N, the share of the compressed cache the model card
+    keeps on the GPU; 8192 is that share of a 256K-token context's 65536
+    chunks, and takes the one-launch short-list path); the step's scores are
+    seeded uniform stand-ins (the pages do not define the step's score
+    function).  HIP-event time per call on the launch stream; bytes = the
+    list and the gathered scores (4 B each per entry) plus the chosen
+    indices.  Host copies of the step's scores and the lists go into
+    leg_inputs[key] for the CPU baseline (key None: not kept)."""
     import torch
 
     keep = torch.empty((B, N), dtype=torch.bool, device="cuda")
@@ -675,7 +677,8 @@ def subset_topk_leg(L, r, scores, B, N, sh, stream, steps, leg_inputs, resident_
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
     nbytes = B * (8 * resident_k + 4 * TOP_K + 8)
-    leg_inputs["subset_topk"] = (step.cpu().numpy(), sub.cpu().numpy())
+    if key is not None:
+        leg_inputs[key] = (step.cpu().numpy(), sub.cpu().numpy())
     return {"us": t * 1e6, "resident_per_row": resident_k, "top_k": TOP_K, "entries_per_s": B * resident_k / t,
             "bytes": nbytes, "hbm_gbs": nbytes / t / 1e9}
 
@@ -977,6 +980,7 @@ def main(argv=None):
     resident = resident_delta_leg(L, r, hidden, pos, comp_k, q, w, mask, B, N, sh, stream, args.steps, leg_inputs)
     score_fp8 = score_fp8_leg(L, r, q, w, comp_k, torch.empty_like(scores), B, N, sh, stream, args.steps)
     subset = subset_topk_leg(L, r, scores, B, N, sh, stream, args.steps, leg_inputs)
+    subset_short = subset_topk_leg(L, r, scores, B, N, sh, stream, args.steps, leg_inputs, resident_k=8192, key=None)
     masking = mask_logits_leg(L, r, mask, B, N, sh, stream, args.steps)
     variants = variants_leg(L, r, q, w, comp_k, scores, mask, B, N, sh, stream, args.steps)
 
@@ -1103,6 +1107,7 @@ def main(argv=None):
         # the metric's own definition: valid chunks / (score + select), query prep apart
         "score_select_chunks_per_s": chunks / (t_score + float(sel.mean())),
         "next_rows": {"resident_delta": resident, "score_fp8": score_fp8, "subset_topk": subset,
+                      "subset_topk_8192": subset_short,
                       "mask_logits": masking},
         "graph_step": graph,
         "pipelined_step": pipelined,

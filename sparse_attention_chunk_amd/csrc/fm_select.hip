@@ -669,6 +669,79 @@ __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float*
   }
 }
 
+// Subset top-K of short lists (cap <= kShortRow) in one launch instead of
+// subset scan + finish: one block per row gathers the keys of its list
+// positions into registers (thread t holds positions kShortPer t .. + 15,
+// so the chosen ones leave in list order after one block scan), selects
+// exactly over the positions with a key (an index in [0, N)) and writes the
+// chosen chunk indices and their number.  Ties go to the earlier position,
+// as on the other paths.
+__global__ __launch_bounds__(kFinishThreads) void subset_short_kernel(const float* __restrict__ scores, int64_t N,
+                                                                      const int32_t* __restrict__ subset,
+                                                                      const int32_t* __restrict__ n_subset,
+                                                                      int32_t cap, int32_t top_k,
+                                                                      int32_t* __restrict__ out,
+                                                                      int32_t* __restrict__ n_out) {
+  __shared__ __attribute__((aligned(16))) uint32_t h[2 * kSelBins];
+  __shared__ uint32_t s_wtot[kFinishThreads / 64];
+  __shared__ uint32_t s_out[3];
+  const int b = blockIdx.x;
+  const uint32_t t = threadIdx.x;
+  const int64_t n64 = n_subset ? (int64_t)n_subset[b] : (int64_t)cap;
+  const uint32_t n = (uint32_t)(n64 < 0 ? 0 : (n64 > cap ? cap : n64));  // cap <= kShortRow
+  if (top_k == 0 || n == 0) {  // uniform over the block
+    if (t == 0) n_out[b] = 0;
+    return;
+  }
+  const int32_t* srow = subset + (size_t)b * cap;
+  const float* row = scores + (size_t)b * N;
+  const uint32_t p0 = t * kShortPer;
+  int32_t idx[kShortPer];
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) idx[j] = p0 + j < n ? srow[p0 + j] : -1;
+  uint32_t keys[kShortPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const bool ok = idx[j] >= 0 && (int64_t)idx[j] < N;
+    keys[j] = ok ? order_key(row[idx[j]]) : 0u;
+    mine += keys[j] != 0u ? 1u : 0u;
+  }
+  uint32_t n_keyed;
+  (void)block_excl_scan(mine, s_wtot, &n_keyed);
+  uint32_t K = (uint32_t)top_k;
+  uint32_t T = 0u, last = 0xffffffffu;
+  const bool all = K >= n_keyed;  // uniform
+  if (all) {
+    K = n_keyed;
+  } else {
+    auto each = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < kShortPer; ++j)
+        if (keys[j] != 0u) f(make_uint2(keys[j], p0 + j));
+    };
+    radix_select<kFinishThreads>(each, K, index_bits(n), h, s_wtot, s_out, &T, &last);
+  }
+  uint32_t chosen = 0u, cnt = 0u;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const uint32_t k = keys[j];
+    const bool c = k != 0u && (all || k > T || (k == T && p0 + j <= last));
+    chosen |= (c ? 1u : 0u) << j;
+    cnt += c ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t pos = block_excl_scan(cnt, s_wtot, &tot);
+  int32_t* orow = out + (size_t)b * top_k;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j)
+    if ((chosen >> j) & 1u) {
+      if (pos < (uint32_t)top_k) orow[pos] = idx[j];
+      ++pos;
+    }
+  if (t == 0) n_out[b] = (int32_t)K;
+}
+
 // Threshold mask: 16 chunks per thread, one 16-byte store when the run is
 // whole and aligned.  grid = (ceil(N / kScanSlice), B), block = kScanThreads.
 __global__ __launch_bounds__(kScanThreads) void threshold_kernel(const float* __restrict__ scores, int64_t N,
@@ -715,6 +788,11 @@ hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, i
 hipError_t launch_select_topk_subset_fast(const Workspace& ws, const float* scores, int B, int64_t N,
                                           const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                           int32_t* out, int32_t* n_out, hipStream_t stream) {
+  if (cap <= kShortRow) {
+    hipLaunchKernelGGL(subset_short_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, subset, n_subset, cap,
+                       top_k, out, n_out);
+    return hipGetLastError();
+  }
   const unsigned slices = (unsigned)((cap + kSubScanSlice - 1) / kSubScanSlice);
   if (slices > 0)
     hipLaunchKernelGGL(subset_scan_kernel, dim3(slices, B), dim3(kScanThreads), 0, stream, scores, N, subset, n_subset,

@@ -70,6 +70,8 @@ def check(retr, scores, subset, n_sub, top_k, with_count=True):
     (2, 262144, 32768, "sorted", 0),     # the longest list of the tile scan + finish path
     (2, 262144, 65536, "sorted", 5),     # longer lists: keys gathered again in every pass
     (3, 4096, 4096, "sorted", 0),
+    (3, 70000, 8192, "shuffled", 4),     # the longest list of the one-launch path
+    (3, 70000, 8193, "sorted", 2),       # the shortest of the tile scan + finish path
 ])
 def test_random_subsets_exact(retr, B, N, cap, order, bad):
     scores, subset, n_sub = make_case(B * 7 + cap, B, N, cap, order, bad)
