@@ -25,9 +25,9 @@
 //      ranked (key descending, index ascending) for the rest.
 // When the listed chunks or the candidates overflow LDS (many equal or
 // nearly equal scores), the finish selects exactly over the whole row with
-// radix passes instead, so the result is always the exact top-K.  Rows of
-// at most kShortRow chunks skip the scan: one launch selects each row with
-// those radix passes directly.
+// radix passes instead, so the result is always the exact top-K.  Short
+// rows (below) skip the scan: one launch selects each row with radix passes
+// over its keys held in registers.
 #include "fm_radix.h"
 
 namespace fm {
@@ -617,15 +617,26 @@ write_out:
   }
 }
 
-// Top-K of short rows (N <= kShortRow) in one launch instead of scan +
+// Top-K of short rows in one launch instead of scan +
 // finish: one block per row loads the row's keys into registers once (all
 // loads in flight together), selects exactly over them with radix passes and
 // then writes each mask byte of the row once.  The same chunks as the
 // two-kernel path: keys above the K-th key T, and of those equal to T the
 // ones up to `last` (ties to the lowest indices).
+// Rows (lists) of up to kShortRow entries always take it (16 keys per
+// thread); up to kShortRowMax (32 keys per thread) when they hold fewer than
+// 18 K entries.  There the scan + finish path has too few tiles per K: the
+// K-th tile maximum cuts almost nothing, the listed chunks overflow LDS and
+// the finish falls back to radix passes that re-read the row (25 us at
+// B=30, N=8193, K=512, against 8-10 us on either side).
 constexpr int64_t kShortRow = 8192;
-constexpr int kShortPer = (int)(kShortRow / kFinishThreads);  // keys per thread
-static_assert(kShortRow % kFinishThreads == 0, "short rows split evenly over the block");
+constexpr int64_t kShortRowMax = 16384;
+static_assert(kShortRow % kFinishThreads == 0 && kShortRowMax % kFinishThreads == 0, "rows split evenly");
+__host__ __device__ constexpr int short_per(int64_t n, int32_t top_k) {
+  return n <= kShortRow ? (int)(kShortRow / kFinishThreads)
+                        : (n <= kShortRowMax && n < 18 * (int64_t)top_k ? (int)(kShortRowMax / kFinishThreads) : 0);
+}
+template <int kShortPer>
 __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float* __restrict__ scores, int64_t N,
                                                                     const int32_t* __restrict__ valid_n,
                                                                     int32_t top_k, uint8_t* __restrict__ mask) {
@@ -637,7 +648,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float*
   const int64_t vn = row_valid(valid_n, b, N);
   const float* row = scores + (size_t)b * N;
   uint8_t* mrow = mask + (size_t)b * N;
-  const uint32_t n_all = (uint32_t)N, vn32 = (uint32_t)vn;  // N <= kShortRow
+  const uint32_t n_all = (uint32_t)N, vn32 = (uint32_t)vn;  // N <= kShortPer kFinishThreads
   if (top_k == 0 || (int64_t)top_k >= vn) {  // uniform over the block: nothing or every valid chunk
     const uint8_t keep = top_k > 0 ? 1 : 0;
     for (uint32_t n = t; n < n_all; n += kFinishThreads) mrow[n] = n < vn32 ? keep : 0;
@@ -669,13 +680,14 @@ __global__ __launch_bounds__(kFinishThreads) void topk_short_kernel(const float*
   }
 }
 
-// Subset top-K of short lists (cap <= kShortRow) in one launch instead of
-// subset scan + finish: one block per row gathers the keys of its list
-// positions into registers (thread t holds positions kShortPer t .. + 15,
+// Subset top-K of short lists (as short rows above) in one launch instead
+// of subset scan + finish: one block per row gathers the keys of its list
+// positions into registers (thread t holds positions kShortPer t onwards,
 // so the chosen ones leave in list order after one block scan), selects
 // exactly over the positions with a key (an index in [0, N)) and writes the
 // chosen chunk indices and their number.  Ties go to the earlier position,
 // as on the other paths.
+template <int kShortPer>
 __global__ __launch_bounds__(kFinishThreads) void subset_short_kernel(const float* __restrict__ scores, int64_t N,
                                                                       const int32_t* __restrict__ subset,
                                                                       const int32_t* __restrict__ n_subset,
@@ -688,7 +700,7 @@ __global__ __launch_bounds__(kFinishThreads) void subset_short_kernel(const floa
   const int b = blockIdx.x;
   const uint32_t t = threadIdx.x;
   const int64_t n64 = n_subset ? (int64_t)n_subset[b] : (int64_t)cap;
-  const uint32_t n = (uint32_t)(n64 < 0 ? 0 : (n64 > cap ? cap : n64));  // cap <= kShortRow
+  const uint32_t n = (uint32_t)(n64 < 0 ? 0 : (n64 > cap ? cap : n64));  // cap <= kShortPer kFinishThreads
   if (top_k == 0 || n == 0) {  // uniform over the block
     if (t == 0) n_out[b] = 0;
     return;
@@ -772,8 +784,11 @@ __global__ __launch_bounds__(kScanThreads) void threshold_kernel(const float* __
 
 hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, int64_t N, const int32_t* valid_n,
                               int32_t top_k, uint8_t* mask, hipStream_t stream) {
-  if (N <= kShortRow) {
-    hipLaunchKernelGGL(topk_short_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k, mask);
+  const int per = short_per(N, top_k);
+  if (per != 0) {
+    auto kern = per == (int)(kShortRow / kFinishThreads) ? topk_short_kernel<(int)(kShortRow / kFinishThreads)>
+                                                         : topk_short_kernel<(int)(kShortRowMax / kFinishThreads)>;
+    hipLaunchKernelGGL(kern, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, valid_n, top_k, mask);
     return hipGetLastError();
   }
   const unsigned slices = (unsigned)((N + kScanSlice - 1) / kScanSlice);
@@ -788,9 +803,12 @@ hipError_t launch_select_topk(const Workspace& ws, const float* scores, int B, i
 hipError_t launch_select_topk_subset_fast(const Workspace& ws, const float* scores, int B, int64_t N,
                                           const int32_t* subset, const int32_t* n_subset, int32_t cap, int32_t top_k,
                                           int32_t* out, int32_t* n_out, hipStream_t stream) {
-  if (cap <= kShortRow) {
-    hipLaunchKernelGGL(subset_short_kernel, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, subset, n_subset, cap,
-                       top_k, out, n_out);
+  const int per = short_per(cap, top_k);
+  if (per != 0) {
+    auto kern = per == (int)(kShortRow / kFinishThreads) ? subset_short_kernel<(int)(kShortRow / kFinishThreads)>
+                                                         : subset_short_kernel<(int)(kShortRowMax / kFinishThreads)>;
+    hipLaunchKernelGGL(kern, dim3(B), dim3(kFinishThreads), 0, stream, scores, N, subset, n_subset, cap, top_k, out,
+                       n_out);
     return hipGetLastError();
   }
   const unsigned slices = (unsigned)((cap + kSubScanSlice - 1) / kSubScanSlice);
